@@ -1,0 +1,167 @@
+"""Gist-compressed KV attention and paged decode for AMD MI355X (gfx950).
+
+Thin torch-facing binding over libgist_attn.so: every function here only
+checks and marshals arguments (device pointers, sizes, the current HIP
+stream) and calls the C entry point of the same name.  All computation runs
+in the library's HIP kernels; torch provides device memory and streams.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import GIST_BF16, GIST_F32, GistError  # noqa: F401
+
+__all__ = [
+    "GistPool", "GistError", "gist_pool_bytes", "gist_pool_create", "gist_pool_write",
+    "gist_attn_forward", "paged_decode_workspace_bytes", "paged_decode_attn",
+]
+
+_DTYPES = {torch.bfloat16: GIST_BF16, torch.float32: GIST_F32}
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {dtype}; use torch.bfloat16 or torch.float32")
+    return _DTYPES[dtype]
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def gist_pool_bytes(L: int, N: int, k: int, H: int, d: int, dtype: torch.dtype) -> int:
+    return _lib.lib().gist_pool_bytes(L, N, k, H, d, _code(dtype))
+
+
+class GistPool:
+    """A gist pool over a caller-owned device tensor [L][N][2][H][k][d]."""
+
+    def __init__(self, storage: torch.Tensor):
+        if storage.dim() != 6 or storage.shape[2] != 2:
+            raise ValueError("storage must have shape [L, N, 2, H, k, d]")
+        L, N, _, H, k, d = storage.shape
+        self.storage = storage
+        self.L, self.N, self.H, self.k, self.d = L, N, H, k, d
+        self.dtype = storage.dtype
+        handle = _lib.ctypes.c_void_p()
+        _lib.check(_lib.lib().gist_pool_create(
+            _lib.ctypes.byref(handle), L, N, k, H, d, _code(storage.dtype),
+            _dev(storage, "storage"), storage.numel() * storage.element_size()),
+            "gist_pool_create")
+        self._handle = handle
+
+    @property
+    def handle(self):
+        return self._handle
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            _lib.lib().gist_pool_destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def gist_pool_create(storage: torch.Tensor) -> GistPool:
+    return GistPool(storage)
+
+
+def gist_pool_write(pool: GistPool, layer: int, ids: torch.Tensor, k_src: torch.Tensor,
+                    v_src: torch.Tensor, src_pos0: int = 1, rope_base: float = 10000.0,
+                    stream=None) -> None:
+    n = ids.numel()
+    shape = (n, pool.k, pool.H, pool.d)
+    args = (_dev(ids, "ids", torch.int32), _dev(k_src, "k_src", pool.dtype, shape),
+            _dev(v_src, "v_src", pool.dtype, shape))
+    _lib.check(_lib.lib().gist_pool_write(pool.handle, layer, args[0], n, args[1], args[2],
+                                          src_pos0, rope_base, _stream_ptr(stream)),
+               "gist_pool_write")
+
+
+def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: torch.Tensor,
+                      k_new: torch.Tensor, v_new: torch.Tensor, pos0: int | None = None,
+                      rope_base: float = 10000.0, scale: float | None = None,
+                      qpool: GistPool | None = None, q_ids: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [P, ell, Hq, d]; k_new, v_new [P, ell, H, d]; returns out [P, ell, Hq, d]."""
+    if q.dim() != 4:
+        raise ValueError("q must have shape [P, ell, Hq, d]")
+    P, ell, Hq, d = q.shape
+    if pos0 is None:
+        pos0 = pool.k + (qpool.k if qpool is not None else 0) + 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    kv_shape = (P, ell, pool.H, pool.d)
+    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q, "q", pool.dtype),
+            _dev(k_new, "k_new", pool.dtype, kv_shape), _dev(v_new, "v_new", pool.dtype, kv_shape),
+            _dev(out, "out", pool.dtype, q.shape))
+    qh, qi = None, None
+    if qpool is not None:
+        qh = qpool.handle
+        qi = _dev(q_ids, "q_ids", torch.int32, (P,))
+    _lib.check(_lib.lib().gist_attn_forward(pool.handle, layer, ptrs[0], P, ell, Hq, ptrs[1],
+                                            ptrs[2], ptrs[3], pos0, rope_base, scale, qh, qi,
+                                            ptrs[4], _stream_ptr(stream)), "gist_attn_forward")
+    return out
+
+
+def paged_decode_workspace_bytes(R: int, Hq: int, max_blocks: int, block_size: int,
+                                 d: int) -> int:
+    return _lib.lib().paged_decode_workspace_bytes(R, Hq, max_blocks, block_size, d)
+
+
+def paged_decode_attn(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                      context_lens: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                      v_new: torch.Tensor, positions: torch.Tensor, rope_base: float = 10000.0,
+                      scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """k_cache, v_cache [n_blocks, H, block_size, d]; block_table [R, max_blocks];
+    q [R, Hq, d]; k_new, v_new [R, H, d]; returns out [R, Hq, d]."""
+    n_blocks, H, bs, d = k_cache.shape
+    R, Hq, _ = q.shape
+    max_blocks = block_table.shape[1] if block_table.dim() == 2 else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    need = paged_decode_workspace_bytes(R, Hq, max(max_blocks, 1), bs, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dt = k_cache.dtype
+    ptrs = (_dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt, k_cache.shape),
+            _dev(block_table, "block_table", torch.int32), _dev(context_lens, "context_lens",
+                                                               torch.int32, (R,)),
+            _dev(q, "q", dt), _dev(k_new, "k_new", dt, (R, H, d)), _dev(v_new, "v_new", dt, (R, H, d)),
+            _dev(positions, "positions", torch.int32, (R,)), _dev(out, "out", dt, q.shape),
+            _dev(workspace, "workspace"))
+    _lib.check(_lib.lib().paged_decode_attn(
+        ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], max_blocks, ptrs[3], R, ptrs[4], ptrs[5], ptrs[6],
+        ptrs[7], Hq, H, d, _code(dt), rope_base, scale, ptrs[8], ptrs[9],
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)), "paged_decode_attn")
+    return out

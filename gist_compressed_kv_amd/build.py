@@ -1,0 +1,70 @@
+"""Compile libgist_attn.so (HIP, gfx950) in-tree with hipcc.
+
+Run as ``python -m gist_compressed_kv_amd.build``.  The library is written
+next to this file; it is a build product, not source.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_NAME = "libgist_attn.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+SOURCES = ["pool.hip", "gist_forward.hip", "paged_decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set HIPCC or install ROCm)")
+
+
+def compile_flags() -> list[str]:
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-Wall",
+        "-Wno-unused-function",
+        # packed fp32 VALU ops are kept out of the generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    objs = []
+    tmpdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(tmpdir, exist_ok=True)
+    cc = hipcc()
+    for src in SOURCES:
+        obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        objs.append(obj)
+    tmp_lib = LIB_PATH + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp_lib, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp_lib, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    path = build(verbose="-v" in sys.argv)
+    print(path)

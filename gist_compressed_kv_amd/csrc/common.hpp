@@ -1,0 +1,110 @@
+// Shared device/host helpers of libgist_attn.so (HIP, gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "../../include/gist_attn.h"
+
+namespace gist {
+
+// ---------------------------------------------------------------------------
+// Error state (thread-local message behind gist_last_error)
+// ---------------------------------------------------------------------------
+void set_error(const std::string& msg);
+void clear_error();
+gist_status fail(gist_status code, const std::string& msg);
+gist_status check_launch(const char* what);
+
+// ---------------------------------------------------------------------------
+// Element types
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16_t;  // bfloat16 bits in memory
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Unpack 8 bf16 held in a uint4 into floats.
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16);
+  f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16);
+  f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+// Round two floats to bf16 (nearest-even, hardware v_cvt_pk_bf16_f32) and
+// pack them low-first into one dword.
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint4 pack8_bf16(const float* f) {
+  return make_uint4(pack2_bf16(f[0], f[1]), pack2_bf16(f[2], f[3]), pack2_bf16(f[4], f[5]),
+                    pack2_bf16(f[6], f[7]));
+}
+
+// ---------------------------------------------------------------------------
+// RoPE angles.  The host computes theta_i = base^(-2i/d) in double; the
+// device forms pos*theta_i in double, reduces it to [-pi, pi] (two-constant
+// Cody-Waite split of 2*pi) and evaluates fp32 sincosf on the remainder, so
+// angles of a few thousand radians keep ~1e-7 accuracy.
+// ---------------------------------------------------------------------------
+constexpr int kMaxHalfDim = 64;  // d <= 128
+
+struct RopeFreqs {
+  double theta[kMaxHalfDim];
+};
+
+inline void make_rope_freqs(RopeFreqs& f, int d, float base) {
+  for (int i = 0; i < kMaxHalfDim; ++i)
+    f.theta[i] = (i < d / 2) ? std::pow((double)base, -2.0 * (double)i / (double)d) : 0.0;
+}
+
+__device__ __forceinline__ void rope_cos_sin(double pos, double theta, float& c, float& s) {
+  const double kTwoPiHi = 6.283185307179586232;     // nearest double to 2*pi
+  const double kTwoPiLo = 2.4492935982947064e-16;    // 2*pi - kTwoPiHi
+  const double kInvTwoPi = 0.15915494309189533577;
+  double a = pos * theta;
+  double n = rint(a * kInvTwoPi);
+  double r = fma(-n, kTwoPiHi, a);
+  r = fma(-n, kTwoPiLo, r);
+  sincosf((float)r, &s, &c);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side pool handle
+// ---------------------------------------------------------------------------
+}  // namespace gist
+
+struct gist_pool {
+  int L;
+  int64_t N;
+  int k;
+  int H;
+  int d;
+  gist_dtype dtype;
+  void* storage;
+  size_t bytes;
+};
+
+namespace gist {
+inline size_t elem_size(gist_dtype t) { return t == GIST_BF16 ? 2 : 4; }
+// elements of one (layer, item) record: [2][H][k][d]
+inline int64_t record_elems(const gist_pool* p) { return 2LL * p->H * p->k * p->d; }
+}  // namespace gist

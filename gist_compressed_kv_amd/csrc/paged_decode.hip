@@ -1,0 +1,435 @@
+// paged_decode_attn: one decode step of R requests over a KV cache kept in
+// fixed-size blocks scattered through a physical block pool.
+//
+// What is computed (mcfzz.com "为什么自回归推理缓存 KV，而不缓存历史 Q？",
+// Reusable-state): the new token's rotated query attends, with softmax scale
+// `scale`, over [the cached keys in logical order ; its own rotated key], and
+// returns the matching weighted sum of [cached values ; its own value].  The
+// logical -> physical block indirection is the block table of icman.com.cn
+// news 64898 (section 6, problem 4; 256-token blocks in section 5).
+//
+// Two kernels (split-K, flash-decoding style):
+//  * decode_split<T, D, MAXG>: one workgroup (4 wave64s) per (request, KV
+//    head, 256-key split).  Each 16-lane row of a wave streams 16 consecutive
+//    keys of one block (a row is 16 lanes x d/16 channels = one full K or V
+//    row, so every load instruction reads whole contiguous rows), keeps an
+//    online-softmax state (max, sum, weighted V) per query head of the GQA
+//    group, and the states of the 16 rows of the workgroup are merged with
+//    cross-lane shuffles and LDS.  The split's (o, m, l) goes to the fp32
+//    workspace.
+//  * decode_combine<T, D>: one wave64 per (request, query head) merges the
+//    split states with the token's own key/value (log-sum-exp weights) and
+//    writes the normalized output.
+#include "common.hpp"
+
+namespace gist {
+
+constexpr int kSplitKeys = 256;  // keys per workgroup of the split kernel
+constexpr int kWsPad = 4;        // workspace row = d channels + (m, l, 2 pad)
+
+struct DecodeArgs {
+  const void* kc;
+  const void* vc;
+  int64_t nblk;
+  int bs;
+  const int32_t* table;
+  int max_blk;
+  const int32_t* ctx;
+  int R;
+  const void* q;
+  const void* kn;
+  const void* vn;
+  const int32_t* positions;
+  int Hq, H, G;
+  float scale_log2;
+  float* ws;
+  int nsplit;
+  void* out;
+  RopeFreqs freqs;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum_d(float x) {
+  x += dpp_row<0xB1>(x);
+  x += dpp_row<0x4E>(x);
+  x += dpp_row<0x141>(x);
+  x += dpp_row<0x140>(x);
+  return x;
+}
+
+template <typename T, int N>
+__device__ __forceinline__ void load_row_slice(const T* __restrict__ p, float* f) {
+  if constexpr (sizeof(T) == 2) {
+    if constexpr (N == 8) {
+      unpack8(*(const uint4*)p, f);
+    } else {  // N == 4
+      const uint2 v = *(const uint2*)p;
+      f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
+      f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 v = *(const float4*)(p + i);
+      f[i] = v.x; f[i + 1] = v.y; f[i + 2] = v.z; f[i + 3] = v.w;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ float elem_f(const T* p, int64_t i) {
+  if constexpr (sizeof(T) == 2)
+    return bf16_bits_to_f32(p[i]);
+  else
+    return p[i];
+}
+
+// Merge online-softmax state (m2, l2, o2) into (m, l, o).
+template <int N>
+__device__ __forceinline__ void merge_state(float& m, float& l, float* o, float m2, float l2,
+                                            const float* o2) {
+  const float mm = fmaxf(m, m2);
+  float a1 = 0.f, a2 = 0.f;
+  if (mm != -INFINITY) {
+    a1 = exp2f(m - mm);
+    a2 = exp2f(m2 - mm);
+  }
+#pragma unroll
+  for (int e = 0; e < N; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  l = l * a1 + l2 * a2;
+  m = mm;
+}
+
+template <typename T, int D, int MAXG>
+__global__ void __launch_bounds__(256)
+decode_split(const DecodeArgs a) {
+  constexpr int E = D / 16;  // channels per lane
+  __shared__ float red[4][MAXG][D + 2];
+
+  const int bid = blockIdx.x;
+  const int s = bid % a.nsplit;
+  const int rg = bid / a.nsplit;
+  const int g = rg % a.H;
+  const int r = rg / a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int gi = lane >> 4, c = lane & 15;
+  const int G = a.G;
+
+  const int ctx = a.ctx[r];
+  const int64_t cap = (int64_t)a.max_blk * a.bs;
+  const bool ctx_bad = ctx < 0 || ctx > cap;
+  const int kbeg = s * kSplitKeys + 64 * wv + 16 * gi;  // this row's 16 keys
+  const int kend = ctx_bad ? 0 : min(kbeg + 16, ctx);
+
+  // rotated query slice of every head of the group: channels [E*c, E*c+E)
+  float qv[MAXG][E];
+  {
+    const double pos = (double)a.positions[r];
+    const int ch0 = E * c;
+    const bool low = ch0 < D / 2;
+    const int partner = low ? ch0 + D / 2 : ch0 - D / 2;
+    const int fi = low ? ch0 : partner;  // frequency index of the pair
+    float cs[E], sn[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) rope_cos_sin(pos, a.freqs.theta[fi + e], cs[e], sn[e]);
+#pragma unroll
+    for (int hh = 0; hh < MAXG; ++hh) {
+      if (hh < G) {
+        const T* qr = (const T*)a.q + ((int64_t)r * a.Hq + (int64_t)g * G + hh) * D;
+        float x[E], y[E];
+        load_row_slice<T, E>(qr + ch0, x);
+        load_row_slice<T, E>(qr + partner, y);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          qv[hh][e] = low ? x[e] * cs[e] - y[e] * sn[e] : x[e] * cs[e] + y[e] * sn[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) qv[hh][e] = 0.f;
+      }
+    }
+  }
+
+  float m[MAXG], l[MAXG], o[MAXG][E];
+#pragma unroll
+  for (int hh = 0; hh < MAXG; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[hh][e] = 0.f;
+  }
+  bool blk_bad = false;
+
+  if (kbeg < kend) {
+    // 16 keys of one row lie in one block (block_size is a multiple of 16)
+    const int32_t phys = a.table[(int64_t)r * a.max_blk + kbeg / a.bs];
+    if (phys < 0 || phys >= a.nblk) {
+      blk_bad = true;
+    } else {
+      const int64_t base = (((int64_t)phys * a.H + g) * a.bs + (kbeg % a.bs)) * D + E * c;
+      const T* kp = (const T*)a.kc + base;
+      const T* vp = (const T*)a.vc + base;
+      const int nkeys = kend - kbeg;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float kr[8][E], vr[8][E];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kk = 8 * half + i;
+          if (kk < nkeys) {
+            load_row_slice<T, E>(kp + (int64_t)kk * D, kr[i]);
+            load_row_slice<T, E>(vp + (int64_t)kk * D, vr[i]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int kk = 8 * half + i;
+          if (kk < nkeys) {
+#pragma unroll
+            for (int hh = 0; hh < MAXG; ++hh) {
+              if (hh < G) {
+                float part = 0.f;
+#pragma unroll
+                for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kr[i][e], part);
+                const float sc = row16_sum_d(part) * a.scale_log2;
+                const float mnew = fmaxf(m[hh], sc);
+                const float alpha = exp2f(m[hh] - mnew);
+                const float pw = exp2f(sc - mnew);
+                m[hh] = mnew;
+                l[hh] = l[hh] * alpha + pw;
+#pragma unroll
+                for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pw, vr[i][e], o[hh][e] * alpha);
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // merge the four rows of the wave (lane ^ 16, lane ^ 32)
+#pragma unroll
+  for (int span = 16; span <= 32; span <<= 1) {
+#pragma unroll
+    for (int hh = 0; hh < MAXG; ++hh) {
+      float o2[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) o2[e] = __shfl_xor(o[hh][e], span);
+      const float m2 = __shfl_xor(m[hh], span);
+      const float l2 = __shfl_xor(l[hh], span);
+      merge_state<E>(m[hh], l[hh], o[hh], m2, l2, o2);
+    }
+  }
+  // a bad block anywhere poisons the split
+  const bool wave_bad = __any(blk_bad) != 0;
+
+  // merge the four waves through LDS
+  if (gi == 0) {
+#pragma unroll
+    for (int hh = 0; hh < MAXG; ++hh) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) red[wv][hh][E * c + e] = o[hh][e];
+      if (c == 0) {
+        red[wv][hh][D] = m[hh];
+        red[wv][hh][D + 1] = wave_bad ? __int_as_float(0x7fc00000) : l[hh];
+      }
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && gi == 0) {
+#pragma unroll
+    for (int hh = 0; hh < MAXG; ++hh) {
+      if (hh >= G) continue;
+      float mm = red[0][hh][D], ll = red[0][hh][D + 1];
+      float oo[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) oo[e] = red[0][hh][E * c + e];
+#pragma unroll
+      for (int w2 = 1; w2 < 4; ++w2) {
+        float o2[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o2[e] = red[w2][hh][E * c + e];
+        merge_state<E>(mm, ll, oo, red[w2][hh][D], red[w2][hh][D + 1], o2);
+      }
+      if (ctx_bad) ll = __int_as_float(0x7fc00000);
+      float* dst = a.ws + (((int64_t)r * a.Hq + (int64_t)g * G + hh) * a.nsplit + s) * (D + kWsPad);
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[E * c + e] = oo[e];
+      if (c == 0) {
+        dst[D] = mm;
+        dst[D + 1] = ll;
+      }
+    }
+  }
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64)
+decode_combine(const DecodeArgs a) {
+  constexpr int EC = D / 64;  // channels per lane: d = lane + 64*e
+  const int bid = blockIdx.x;
+  const int h = bid % a.Hq;
+  const int r = bid / a.Hq;
+  const int g = h / a.G;
+  const int lane = threadIdx.x;
+  const double pos = (double)a.positions[r];
+  const T* qr = (const T*)a.q + ((int64_t)r * a.Hq + h) * D;
+  const T* kr = (const T*)a.kn + ((int64_t)r * a.H + g) * D;
+  const T* vr = (const T*)a.vn + ((int64_t)r * a.H + g) * D;
+
+  float part = 0.f;
+  float vself[EC];
+#pragma unroll
+  for (int e = 0; e < EC; ++e) {
+    const int d = lane + 64 * e;
+    const bool low = d < D / 2;
+    const int partner = low ? d + D / 2 : d - D / 2;
+    float cs, sn;
+    rope_cos_sin(pos, a.freqs.theta[low ? d : partner], cs, sn);
+    const float qd = elem_f(qr, d), qp = elem_f(qr, partner);
+    const float kd = elem_f(kr, d), kpn = elem_f(kr, partner);
+    const float qrot = low ? qd * cs - qp * sn : qd * cs + qp * sn;
+    const float krot = low ? kd * cs - kpn * sn : kd * cs + kpn * sn;
+    part = fmaf(qrot, krot, part);
+    vself[e] = elem_f(vr, d);
+  }
+  part += __shfl_xor(part, 32);
+  part += __shfl_xor(part, 16);
+  const float sself = row16_sum_d(part) * a.scale_log2;
+
+  const float* ws = a.ws + ((int64_t)r * a.Hq + h) * a.nsplit * (D + kWsPad);
+  float mm = sself;
+  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, ws[s * (D + kWsPad) + D]);
+  const float wself = exp2f(sself - mm);
+  float ll = wself;
+  float acc[EC];
+#pragma unroll
+  for (int e = 0; e < EC; ++e) acc[e] = wself * vself[e];
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* row = ws + s * (D + kWsPad);
+    const float ms = row[D];
+    const float ls = row[D + 1];
+    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
+    ll = fmaf(ls, w, ll);  // NaN l (bad block/context) poisons the output
+#pragma unroll
+    for (int e = 0; e < EC; ++e) acc[e] = fmaf(row[lane + 64 * e], w, acc[e]);
+  }
+  const float inv = 1.f / ll;
+  T* orow = (T*)a.out + ((int64_t)r * a.Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < EC; ++e) {
+    const float y = acc[e] * inv;
+    if constexpr (sizeof(T) == 2)
+      orow[lane + 64 * e] = (T)(pack2_bf16(y, 0.f) & 0xffffu);
+    else
+      orow[lane + 64 * e] = y;
+  }
+}
+
+}  // namespace gist
+
+using namespace gist;
+
+namespace {
+int num_splits(int max_blocks, int block_size) {
+  const int64_t keys = (int64_t)max_blocks * block_size;
+  return (int)((keys + kSplitKeys - 1) / kSplitKeys);
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+template <typename T, int D>
+void launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid1((unsigned)((int64_t)a.R * a.H * a.nsplit));
+  if (a.G <= 1)
+    hipLaunchKernelGGL((decode_split<T, D, 1>), grid1, dim3(256), 0, s, a);
+  else if (a.G <= 2)
+    hipLaunchKernelGGL((decode_split<T, D, 2>), grid1, dim3(256), 0, s, a);
+  else if (a.G <= 4)
+    hipLaunchKernelGGL((decode_split<T, D, 4>), grid1, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split<T, D, 8>), grid1, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_combine<T, D>), dim3((unsigned)((int64_t)a.R * a.Hq)), dim3(64), 0,
+                     s, a);
+}
+}  // namespace
+
+extern "C" size_t paged_decode_workspace_bytes(int R, int Hq, int max_blocks, int block_size,
+                                               int d) {
+  if (R < 0 || Hq <= 0 || max_blocks <= 0 || block_size <= 0 || d <= 0) return 0;
+  return (size_t)R * Hq * num_splits(max_blocks, block_size) * (d + kWsPad) * sizeof(float);
+}
+
+extern "C" gist_status paged_decode_attn(const void* k_cache, const void* v_cache,
+                                         int64_t n_blocks, int block_size,
+                                         const int32_t* block_table, int max_blocks,
+                                         const int32_t* context_lens, int R, const void* q,
+                                         const void* k_new, const void* v_new,
+                                         const int32_t* positions, int Hq, int H, int d,
+                                         gist_dtype dtype, float rope_base, float scale, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (dtype != GIST_BF16 && dtype != GIST_F32)
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: unknown dtype");
+  if (R < 0) return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: R < 0");
+  if (H <= 0 || Hq < H || Hq % H != 0)
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: Hq must be a positive multiple of H");
+  if (Hq / H > 8) return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: Hq/H must be <= 8");
+  if (d != 64 && d != 128)
+    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: head_dim must be 64 or 128");
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: block_size must be a multiple of 16");
+  if (n_blocks <= 0 || max_blocks <= 0)
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: n_blocks and max_blocks must be > 0");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: scale must be positive and finite");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: rope_base must be positive");
+  if (R == 0) return GIST_OK;
+  if (!k_cache || !v_cache || !block_table || !context_lens || !q || !k_new || !v_new ||
+      !positions || !out || !workspace)
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: NULL pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(out) || !aligned16(workspace))
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: tensors must be 16-byte aligned");
+  const size_t need = paged_decode_workspace_bytes(R, Hq, max_blocks, block_size, d);
+  if (workspace_bytes < need)
+    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: workspace too small (" +
+                                          std::to_string(workspace_bytes) + " < " +
+                                          std::to_string(need) + ")");
+  const int nsplit = num_splits(max_blocks, block_size);
+  if ((int64_t)R * H * nsplit > INT32_MAX)
+    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: too many splits for one launch");
+
+  DecodeArgs a;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.nblk = n_blocks;
+  a.bs = block_size;
+  a.table = block_table;
+  a.max_blk = max_blocks;
+  a.ctx = context_lens;
+  a.R = R;
+  a.q = q;
+  a.kn = k_new;
+  a.vn = v_new;
+  a.positions = positions;
+  a.Hq = Hq;
+  a.H = H;
+  a.G = Hq / H;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.ws = (float*)workspace;
+  a.nsplit = nsplit;
+  a.out = out;
+  make_rope_freqs(a.freqs, d, rope_base);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GIST_BF16) {
+    if (d == 64) launch_decode<bf16_t, 64>(a, s);
+    else launch_decode<bf16_t, 128>(a, s);
+  } else {
+    if (d == 64) launch_decode<float, 64>(a, s);
+    else launch_decode<float, 128>(a, s);
+  }
+  return check_launch("paged_decode_attn");
+}

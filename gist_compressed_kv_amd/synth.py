@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs and workload shapes.
+
+Only random-number generation and bookkeeping live here; none of the
+attention arithmetic does.  The oracle and the HIP path both consume what
+these functions produce (the oracle always receives the exact device
+values, copied back).
+
+Workloads mirror the shapes the gist article works with (liam.page
+"把 item 压成 KV：gist 能不能用在相关性任务上": 24 layers / 2 KV heads /
+head_dim 64 and 28 layers / 8 KV heads / head_dim 128 in 收益有多大：存储,
+k = 8 gist positions, ell = 64 query tokens (63 + EOS), 50 candidates per
+query in 装不下的时候自然要分片, query gist k' = 8 in 能不能再进一步) and,
+for paged decode, 256-token blocks (icman.com.cn news 64898, section 5).
+Every tensor is N(0, 1) in fp32, rounded once to the target dtype.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+def generator(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn(shape, seed: int, dtype: torch.dtype, device, chunk_elems: int = 1 << 27) -> torch.Tensor:
+    """N(0,1) drawn in fp32 from a seeded generator, rounded to ``dtype``.
+
+    Large tensors are filled in chunks along the first axis so that the fp32
+    staging buffer stays bounded.
+    """
+    out = torch.empty(shape, dtype=dtype, device=device)
+    g = generator(seed, device)
+    flat = out.view(-1)
+    n = flat.numel()
+    for start in range(0, n, chunk_elems):
+        stop = min(n, start + chunk_elems)
+        flat[start:stop].copy_(torch.randn(stop - start, generator=g, device=device,
+                                           dtype=torch.float32))
+    return out
+
+
+def item_ids_per_query(n_queries: int, n_candidates: int, n_items: int, seed: int,
+                       device) -> torch.Tensor:
+    """Candidate ids, query-major: each query draws n_candidates distinct items
+    uniformly (a prefix of a random permutation)."""
+    g = generator(seed, "cpu")
+    rows = [torch.randperm(n_items, generator=g)[:n_candidates] for _ in range(n_queries)]
+    return torch.cat(rows).to(torch.int32).to(device)
+
+
+def block_table(n_requests: int, blocks_per_request: int, n_blocks: int, seed: int,
+                device) -> torch.Tensor:
+    """Each request's logical blocks map to distinct physical blocks drawn from
+    a seeded random permutation of the block pool."""
+    g = generator(seed, "cpu")
+    perm = torch.randperm(n_blocks, generator=g)[: n_requests * blocks_per_request]
+    return perm.view(n_requests, blocks_per_request).to(torch.int32).to(device)
+
+
+def tensor_seed(seed: int, tensor_id: int, layer: int = 0) -> int:
+    return seed * 1000 + tensor_id + 100003 * layer
+
+
+@dataclass(frozen=True)
+class GistWorkload:
+    name: str
+    layers: int
+    n_items: int
+    k: int
+    ell: int
+    hq: int
+    h: int
+    d: int
+    pairs: int
+    queries: int
+    dtype: torch.dtype
+    seed: int
+    kq: int = 0  # query-gist positions (0 = no query gist)
+
+    @property
+    def pos0(self) -> int:
+        return self.k + self.kq + 1
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    layers: int
+    requests: int
+    context: int
+    block_size: int
+    hq: int
+    h: int
+    d: int
+    dtype: torch.dtype
+    seed: int
+
+    @property
+    def blocks_per_request(self) -> int:
+        return -(-self.context // self.block_size)
+
+
+TINY = GistWorkload("tiny: 1 layer, 4 pairs over 2 items, k=8, ell=16, Hq=4, H=1, d=64, fp32",
+                    1, 2, 8, 16, 4, 1, 64, 4, 2, torch.float32, 1)
+SINGLE_LAYER = GistWorkload("1 layer, Hq=14, H=2, d=64, k=8, ell=64, 500 pairs, 100k-item pool, bf16",
+                            1, 100_000, 8, 64, 14, 2, 64, 500, 10, torch.bfloat16, 2)
+L24_B500 = GistWorkload("24 layers, Hq=14, H=2, d=64, k=8, ell=64, 500 pairs, 100k-item pools, bf16",
+                        24, 100_000, 8, 64, 14, 2, 64, 500, 10, torch.bfloat16, 3)
+L24_B2000 = GistWorkload("24 layers, Hq=14, H=2, d=64, k=8, ell=64, 2000 pairs, 100k-item pools, bf16",
+                         24, 100_000, 8, 64, 14, 2, 64, 2000, 40, torch.bfloat16, 3)
+WIDE_ELL64 = GistWorkload("28 layers, Hq=64, H=8, d=128, k=8, ell=64, 2000 pairs, 100k-item pool, bf16",
+                          28, 100_000, 8, 64, 64, 8, 128, 2000, 40, torch.bfloat16, 4)
+WIDE_EOS = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query gist k'=8 + EOS (ell=1), "
+                        "2000 pairs, bf16", 28, 100_000, 8, 1, 64, 8, 128, 2000, 40,
+                        torch.bfloat16, 4, kq=8)
+PAGED = DecodeWorkload("paged decode: 32 requests x 4096 cached tokens in 256-token blocks, "
+                       "Hq=H=32, d=128, 32 layers, bf16", 32, 32, 4096, 256, 32, 32, 128,
+                       torch.bfloat16, 5)

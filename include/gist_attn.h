@@ -1,0 +1,172 @@
+/*
+ * gist_attn.h — C ABI of libgist_attn.so: gist-compressed KV attention and
+ * paged single-token decode on AMD MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [GIST] liam.page, "把 item 压成 KV：gist 能不能用在相关性任务上"
+ *   [KVC]  mcfzz.com, "为什么自回归推理缓存 KV，而不缓存历史 Q？"
+ *   [SFX]  icman.com.cn/news/64898 (suffix-cache article)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a plain device pointer owned by the caller.  The
+ *   library never allocates device memory and never frees caller memory.
+ * - Layouts are dense, row-major, with the last dimension contiguous.
+ * - Element type: GIST_BF16 (bfloat16 bits) or GIST_F32.  All arithmetic
+ *   inside the kernels is fp32; bf16 outputs are rounded to nearest-even.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  The
+ *   calls enqueue work and return; results are visible after the stream syncs.
+ * - Arguments are validated on the host before any HIP call.  On invalid
+ *   arguments the call returns a negative gist_status, enqueues nothing and
+ *   records a message readable with gist_last_error().  A launch failure
+ *   reported by the HIP runtime returns GIST_ERR_HIP.
+ * - Index arrays (item ids, block tables) are read on the device and are
+ *   bounds-checked there: an out-of-range index never causes an access
+ *   outside the pool; the rows that depend on it are written as NaN.
+ * - Calls that write memory another call reads must be ordered by the
+ *   caller's streams.
+ * - RoPE: channel pair (i, i + d/2) turns by pos * base^(-2i/d) ("rotate
+ *   half"); positions are 1-based.  Only position differences matter
+ *   ([GIST] 在线的一次 attention), so any origin works if it is consistent.
+ * - GQA: query head h reads KV head h / (Hq / H).
+ */
+#ifndef GIST_ATTN_H
+#define GIST_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GIST_OK = 0,
+  GIST_ERR_INVALID_ARG = -1,  /* null pointer, negative size, inconsistent shapes */
+  GIST_ERR_UNSUPPORTED = -2,  /* valid request outside what the kernels implement */
+  GIST_ERR_OUT_OF_RANGE = -3, /* a host-visible index (layer) is out of range */
+  GIST_ERR_HIP = -4           /* the HIP runtime reported an error */
+} gist_status;
+
+typedef enum { GIST_F32 = 0, GIST_BF16 = 1 } gist_dtype;
+
+/* Opaque handle describing a caller-owned gist pool (host metadata only). */
+typedef struct gist_pool gist_pool;
+
+/*
+ * gist_pool_bytes — bytes of a pool holding N items, each with k gist
+ * positions in each of L layers: N * 2*L*k*H*d * sizeof(dtype), the per-item
+ * size 2·L·k·H·h·b of [GIST] 在线的一次 attention / 收益有多大：存储.
+ * Returns 0 for invalid shapes.
+ */
+size_t gist_pool_bytes(int L, int64_t N, int k, int H, int d, gist_dtype dtype);
+
+/*
+ * gist_pool_create — wrap caller-owned device storage as a gist pool.
+ *   storage       device buffer of exactly gist_pool_bytes(...) bytes,
+ *                 16-byte aligned, layout [L][N][2][H][k][d]; index 0 of the
+ *                 "2" axis holds K, index 1 holds V.  For every (layer, item)
+ *                 the K and V rows of all H heads form one contiguous record.
+ *   K rows are stored already rotated at the canonical gist positions
+ *   1..k ([GIST] 在线的一次 attention: the query sits k positions after the
+ *   gist, as in training).  The handle is immutable and may be shared by
+ *   concurrent streams.  Requires d in {64, 128}, 1 <= k <= 64, H >= 1.
+ *   Writes the new handle to *out (host memory, freed by gist_pool_destroy).
+ */
+gist_status gist_pool_create(gist_pool** out, int L, int64_t N, int k, int H, int d,
+                             gist_dtype dtype, void* storage, size_t storage_bytes);
+
+/* gist_pool_destroy — free the handle (never the storage).  NULL is a no-op. */
+gist_status gist_pool_destroy(gist_pool* pool);
+
+/*
+ * gist_pool_write — store n items' gist K/V for one layer (the offline
+ * extraction output of [GIST] 论文做了什么 / 在线的一次 attention).
+ *   ids      device int32 [n], destination item rows (each < N; out-of-range
+ *            ids are skipped on the device)
+ *   k_src    device [n][k][H][d], pool dtype; row i rotated at position
+ *            src_pos0 + i.  It is re-rotated to the canonical position 1 + i
+ *            (a rotation by 1 - src_pos0; a plain copy when src_pos0 == 1).
+ *   v_src    device [n][k][H][d], pool dtype, copied unchanged.
+ *   rope_base RoPE base used for the re-rotation.
+ * Duplicate ids in one call race (one of the writes wins).  n == 0 is a no-op.
+ */
+gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids, int64_t n,
+                            const void* k_src, const void* v_src, int src_pos0,
+                            float rope_base, void* stream);
+
+/*
+ * gist_attn_forward — one layer of online gist attention for P (item, query)
+ * pairs ([GIST] 在线的一次 attention; query-gist variant: 能不能再进一步).
+ * For pair p and query head h (KV head g = h / (Hq/H)) the keys are
+ *   [ item gist of item_ids[p] (k rows, from pool)
+ *   ; query gist of q_ids[p] (k' rows, from qpool; only if qpool != NULL)
+ *   ; RoPE(k_new[p][t][g], pos0 + t) for t < ell ]
+ * and the values are the same sequence of V rows.  Query token t (rotated at
+ * pos0 + t) sees every gist key and new keys 0..t (itself included); the
+ * output is softmax(scale * q·K^T) V over those keys ([KVC] Reusable-state).
+ *   pool      item gist pool; dtype, H and d of the call come from it
+ *   item_ids  device int32 [P]
+ *   q         device [P][ell][Hq][d]
+ *   k_new     device [P][ell][H][d]   (not yet rotated)
+ *   v_new     device [P][ell][H][d]
+ *   pos0      position of the first new token: k + 1 (k + k' + 1 with a
+ *             query gist), so the query-to-gist distance matches training
+ *   scale     softmax scale, normally 1/sqrt(d)
+ *   qpool     optional query-gist pool (same L, H, d, dtype); NULL for none
+ *   q_ids     device int32 [P] rows of qpool (ignored when qpool is NULL)
+ *   out       device [P][ell][Hq][d], pool dtype; must not alias the inputs
+ * Limits: 1 <= ell <= 1024, Hq % H == 0, Hq / H <= 32.  P == 0 is a no-op.
+ * bf16 with 2 <= ell <= 64 and k + k' + ell <= 128 runs the MFMA kernel;
+ * every other case runs the VALU kernel.
+ */
+gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
+                              int ell, int Hq, const void* q, const void* k_new,
+                              const void* v_new, int pos0, float rope_base, float scale,
+                              const gist_pool* qpool, const int32_t* q_ids, void* out,
+                              void* stream);
+
+/*
+ * paged_decode_workspace_bytes — fp32 workspace that paged_decode_attn needs
+ * for R requests, Hq query heads, block tables of max_blocks entries of
+ * block_size tokens and head size d.  Returns 0 for invalid shapes.
+ */
+size_t paged_decode_workspace_bytes(int R, int Hq, int max_blocks, int block_size, int d);
+
+/*
+ * paged_decode_attn — one decode step of R requests over a paged KV cache
+ * ([KVC] Reusable-state: K_{<=t} = [K_{<t}; k_t], o_t = softmax(q_t K^T
+ * /sqrt(d_k)) V; [SFX] section 6 problem 4: attention finds each logical
+ * block through a logical->physical table; [SFX] section 5: 256-token blocks).
+ *   k_cache, v_cache  device [n_blocks][H][block_size][d]; cached K is
+ *                     already rotated at its own position
+ *   block_table       device int32 [R][max_blocks]; logical token j of
+ *                     request r is row j % block_size of physical block
+ *                     block_table[r][j / block_size]
+ *   context_lens      device int32 [R], cached tokens per request
+ *                     (0 <= len <= max_blocks * block_size)
+ *   q                 device [R][Hq][d]; k_new, v_new device [R][H][d]
+ *   positions         device int32 [R], position of the new token
+ *   out               device [R][Hq][d]
+ *   workspace         device buffer of >= paged_decode_workspace_bytes(...)
+ *                     bytes, 16-byte aligned; contents are scratch
+ * The new token attends to the whole cache and to itself; k_new/v_new are
+ * not written back.  Limits: d in {64, 128}, Hq % H == 0, Hq / H <= 8,
+ * block_size a multiple of 16.  R == 0 is a no-op.
+ */
+gist_status paged_decode_attn(const void* k_cache, const void* v_cache, int64_t n_blocks,
+                              int block_size, const int32_t* block_table, int max_blocks,
+                              const int32_t* context_lens, int R, const void* q,
+                              const void* k_new, const void* v_new, const int32_t* positions,
+                              int Hq, int H, int d, gist_dtype dtype, float rope_base,
+                              float scale, void* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* gist_last_error — message of the last failed call on this thread ("" if none). */
+const char* gist_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GIST_ATTN_H */

@@ -219,10 +219,9 @@ def gather_logical(cache: np.ndarray, block_row, n_tokens: int, g: int) -> np.nd
     block_row[j // bs] at row j % bs.
     """
     bs = cache.shape[2]
-    rows = [cache[int(block_row[j // bs]), g, j % bs] for j in range(n_tokens)]
-    if not rows:
-        return np.zeros((0, cache.shape[3]), np.float64)
-    return np.asarray(np.stack(rows), np.float64)
+    j = np.arange(n_tokens)
+    blocks = np.asarray(block_row, dtype=np.int64)[j // bs]
+    return np.asarray(cache[blocks, g, j % bs], np.float64).reshape(n_tokens, cache.shape[3])
 
 
 def paged_decode(k_cache: np.ndarray, v_cache: np.ndarray, block_table,

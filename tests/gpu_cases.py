@@ -1,0 +1,126 @@
+"""Helpers shared by the GPU parity tests: build seeded inputs on the device,
+run the library through its C ABI (via the ctypes binding), copy the exact
+device values back and compare with the fp64 oracle."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import gist_compressed_kv_amd as G
+from gist_compressed_kv_amd import synth
+from oracle import gist_oracle as O
+
+TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-5}
+ROPE_BASE = 10000.0
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+class GistCase:
+    """One layer-set of gist attention inputs on the GPU."""
+
+    def __init__(self, layers, n_items, k, ell, hq, h, d, pairs, dtype, seed, kq=0,
+                 n_qrows=0, ids=None, q_ids=None, device="cuda"):
+        self.layers, self.n_items, self.k, self.ell = layers, n_items, k, ell
+        self.hq, self.h, self.d, self.pairs, self.dtype, self.kq = hq, h, d, pairs, dtype, kq
+        self.pool_t = synth.randn((layers, n_items, 2, h, k, d), synth.tensor_seed(seed, 1),
+                                  dtype, device)
+        self.pool = G.GistPool(self.pool_t)
+        if ids is None:
+            ids = torch.randint(0, n_items, (pairs,), generator=synth.generator(seed, "cpu"),
+                                dtype=torch.int32)
+        self.ids = ids.to(device=device, dtype=torch.int32)
+        self.qpool_t = self.qpool = self.q_ids = None
+        if kq:
+            self.qpool_t = synth.randn((layers, n_qrows, 2, h, kq, d), synth.tensor_seed(seed, 2),
+                                       dtype, device)
+            self.qpool = G.GistPool(self.qpool_t)
+            self.q_ids = q_ids.to(device=device, dtype=torch.int32)
+        self.q, self.kn, self.vn = [], [], []
+        for li in range(layers):
+            self.q.append(synth.randn((pairs, ell, hq, d), synth.tensor_seed(seed, 3, li), dtype, device))
+            self.kn.append(synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 4, li), dtype, device))
+            self.vn.append(synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 5, li), dtype, device))
+        self.pos0 = k + kq + 1
+        self.scale = 1.0 / math.sqrt(d)
+
+    def run(self, layer, out=None):
+        return G.gist_attn_forward(self.pool, layer, self.ids, self.q[layer], self.kn[layer],
+                                   self.vn[layer], self.pos0, ROPE_BASE, self.scale,
+                                   qpool=self.qpool, q_ids=self.q_ids, out=out)
+
+    def oracle(self, layer, sample):
+        """Oracle rows for the sampled pairs; only the referenced pool rows are
+        copied back."""
+        sample = np.asarray(sample)
+        idx = torch.as_tensor(sample, device=self.ids.device)
+        ids = self.ids[idx].long()
+        pool = f64(self.pool_t[layer][ids])[None]  # [1][S][2][H][k][d]
+        qpool = qids = None
+        if self.qpool is not None:
+            qr = self.q_ids[idx].long()
+            qpool = f64(self.qpool_t[layer][qr])[None]
+            qids = np.arange(len(sample))
+        return O.gist_attn_forward(pool, 0, np.arange(len(sample)), f64(self.q[layer][idx]),
+                                   f64(self.kn[layer][idx]), f64(self.vn[layer][idx]),
+                                   self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids)
+
+    def max_err(self, layer, out, sample):
+        ref = self.oracle(layer, sample)
+        got = f64(out[torch.as_tensor(np.asarray(sample), device=out.device)])
+        assert np.isfinite(got).all(), "non-finite output"
+        return float(np.abs(got - ref).max())
+
+
+class DecodeCase:
+    def __init__(self, n_blocks, h, bs, d, hq, lens, dtype, seed, table=None, max_blocks=None,
+                 device="cuda"):
+        self.kc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 11), dtype, device)
+        self.vc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 12), dtype, device)
+        R = len(lens)
+        if max_blocks is None:
+            max_blocks = max(1, -(-max(lens) // bs))
+        if table is None:
+            table = synth.block_table(R, max_blocks, n_blocks, seed, device)
+        self.table = table.to(device=device, dtype=torch.int32)
+        self.lens = torch.as_tensor(lens, dtype=torch.int32, device=device)
+        self.positions = self.lens + 1
+        self.q = synth.randn((R, hq, d), synth.tensor_seed(seed, 13), dtype, device)
+        self.kn = synth.randn((R, h, d), synth.tensor_seed(seed, 14), dtype, device)
+        self.vn = synth.randn((R, h, d), synth.tensor_seed(seed, 15), dtype, device)
+        self.scale = 1.0 / math.sqrt(d)
+        self.dtype = dtype
+
+    def run(self, out=None, workspace=None):
+        return G.paged_decode_attn(self.kc, self.vc, self.table, self.lens, self.q, self.kn,
+                                   self.vn, self.positions, ROPE_BASE, self.scale, out=out,
+                                   workspace=workspace)
+
+    def oracle(self, reqs=None):
+        R = self.q.shape[0]
+        reqs = np.arange(R) if reqs is None else np.asarray(reqs)
+        table = self.table.cpu().numpy()[reqs]
+        lens = self.lens.cpu().numpy()[reqs]
+        # copy back only the referenced blocks
+        used = sorted({int(b) for r in range(len(reqs))
+                       for b in table[r][: -(-int(lens[r]) // self.kc.shape[2])]} | {0})
+        remap = {b: i for i, b in enumerate(used)}
+        used_t = torch.as_tensor(used, device=self.kc.device)
+        kc = f64(self.kc[used_t])
+        vc = f64(self.vc[used_t])
+        t2 = np.vectorize(lambda b: remap.get(int(b), 0))(table)
+        idx = torch.as_tensor(reqs, device=self.q.device)
+        return O.paged_decode(kc, vc, t2, lens, f64(self.q[idx]), f64(self.kn[idx]),
+                              f64(self.vn[idx]), self.positions.cpu().numpy()[reqs], ROPE_BASE,
+                              self.scale)

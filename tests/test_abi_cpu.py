@@ -1,0 +1,169 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every
+symbol include/gist_attn.h declares, and validates arguments on the host
+before any HIP call (so every error path below runs with no device)."""
+
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+from gist_compressed_kv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gist_attn.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "byte_counts.json")
+
+BF16, F32 = _lib.GIST_BF16, _lib.GIST_F32
+FAKE = ctypes.c_void_p(1 << 20)  # an aligned address that is never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", text)) - {"sizeof"})
+
+
+def test_every_declared_symbol_is_exported_and_bound(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), names
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_pool_bytes_matches_printed_per_item_size(L):
+    g = json.load(open(GOLDEN))
+    for e in g["per_item_gist"]:
+        assert L.gist_pool_bytes(e["L"], 1, e["k"], e["H"], e["h"], BF16) == e["bytes"]
+    for e in g["pool_totals_100k_items_k8"]:
+        n = L.gist_pool_bytes(e["L"], e["items"], e["k"], e["H"], e["h"], BF16)
+        assert abs(n / 2**30 - e["gib"]) <= e["rel_tol"] * e["gib"]
+    assert L.gist_pool_bytes(1, 2, 8, 1, 64, F32) == 2 * 2 * 8 * 64 * 4
+    assert L.gist_pool_bytes(0, 2, 8, 1, 64, BF16) == 0
+    assert L.gist_pool_bytes(1, 2, 8, 1, 64, 7) == 0
+
+
+def _create(L, *args):
+    h = ctypes.c_void_p()
+    st = L.gist_pool_create(ctypes.byref(h), *args)
+    return st, h
+
+
+def test_pool_create_validation(L):
+    nbytes = L.gist_pool_bytes(2, 10, 8, 2, 64, BF16)
+    st, h = _create(L, 2, 10, 8, 2, 64, BF16, FAKE, nbytes)
+    assert st == _lib.GIST_OK and h.value
+    assert L.gist_pool_destroy(h) == _lib.GIST_OK
+    cases = [
+        ((2, 10, 8, 2, 64, BF16, None, nbytes), _lib.GIST_ERR_INVALID_ARG, "NULL"),
+        ((2, 10, 8, 2, 64, BF16, FAKE, nbytes - 2), _lib.GIST_ERR_INVALID_ARG, "storage_bytes"),
+        ((2, 10, 8, 2, 64, BF16, ctypes.c_void_p((1 << 20) + 8), nbytes),
+         _lib.GIST_ERR_INVALID_ARG, "aligned"),
+        ((2, 10, 8, 2, 96, BF16, FAKE, L.gist_pool_bytes(2, 10, 8, 2, 96, BF16)),
+         _lib.GIST_ERR_UNSUPPORTED, "head_dim"),
+        ((2, 10, 65, 2, 64, BF16, FAKE, L.gist_pool_bytes(2, 10, 65, 2, 64, BF16)),
+         _lib.GIST_ERR_UNSUPPORTED, "k must"),
+        ((0, 10, 8, 2, 64, BF16, FAKE, 0), _lib.GIST_ERR_INVALID_ARG, "positive"),
+        ((2, 10, 8, 2, 64, 5, FAKE, nbytes), _lib.GIST_ERR_INVALID_ARG, "dtype"),
+    ]
+    for args, code, msg in cases:
+        st, h = _create(L, *args)
+        assert st == code, (args, st)
+        assert h.value is None
+        assert msg in L.gist_last_error().decode()
+    assert L.gist_pool_create(None, 2, 10, 8, 2, 64, BF16, FAKE, nbytes) == _lib.GIST_ERR_INVALID_ARG
+    assert L.gist_pool_destroy(None) == _lib.GIST_OK
+
+
+def _pool(L, Lyr=2, N=10, k=8, H=2, d=64, dt=BF16):
+    st, h = _create(L, Lyr, N, k, H, d, dt, FAKE, L.gist_pool_bytes(Lyr, N, k, H, d, dt))
+    assert st == 0
+    return h
+
+
+def _fwd(L, pool, layer=0, P=4, ell=16, Hq=14, pos0=9, base=1e4, scale=0.125, qpool=None,
+         qids=None, ptr=FAKE, ids=FAKE):
+    return L.gist_attn_forward(pool, layer, ids, P, ell, Hq, ptr, ptr, ptr, pos0, base, scale,
+                               qpool, qids, ptr, None)
+
+
+def test_forward_validation(L):
+    pool = _pool(L)
+    try:
+        assert _fwd(L, None) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, layer=2) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert _fwd(L, pool, layer=-1) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert _fwd(L, pool, P=-1) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ell=0) == _lib.GIST_ERR_UNSUPPORTED
+        assert _fwd(L, pool, ell=1025) == _lib.GIST_ERR_UNSUPPORTED
+        assert _fwd(L, pool, Hq=13) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, Hq=1) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, Hq=66) == _lib.GIST_ERR_UNSUPPORTED
+        assert _fwd(L, pool, scale=0.0) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, scale=float("nan")) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, base=-1.0) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ids=None) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ptr=ctypes.c_void_p((1 << 20) + 4)) == _lib.GIST_ERR_INVALID_ARG
+        # an empty batch is accepted without touching the device
+        assert _fwd(L, pool, P=0, ptr=None, ids=None) == _lib.GIST_OK
+        # query-gist pool must match the item pool
+        other = _pool(L, d=128)
+        try:
+            assert _fwd(L, pool, qpool=other, qids=FAKE) == _lib.GIST_ERR_INVALID_ARG
+        finally:
+            L.gist_pool_destroy(other)
+        same = _pool(L, k=4)
+        try:
+            assert _fwd(L, pool, qpool=same, qids=None) == _lib.GIST_ERR_INVALID_ARG
+        finally:
+            L.gist_pool_destroy(same)
+    finally:
+        L.gist_pool_destroy(pool)
+
+
+def test_pool_write_validation(L):
+    pool = _pool(L)
+    try:
+        w = L.gist_pool_write
+        assert w(None, 0, FAKE, 1, FAKE, FAKE, 1, 1e4, None) == _lib.GIST_ERR_INVALID_ARG
+        assert w(pool, 5, FAKE, 1, FAKE, FAKE, 1, 1e4, None) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert w(pool, 0, FAKE, -1, FAKE, FAKE, 1, 1e4, None) == _lib.GIST_ERR_INVALID_ARG
+        assert w(pool, 0, None, 1, FAKE, FAKE, 1, 1e4, None) == _lib.GIST_ERR_INVALID_ARG
+        assert w(pool, 0, FAKE, 1, FAKE, FAKE, 1, 0.0, None) == _lib.GIST_ERR_INVALID_ARG
+        assert w(pool, 0, None, 0, None, None, 1, 1e4, None) == _lib.GIST_OK
+    finally:
+        L.gist_pool_destroy(pool)
+
+
+def _dec(L, R=2, Hq=4, H=2, d=64, bs=16, max_blk=4, nblk=8, dt=BF16, ws_bytes=None, ptr=FAKE,
+         scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = L.paged_decode_workspace_bytes(R, Hq, max_blk, bs, d)
+    return L.paged_decode_attn(ptr, ptr, nblk, bs, ptr, max_blk, ptr, R, ptr, ptr, ptr, ptr, Hq,
+                               H, d, dt, 1e4, scale, ptr, ptr, ws_bytes, None)
+
+
+def test_paged_decode_validation(L):
+    assert L.paged_decode_workspace_bytes(32, 32, 16, 256, 128) == 32 * 32 * 16 * 132 * 4
+    assert L.paged_decode_workspace_bytes(1, 1, 1, 16, 64) == 68 * 4
+    assert L.paged_decode_workspace_bytes(0, 4, 4, 16, 64) == 0
+    assert _dec(L, R=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, Hq=5) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, Hq=32, H=2) == _lib.GIST_ERR_UNSUPPORTED
+    assert _dec(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _dec(L, bs=24) == _lib.GIST_ERR_UNSUPPORTED
+    assert _dec(L, nblk=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, max_blk=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, dt=3) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, scale=-1.0) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, ws_bytes=16) == _lib.GIST_ERR_INVALID_ARG
+    assert "workspace too small" in L.gist_last_error().decode()
+    assert _dec(L, R=0, ptr=None) == _lib.GIST_OK

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP library (called through its C ABI) against the fp64 oracle.
+
+Bars: max-abs error <= 2e-2 for bf16 inputs (fp32 accumulation) and <= 1e-5
+for fp32, on every element checked.  Small cases are checked in full; the
+full-size workloads (100k-item pools, 24/28/32 layers) are checked on
+seeded samples of pairs/requests, every head and token of each.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_cases import TOL, DecodeCase, GistCase, f64, say
+from gist_compressed_kv_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _cleanup():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def check_gist(case, layers=None, sample=None, label=""):
+    layers = range(case.layers) if layers is None else layers
+    worst = 0.0
+    for li in layers:
+        out = case.run(li)
+        torch.cuda.synchronize()
+        s = np.arange(case.pairs) if sample is None else sample
+        err = case.max_err(li, out, s)
+        worst = max(worst, err)
+        assert err <= TOL[case.dtype], f"{label} layer {li}: max-abs err {err}"
+    say(f"{label}: max-abs err {worst:.3g}")
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# The tiny fp32 workload, in full
+# ---------------------------------------------------------------------------
+
+
+def test_tiny_fp32_workload():
+    wl = synth.TINY
+    case = GistCase(1, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    ids=torch.tensor([0, 1, 0, 1]))
+    check_gist(case, label="tiny fp32")
+
+
+# ---------------------------------------------------------------------------
+# MFMA path (bf16, 2 <= ell <= 64, k + k' + ell <= 128)
+# ---------------------------------------------------------------------------
+
+MFMA_SHAPES = [
+    # ell, k, kq, hq, h, d, pairs
+    (2, 8, 0, 14, 2, 64, 3),
+    (16, 8, 0, 4, 1, 64, 4),
+    (37, 8, 0, 14, 2, 64, 5),
+    (64, 8, 0, 14, 2, 64, 6),
+    (64, 8, 0, 64, 8, 128, 3),
+    (33, 1, 0, 8, 8, 64, 3),
+    (64, 64, 0, 8, 2, 64, 2),
+    (20, 8, 8, 16, 2, 128, 3),
+    (63, 5, 0, 7, 1, 64, 2),
+    (64, 24, 0, 32, 1, 128, 2),
+]
+
+
+@pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "ell%d_k%d_kq%d_hq%d_h%d_d%d" % s[:6])
+def test_mfma_path_shapes(shape):
+    ell, k, kq, hq, h, d, P = shape
+    qids = torch.arange(P) % 2 if kq else None
+    case = GistCase(2, 7, k, ell, hq, h, d, P, torch.bfloat16, 100 + ell, kq=kq, n_qrows=2,
+                    q_ids=qids)
+    check_gist(case, label=f"mfma {shape}")
+
+
+# ---------------------------------------------------------------------------
+# VALU path (ell = 1, long ell, fp32)
+# ---------------------------------------------------------------------------
+
+VALU_SHAPES = [
+    # ell, k, kq, hq, h, d, pairs, dtype
+    (1, 8, 0, 14, 2, 64, 5, torch.bfloat16),
+    (1, 8, 8, 64, 8, 128, 4, torch.bfloat16),
+    (1, 8, 8, 8, 4, 64, 4, torch.bfloat16),
+    (1, 3, 0, 3, 1, 128, 3, torch.bfloat16),
+    (100, 8, 0, 14, 2, 64, 2, torch.bfloat16),
+    (70, 64, 0, 4, 2, 128, 2, torch.bfloat16),
+    (1, 8, 0, 14, 2, 64, 3, torch.float32),
+    (7, 8, 8, 16, 2, 128, 3, torch.float32),
+    (64, 8, 0, 14, 2, 64, 2, torch.float32),
+    (5, 2, 0, 32, 1, 64, 2, torch.float32),
+]
+
+
+@pytest.mark.parametrize("shape", VALU_SHAPES,
+                         ids=lambda s: "ell%d_k%d_kq%d_hq%d_h%d_d%d_%s" % (*s[:6], str(s[7])[6:]))
+def test_valu_path_shapes(shape):
+    ell, k, kq, hq, h, d, P, dtype = shape
+    qids = (torch.arange(P) * 3) % 2 if kq else None
+    case = GistCase(2, 6, k, ell, hq, h, d, P, dtype, 200 + ell, kq=kq, n_qrows=2, q_ids=qids)
+    check_gist(case, label=f"valu {shape}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (sampled pairs)
+# ---------------------------------------------------------------------------
+
+
+def _ids(wl, device="cuda"):
+    return synth.item_ids_per_query(wl.queries, wl.pairs // wl.queries, wl.n_items, wl.seed, device)
+
+
+def test_single_layer_workload_all_pairs():
+    wl = synth.SINGLE_LAYER
+    case = GistCase(1, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    ids=_ids(wl))
+    check_gist(case, label="single layer, 500 pairs (all checked)")
+
+
+@pytest.mark.parametrize("wl", [synth.L24_B500, synth.L24_B2000], ids=["b500", "b2000"])
+def test_24_layer_workload_sampled(wl):
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed, ids=_ids(wl))
+    rng = np.random.default_rng(wl.seed)
+    sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 6)]))
+    check_gist(case, sample=sample, label=f"24 layers, {wl.pairs} pairs (sampled)")
+
+
+def test_wide_ell64_workload_sampled():
+    wl = synth.WIDE_ELL64
+    # two of the 28 layers, each with a full 100k-item pool layer
+    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    ids=_ids(wl))
+    sample = np.array([0, 1, 777, wl.pairs - 1])
+    check_gist(case, sample=sample, label="wide ell=64, 2000 pairs (sampled)")
+
+
+def test_wide_eos_query_gist_workload():
+    wl = synth.WIDE_EOS
+    qids = torch.arange(wl.pairs) // (wl.pairs // wl.queries)
+    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids)
+    rng = np.random.default_rng(7)
+    sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 62)]))
+    check_gist(case, sample=sample, label="wide EOS over item+query gist, 2000 pairs")
+
+
+# ---------------------------------------------------------------------------
+# Paged decode
+# ---------------------------------------------------------------------------
+
+
+def test_paged_decode_workload():
+    wl = synth.PAGED
+    n_blocks = wl.requests * wl.blocks_per_request
+    worst = 0.0
+    for layer in range(2):
+        case = DecodeCase(n_blocks, wl.h, wl.block_size, wl.d, wl.hq, [wl.context] * wl.requests,
+                          wl.dtype, synth.tensor_seed(wl.seed, 0, layer),
+                          table=synth.block_table(wl.requests, wl.blocks_per_request, n_blocks,
+                                                  wl.seed, "cuda"))
+        out = case.run()
+        torch.cuda.synchronize()
+        err = float(np.abs(f64(out) - case.oracle()).max())
+        worst = max(worst, err)
+        assert err <= TOL[wl.dtype], f"layer {layer}: {err}"
+        del case, out
+    say(f"paged decode 32x4096: max-abs err {worst:.3g}")
+
+
+DECODE_SHAPES = [
+    # hq, h, d, bs, lens, dtype
+    (32, 32, 128, 256, [4096, 0, 1, 255, 256, 257, 4000], torch.bfloat16),
+    (8, 2, 64, 16, [0, 15, 16, 17, 100, 333], torch.bfloat16),
+    (28, 4, 128, 64, [1, 64, 129, 900], torch.bfloat16),
+    (4, 4, 64, 32, [0, 31, 32, 77, 500], torch.float32),
+    (16, 2, 128, 256, [1, 300, 1000], torch.float32),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "hq%d_h%d_d%d_bs%d" % s[:4] + "_" + str(s[5])[6:])
+def test_paged_decode_shapes(shape):
+    hq, h, d, bs, lens, dtype = shape
+    max_blocks = -(-max(lens) // bs) + 1  # one spare table column
+    n_blocks = len(lens) * max_blocks + 5
+    case = DecodeCase(n_blocks, h, bs, d, hq, lens, dtype, 300 + d, max_blocks=max_blocks)
+    out = case.run()
+    torch.cuda.synchronize()
+    err = float(np.abs(f64(out) - case.oracle()).max())
+    say(f"decode {shape[:4]} {str(dtype)}: max-abs err {err:.3g}")
+    assert err <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# Error behaviour and determinism
+# ---------------------------------------------------------------------------
+
+
+def test_out_of_range_ids_give_nan_rows_only():
+    case = GistCase(1, 5, 8, 16, 14, 2, 64, 4, torch.bfloat16, 401,
+                    ids=torch.tensor([0, -1, 5, 3]))
+    out = case.run(0)
+    torch.cuda.synchronize()
+    o = f64(out)
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all()
+    assert np.isfinite(o[0]).all() and np.isfinite(o[3]).all()
+    assert case.max_err(0, out, [0, 3]) <= 2e-2
+    # the VALU path (ell = 1) does the same
+    case1 = GistCase(1, 5, 8, 1, 14, 2, 64, 3, torch.bfloat16, 402, ids=torch.tensor([7, 1, 2]))
+    o1 = f64(case1.run(0))
+    assert np.isnan(o1[0]).all() and np.isfinite(o1[1:]).all()
+
+
+def test_bad_block_table_entry_gives_nan_for_that_request():
+    case = DecodeCase(40, 2, 16, 64, 4, [30, 30, 30], torch.bfloat16, 403)
+    case.table[1, 1] = 1000
+    o = f64(case.run())
+    assert np.isnan(o[1]).all()
+    ok = [0, 2]
+    assert np.abs(o[ok] - case.oracle(ok)).max() <= 2e-2
+
+
+def test_bitwise_deterministic_reruns():
+    case = GistCase(1, 50, 8, 64, 14, 2, 64, 64, torch.bfloat16, 404)
+    a = case.run(0).clone()
+    b = case.run(0).clone()
+    assert torch.equal(a, b)
+    dc = DecodeCase(64, 4, 256, 128, 8, [1000, 2000, 17], torch.bfloat16, 405)
+    assert torch.equal(dc.run().clone(), dc.run().clone())
+
+
+def test_empty_batch_is_a_noop():
+    import gist_compressed_kv_amd as G
+    case = GistCase(1, 3, 8, 16, 4, 1, 64, 1, torch.bfloat16, 406)
+    e = torch.empty((0, 16, 4, 64), dtype=torch.bfloat16, device="cuda")
+    ek = torch.empty((0, 16, 1, 64), dtype=torch.bfloat16, device="cuda")
+    out = G.gist_attn_forward(case.pool, 0, torch.empty(0, dtype=torch.int32, device="cuda"), e,
+                              ek, ek)
+    assert out.shape == (0, 16, 4, 64)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("src_pos0", [1, 38])
+def test_pool_write_matches_oracle(dtype, src_pos0):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    L, N, k, h, d, n = 2, 9, 8, 2, 128, 4
+    pool_t = torch.zeros((L, N, 2, h, k, d), dtype=dtype, device="cuda")
+    pool = G.GistPool(pool_t)
+    ids = torch.tensor([3, 0, 8, 5], dtype=torch.int32, device="cuda")
+    ks = synth.randn((n, k, h, d), 500, dtype, "cuda")
+    vs = synth.randn((n, k, h, d), 501, dtype, "cuda")
+    G.gist_pool_write(pool, 1, ids, ks, vs, src_pos0=src_pos0, rope_base=10000.0)
+    torch.cuda.synchronize()
+    ref = O.pool_write(np.zeros((L, N, 2, h, k, d)), 1, ids.cpu().numpy(), f64(ks), f64(vs),
+                       src_pos0, 10000.0)
+    got = f64(pool_t)
+    # bf16 storage rounds the re-rotated K once (half an ulp, <= 2^-9 relative)
+    tol = 1e-6 if dtype == torch.float32 else 2.0 ** -8 * np.abs(ref).max()
+    assert np.abs(got - ref).max() <= tol
+    if src_pos0 == 1:
+        assert np.array_equal(got, ref)
