@@ -1,0 +1,259 @@
+"""Throughput of gist-compressed KV attention on one MI355X.
+
+A step is one full pass of the hot path over one batch: for every layer, one
+gist_attn_forward call (gather of each pair's gist K/V from that layer's
+100k-item pool, RoPE on Q and K_new, masked GQA softmax attention, output
+store).  The default workload is 24 layers, Hq=14, H=2 KV heads, head_dim 64,
+k=8 gist positions, ell=64 query tokens, 500 (item, query) pairs = 10 queries
+x 50 candidates, bf16, each layer with its own pool and its own Q/K/V/O.
+
+Prints one JSON line.  `value` is pairs/s for the whole pass with all inputs
+resident in HBM; `roofline` prices the dominant kernel's algorithmic bytes per
+launch against its average launch duration (HIP events on the launch stream);
+`cpu_baseline` times the fp64 oracle on a bounded sample on the host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+METRIC = "pairs/s + % of HBM peak, gist-KV attention (24L, GQA 14:2, k=8, ℓ=64)"
+KERNEL_SOURCE = os.path.join(ROOT, "gist_compressed_kv_amd", "csrc", "gist_forward.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "gist_fwd_mfma_d64_24L_b500_counters.json")
+
+
+def gist_bytes_per_pair_layer(wl) -> int:
+    """Algorithmic HBM bytes one (pair, layer) must move: the item's gist K/V
+    (and query gist, if any), Q in, K_new/V_new in, O out, the 4-byte id."""
+    b = wl.dtype.itemsize
+    gist = 2 * wl.k * wl.h * wl.d * b
+    qgist = 2 * wl.kq * wl.h * wl.d * b  # per pair; shared rows are re-read per pair
+    q = wl.ell * wl.hq * wl.d * b
+    kv_new = 2 * wl.ell * wl.h * wl.d * b
+    o = wl.ell * wl.hq * wl.d * b
+    ids = 4 * (2 if wl.kq else 1)
+    return gist + qgist + q + kv_new + o + ids
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="24L_b500",
+                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos", "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-pairs", type=int, default=500)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, only if they
+    were taken on the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != workload_name:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, wl, sample_pairs: int):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gist_oracle as O
+
+    sample = np.linspace(0, wl.pairs - 1, num=min(sample_pairs, wl.pairs)).astype(np.int64)
+    idx = torch.as_tensor(sample, device="cuda")
+
+    def f64(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    inputs = []
+    for li in range(wl.layers):
+        ids = case["ids"][idx].long()
+        pool = f64(case["pool"][li][ids])[None]
+        inputs.append((pool, f64(case["q"][li][idx]), f64(case["kn"][li][idx]),
+                       f64(case["vn"][li][idx])))
+    scale = 1.0 / math.sqrt(wl.d)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for pool, q, kn, vn in inputs:
+            O.gist_attn_forward(pool, 0, np.arange(len(sample)), q, kn, vn, wl.pos0, 10000.0, scale)
+        dt = time.perf_counter() - t0
+    return {"value": len(sample) / dt, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sample)} of {wl.pairs} pairs, all {wl.layers} layers, every head and "
+                      f"token; fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+
+
+def copy_probe(args):
+    """A plain device-to-device copy of 1 GiB: the reference whose HBM counter
+    readings (FETCH_SIZE, WRITE_SIZE) calibrate the counter runs."""
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"metric": "device copy", "value": 2 * n / dt / 1e9, "unit": "GB/s",
+                      "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                      "ms_per_step": dt * 1e3}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the gist path has no "
+              "cross-GPU step in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.workload == "copy":
+        copy_probe(args)
+        return
+
+    import gist_compressed_kv_amd as G
+    from gist_compressed_kv_amd import synth
+
+    wl = {"24L_b500": synth.L24_B500, "24L_b2000": synth.L24_B2000,
+          "1L_b500": synth.SINGLE_LAYER, "wide_ell64": synth.WIDE_ELL64,
+          "wide_eos": synth.WIDE_EOS}[args.workload]
+    dev = "cuda"
+    torch.cuda.init()
+
+    # ---- inputs, all resident in HBM ------------------------------------
+    print(f"[bench] generating inputs: {wl.name}", file=sys.stderr, flush=True)
+    pool_t = synth.randn((wl.layers, wl.n_items, 2, wl.h, wl.k, wl.d),
+                         synth.tensor_seed(wl.seed, 1), wl.dtype, dev)
+    pool = G.GistPool(pool_t)
+    ids = synth.item_ids_per_query(wl.queries, wl.pairs // wl.queries, wl.n_items, wl.seed, dev)
+    qpool = q_ids = None
+    if wl.kq:
+        qpool_t = synth.randn((wl.layers, wl.queries, 2, wl.h, wl.kq, wl.d),
+                              synth.tensor_seed(wl.seed, 2), wl.dtype, dev)
+        qpool = G.GistPool(qpool_t)
+        q_ids = (torch.arange(wl.pairs, device=dev) // (wl.pairs // wl.queries)).to(torch.int32)
+    # one distinct activation set per layer (wide workloads reuse one set:
+    # 4.8 GB per layer already dwarfs every cache)
+    n_sets = wl.layers if wl.d == 64 else 1
+    qs, kns, vns, outs = [], [], [], []
+    for li in range(n_sets):
+        qs.append(synth.randn((wl.pairs, wl.ell, wl.hq, wl.d), synth.tensor_seed(wl.seed, 3, li), wl.dtype, dev))
+        kns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 4, li), wl.dtype, dev))
+        vns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 5, li), wl.dtype, dev))
+        outs.append(torch.empty_like(qs[-1]))
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(wl.d)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for li in range(wl.layers):
+            si = li % n_sets
+            if events is not None:
+                events[li][0].record(stream)
+            G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
+                                qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
+            if events is not None:
+                events[li][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole passes -------------------------------------
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- per-launch kernel time, HIP events on the launch stream ------------
+    launch_ms = []
+    ev_steps = max(1, min(args.steps, 50))
+    for _ in range(ev_steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(wl.layers)]
+        step(evs)
+        torch.cuda.synchronize()
+        launch_ms.extend(a.elapsed_time(b) for a, b in evs)
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+
+    bytes_unit = gist_bytes_per_pair_layer(wl)
+    bytes_launch = bytes_unit * wl.pairs
+    achieved_gbps = bytes_launch / avg_launch_s / 1e9
+    pairs_per_s = wl.pairs / (ms_per_step / 1e3)
+    traffic = measured_traffic(args.workload)
+
+    res = {
+        "metric": METRIC,
+        "value": pairs_per_s,
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic: N(0,1) pools, Q/K/V; seeded item ids (50 distinct candidates per query)",
+        "config": {"workload": wl.name, "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
+                   "h": wl.h, "head_dim": wl.d, "k": wl.k, "k_query_gist": wl.kq, "ell": wl.ell,
+                   "pool_items": wl.n_items, "parallelism": "single GPU"},
+        "tokens_per_s": pairs_per_s * wl.ell,
+        "pass_hbm_gbps_algorithmic": bytes_launch * wl.layers / (ms_per_step / 1e3) / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
+                      ("gist_fwd_mfma<128>" if wl.ell > 1 else "gist_fwd_valu<bf16,128>"),
+            "achieved": achieved_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved_gbps / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "bytes_per_unit": bytes_unit,
+            "units_per_launch": wl.pairs,
+            "avg_launch_us": avg_launch_s * 1e6,
+        },
+    }
+    if not args.no_cpu_baseline:
+        case = {"pool": pool_t, "ids": ids, "q": qs, "kn": kns, "vn": vns}
+        if wl.kq or n_sets != wl.layers:
+            res["cpu_baseline"] = None
+        else:
+            print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+            res["cpu_baseline"] = cpu_baseline(case, wl, args.cpu_sample_pairs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -34,6 +34,7 @@ def compile_flags() -> list[str]:
         "-fPIC",
         "-Wall",
         "-Wno-unused-function",
+        "-Wno-pass-failed",
         # packed fp32 VALU ops are kept out of the generated code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     ]

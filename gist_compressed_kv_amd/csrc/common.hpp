@@ -60,31 +60,53 @@ __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
 }
 
 // ---------------------------------------------------------------------------
-// RoPE angles.  The host computes theta_i = base^(-2i/d) in double; the
-// device forms pos*theta_i in double, reduces it to [-pi, pi] (two-constant
-// Cody-Waite split of 2*pi) and evaluates fp32 sincosf on the remainder, so
-// angles of a few thousand radians keep ~1e-7 accuracy.
+// RoPE angles.  The host computes theta_i / (2*pi) = base^(-2i/d) / (2*pi)
+// (revolutions per position) in double.  The device forms pos * rev in double,
+// keeps the fractional revolution (exact in double, |f| <= 1/2) and feeds it
+// to the hardware v_sin_f32 / v_cos_f32, whose argument is in revolutions.
+// The fp64 reduction keeps the angle exact for positions in the thousands;
+// the hardware sine/cosine contribute an absolute error of a few 1e-7.
 // ---------------------------------------------------------------------------
 constexpr int kMaxHalfDim = 64;  // d <= 128
 
 struct RopeFreqs {
-  double theta[kMaxHalfDim];
+  double rev[kMaxHalfDim];  // revolutions per position of channel pair i
 };
 
 inline void make_rope_freqs(RopeFreqs& f, int d, float base) {
+  const double two_pi = 6.283185307179586476925286766559;
   for (int i = 0; i < kMaxHalfDim; ++i)
-    f.theta[i] = (i < d / 2) ? std::pow((double)base, -2.0 * (double)i / (double)d) : 0.0;
+    f.rev[i] = (i < d / 2) ? std::pow((double)base, -2.0 * (double)i / (double)d) / two_pi : 0.0;
 }
 
-__device__ __forceinline__ void rope_cos_sin(double pos, double theta, float& c, float& s) {
-  const double kTwoPiHi = 6.283185307179586232;     // nearest double to 2*pi
-  const double kTwoPiLo = 2.4492935982947064e-16;    // 2*pi - kTwoPiHi
-  const double kInvTwoPi = 0.15915494309189533577;
-  double a = pos * theta;
-  double n = rint(a * kInvTwoPi);
-  double r = fma(-n, kTwoPiHi, a);
-  r = fma(-n, kTwoPiLo, r);
-  sincosf((float)r, &s, &c);
+// rev[base + 8*chunk + e] for a lane-dependent chunk < NC, with base and e
+// known at compile time: every table read is a scalar load and the lane picks
+// its value with selects.  (Indexing the kernel-argument table with a
+// lane-dependent index would instead issue vector memory loads, which share
+// the wait counter with the data loads in flight.)
+__device__ __forceinline__ double sgpr_value(double v) {
+  // empty asm: keeps v a scalar-loaded value the optimizer cannot fold the
+  // selects below back into one lane-indexed (vector) load
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+template <int NC>
+__device__ __forceinline__ double rev_pick(const RopeFreqs& f, int base, int chunk, int e) {
+  double r = sgpr_value(f.rev[base + e]);
+#pragma unroll
+  for (int c = 1; c < NC; ++c) {
+    const double v = sgpr_value(f.rev[base + 8 * c + e]);
+    r = chunk == c ? v : r;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void rope_cos_sin(double pos, double rev, float& c, float& s) {
+  const double r = pos * rev;
+  const float f = (float)(r - rint(r));
+  s = __builtin_amdgcn_sinf(f);
+  c = __builtin_amdgcn_cosf(f);
 }
 
 // ---------------------------------------------------------------------------

@@ -73,6 +73,12 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// max of three floats: IEEE-754-2019 maximum (NaN-propagating), which gfx950
+// executes as one v_maximum3_f32 with no NaN canonicalization of its inputs
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 template <typename T>
 __device__ __forceinline__ T nan_value() {
   if constexpr (sizeof(T) == 2)
@@ -89,29 +95,64 @@ __device__ __forceinline__ T nan_value() {
 // chosen so that after the P·V product each lane holds, for every 32-channel
 // step s, the eight consecutive channels 32s + 8*(lane/16) .. +8 of its token:
 // the same layout the Q loads use, so output stores are 16-byte vectors.
-__device__ __forceinline__ int vt_row(int dt, int r) {
+__device__ __forceinline__ constexpr int vt_row(int dt, int r) {
   return 32 * (dt >> 1) + 8 * (r >> 2) + 4 * (dt & 1) + (r & 3);
 }
 
-template <int D>
-__global__ void __launch_bounds__(256)
-gist_fwd_mfma(const FwdArgs a, int nk_pad, int vs) {
+// Source row of key j (K or V part selected by `v`) of pair p, KV head g.
+__device__ __forceinline__ const bf16_t* key_row(const FwdArgs& a, const bf16_t* gK,
+                                                 const bf16_t* qK, int p, int g, int j, int kg,
+                                                 int D, bool v) {
+  if (j < a.k) return gK + (int64_t)((v ? a.H * a.k : 0) + j) * D;
+  if (j < kg) return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+  const bf16_t* base = (const bf16_t*)(v ? a.v_new : a.k_new);
+  return base + (((int64_t)p * a.ell + (j - kg)) * a.H + g) * D;
+}
+
+template <int D, int NKT>
+struct MfmaLds {
+  static constexpr int KS = D + 8;          // K row stride (elements): 16*odd bytes
+  static constexpr int VS = 16 * NKT + 8;   // Vᵀ row stride (elements)
+  static constexpr size_t bytes(int nk_pad) {
+    return ((size_t)nk_pad * KS + (size_t)D * VS) * sizeof(bf16_t);
+  }
+};
+
+// D: head_dim.  NKT: maximum number of 16-key tiles (keys <= 16*NKT).
+// QPF: query heads whose Q is kept in flight ahead of use.
+// GT: the GQA group size when known at compile time (0 = taken from the
+// arguments).  With GT > 0 the head loop is fully unrolled, so the compiler
+// knows exactly which loads each wait has to cover and never drains the
+// output stores (which share the vector-memory counter) before a Q load.
+//
+// LDS holds the pair's keys in reverse order: key κ (0 = first gist row) is
+// row nk_pad-1-κ of Ks and column nk_pad-1-κ of Vᵀ.  A wave visits its key
+// tiles from the causal edge backwards (j = 0 is the tile with the last
+// visible key), so tile j sits at a compile-time offset from one per-wave
+// base address, and only tiles j = 0 and j = 1 can hold keys that some token
+// of the wave may not see.
+template <int D, int NKT, int QPF, int GT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
+gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
-  constexpr int KS = D + 8;  // K row stride in LDS (elements): 16*odd bytes
-  constexpr int NS = D / 32;  // 32-channel k-steps of the Q·Kᵀ product
-  constexpr int NP = NS / 2;  // RoPE: step s pairs with step s + NP
-  constexpr int NDT = D / 16; // 16-channel tiles of the output
-  bf16_t* Ks = smem;               // [nk_pad][KS]
-  bf16_t* Vt = smem + nk_pad * KS; // [D][vs]
+  constexpr int KS = MfmaLds<D, NKT>::KS;
+  constexpr int VS = MfmaLds<D, NKT>::VS;
+  constexpr int NS = D / 32;   // 32-channel k-steps of the Q·Kᵀ product
+  constexpr int NP = NS / 2;   // RoPE: step s pairs with step s + NP
+  constexpr int NDT = D / 16;  // 16-channel tiles of the output
+  constexpr int CH = D / 16;   // K staging units per row (8 channels + partners)
+  constexpr int CV = D / 8;    // V staging units per key pair (8 channels)
+  constexpr int IT = D / 32;   // staging units per thread (nk_pad <= 128)
+  bf16_t* Ks = smem;                // [nk_pad][KS], reversed key order
+  bf16_t* Vt = smem + nk_pad * KS;  // [D][VS], reversed key order
 
   const int p = blockIdx.x / a.H;
   const int g = blockIdx.x - p * a.H;
   const int tid = threadIdx.x;
   const int kg = a.k + a.kq;
-  const int nk = kg + a.ell;
   const int ell = a.ell;
-  const int Hq = a.Hq, H = a.H, G = a.G;
-
+  const int nk = kg + ell;
+  const int Hq = a.Hq, G = GT > 0 ? GT : a.G;
   bf16_t* out = (bf16_t*)a.out;
 
   // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
@@ -130,38 +171,77 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad, int vs) {
     }
     return;
   }
-  const bf16_t* pool = (const bf16_t*)a.pool;
-  const int64_t rec_i = 2LL * H * a.k * D;
-  const bf16_t* gK = pool + a.pool_layer_off + (int64_t)item * rec_i + (int64_t)g * a.k * D;
-  const bf16_t* gV = gK + (int64_t)H * a.k * D;
+  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+                     (int64_t)g * a.k * D;
   const bf16_t* qK = nullptr;
-  const bf16_t* qV = nullptr;
-  if (a.kq) {
-    const int64_t rec_q = 2LL * H * a.kq * D;
-    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * rec_q +
+  if (a.kq)
+    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
          (int64_t)g * a.kq * D;
-    qV = qK + (int64_t)H * a.kq * D;
-  }
-  const bf16_t* knew = (const bf16_t*)a.k_new;
-  const bf16_t* vnew = (const bf16_t*)a.v_new;
 
-  // ---- stage K (rotating the new rows) ------------------------------------
-  constexpr int CH = D / 16;  // chunk pairs (8 channels + their RoPE partners)
-  for (int u = tid; u < nk_pad * CH; u += 256) {
+  // ---- issue every staging load of this thread ----------------------------
+  // Every load below is unconditional (out-of-range units read row 0 and
+  // are zeroed afterwards), so the compiler can count the loads in flight
+  // exactly and later waits never have to drain the Q prefetch.
+  uint4 klo[IT], khi[IT], v0[IT], v1[IT];
+  const int npairs = nk_pad >> 1;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int u = tid + 256 * it;
     const int j = u / CH, c = u - j * CH;
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-    if (j < nk) {
-      const bf16_t* src;
-      if (j < a.k) {
-        src = gK + (int64_t)j * D;
-      } else if (j < kg) {
-        src = qK + (int64_t)(j - a.k) * D;
-      } else {
-        src = knew + (((int64_t)p * ell + (j - kg)) * H + g) * D;
-      }
-      lo = *(const uint4*)(src + 8 * c);
-      hi = *(const uint4*)(src + D / 2 + 8 * c);
-      if (j >= kg) {
+    const bf16_t* src = key_row(a, gK, qK, p, g, j < nk ? j : 0, kg, D, false);
+    klo[it] = *(const uint4*)(src + 8 * c);
+    khi[it] = *(const uint4*)(src + D / 2 + 8 * c);
+    const int cv = u / npairs, jp = u - cv * npairs;
+    const int cvc = cv < CV ? cv : 0;
+    v0[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp < nk ? 2 * jp : 0, kg, D, true) + 8 * cvc);
+    v1[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp + 1 < nk ? 2 * jp + 1 : 0, kg, D, true) + 8 * cvc);
+  }
+
+  // keep the issue order: staging loads first, then the Q prefetch, so the
+  // wait before the LDS stores covers the staging loads only
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- issue the first QPF heads' Q loads of this wave ----------------------
+  // (wave index read through readfirstlane so every per-wave quantity below
+  // is a scalar and the tile loops branch on SGPRs)
+  // The token block of a wave rotates with the workgroup index: later blocks
+  // see more keys, and the rotation spreads that extra work over the SIMDs.
+  const int wv = __builtin_amdgcn_readfirstlane(((tid >> 6) + blockIdx.x) & 3);
+  const int lane = tid & 63;
+  const int n = lane & 15, q4 = lane >> 4;
+  const int t0 = 16 * wv;
+  const int t = t0 + n;
+  const bool wave_active = t0 < ell;
+  const bool tvalid = t < ell;
+  // rows past ell read the last valid token (finite values, never stored)
+  const int tl = tvalid ? t : ell - 1;
+  // Q and O of this pair: a wave-uniform base plus 32-bit lane offsets (the
+  // loads and stores then take the scalar-base addressing form)
+  const int64_t pair_off = (int64_t)p * ell * Hq * D;
+  const char* qpair = (const char*)((const bf16_t*)a.q + pair_off);
+  char* opair = (char*)(out + pair_off);
+  const uint32_t qlane = (uint32_t)(((tl * Hq + g * G) * D + 8 * q4) * 2);
+  const uint32_t olane = (uint32_t)(((t * Hq + g * G) * D + 8 * q4) * 2);
+  uint4 raw[QPF][NS];
+#pragma unroll
+  for (int i = 0; i < QPF; ++i) {
+    const int hq = i < G ? i : G - 1;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      raw[i][s] = *(const uint4*)(qpair + qlane + (uint32_t)(hq * D + 32 * s) * 2);
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- K: rotate the new rows, store; V: transpose, store (reversed) -------
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int u = tid + 256 * it;
+    const int j = u / CH, c = u - j * CH;
+    if (j < nk_pad) {
+      const uint4 zero = make_uint4(0, 0, 0, 0);
+      uint4 lo = j < nk ? klo[it] : zero, hi = j < nk ? khi[it] : zero;
+      if (j >= kg && j < nk) {
         float xl[8], xh[8], yl[8], yh[8];
         unpack8(lo, xl);
         unpack8(hi, xh);
@@ -169,152 +249,167 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad, int vs) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float cs, sn;
-          rope_cos_sin(pos, a.freqs.theta[8 * c + e], cs, sn);
+          rope_cos_sin(pos, rev_pick<CH>(a.freqs, 0, c, e), cs, sn);
           yl[e] = xl[e] * cs - xh[e] * sn;
           yh[e] = xh[e] * cs + xl[e] * sn;
         }
         lo = pack8_bf16(yl);
         hi = pack8_bf16(yh);
       }
+      bf16_t* dst = Ks + (nk_pad - 1 - j) * KS;
+      *(uint4*)(dst + 8 * c) = lo;
+      *(uint4*)(dst + D / 2 + 8 * c) = hi;
     }
-    *(uint4*)(Ks + j * KS + 8 * c) = lo;
-    *(uint4*)(Ks + j * KS + D / 2 + 8 * c) = hi;
-  }
-  // ---- stage V transposed, two keys per thread ----------------------------
-  {
-    const int npairs = nk_pad / 2;
-    constexpr int CV = D / 8;
-    for (int u = tid; u < npairs * CV; u += 256) {
-      const int c = u / npairs, jp = u - c * npairs;
-      uint4 v[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int j = 2 * jp + m;
-        v[m] = make_uint4(0, 0, 0, 0);
-        if (j < nk) {
-          const bf16_t* src;
-          if (j < a.k)
-            src = gV + (int64_t)j * D;
-          else if (j < kg)
-            src = qV + (int64_t)(j - a.k) * D;
-          else
-            src = vnew + (((int64_t)p * ell + (j - kg)) * H + g) * D;
-          v[m] = *(const uint4*)(src + 8 * c);
-        }
-      }
-      const uint32_t a0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-      const uint32_t a1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+    const int cv = u / npairs, jp = u - cv * npairs;
+    if (cv < CV) {
+      // keys 2jp, 2jp+1 land in reversed columns nk_pad-2-2jp (key 2jp+1)
+      // and nk_pad-1-2jp (key 2jp): one dword, high key in the low half
+      const uint4 zero = make_uint4(0, 0, 0, 0);
+      const uint4 w0 = 2 * jp < nk ? v0[it] : zero, w1 = 2 * jp + 1 < nk ? v1[it] : zero;
+      const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w};
+      const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w};
+      const int col = nk_pad - 2 - 2 * jp;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        // channel 8c+2e: low halves; channel 8c+2e+1: high halves
-        const uint32_t w0 = (a0[e] & 0xffffu) | (a1[e] << 16);
-        const uint32_t w1 = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-        *(uint32_t*)(Vt + (8 * c + 2 * e) * vs + 2 * jp) = w0;
-        *(uint32_t*)(Vt + (8 * c + 2 * e + 1) * vs + 2 * jp) = w1;
+        // channel 8cv+2e: low halves; channel 8cv+2e+1: high halves
+        *(uint32_t*)(Vt + (8 * cv + 2 * e) * VS + col) = (a1[e] & 0xffffu) | (a0[e] << 16);
+        *(uint32_t*)(Vt + (8 * cv + 2 * e + 1) * VS + col) = (a1[e] >> 16) | (a0[e] & 0xffff0000u);
       }
     }
   }
-  __syncthreads();
 
-  // ---- per wave: 16 query tokens, all G heads ------------------------------
-  const int wv = tid >> 6;
-  const int lane = tid & 63;
-  const int t0 = 16 * wv;
-  if (t0 >= ell) return;
-  const int n = lane & 15, q4 = lane >> 4;
-  const int t = t0 + n;
-  const bool tvalid = t < ell;
-  const int tlast = min(t0 + 15, ell - 1);
-  const int nkt = (kg + tlast + 1 + 15) >> 4;
-  const int vis_last = kg + t;  // key j visible to token t iff j <= kg + t
-
+  // ---- RoPE angles of this lane's token (channels 32s + 8*q4 + e), with the
+  // softmax scale and log2(e) folded in: logits come out ready for exp2 ----
+  const float sl2 = a.scale_log2;
   float qc[NP][8], qsn[NP][8];
   {
     const double pos = (double)(a.pos0 + t);
 #pragma unroll
     for (int s = 0; s < NP; ++s)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) rope_cos_sin(pos, a.freqs.theta[32 * s + 8 * q4 + e], qc[s][e], qsn[s][e]);
-  }
-
-  const bf16_t* qg = (const bf16_t*)a.q;
-  const float sl2 = a.scale_log2;
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    const int64_t row = (((int64_t)p * ell + t) * Hq + h) * D;
-    uint4 raw[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      raw[s] = tvalid ? *(const uint4*)(qg + row + 32 * s + 8 * q4) : make_uint4(0, 0, 0, 0);
-    bf16x8_t qf[NS];
-#pragma unroll
-    for (int s = 0; s < NP; ++s) {
-      float xl[8], xh[8], yl[8], yh[8];
-      unpack8(raw[s], xl);
-      unpack8(raw[s + NP], xh);
-#pragma unroll
       for (int e = 0; e < 8; ++e) {
-        yl[e] = xl[e] * qc[s][e] - xh[e] * qsn[s][e];
-        yh[e] = xh[e] * qc[s][e] + xl[e] * qsn[s][e];
+        float cs, sn;
+        rope_cos_sin(pos, rev_pick<4>(a.freqs, 32 * s, q4, e), cs, sn);
+        qc[s][e] = cs * sl2;
+        qsn[s][e] = sn * sl2;
       }
-      qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
-      qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
-    }
+  }
+  __syncthreads();
+  if (!wave_active) return;
 
-    float m = -INFINITY, lsum = 0.f;
-    f32x4_t o[NDT];
+  const int tlast = min(t0 + 15, ell - 1);
+  const int nkt = (kg + tlast + 1 + 15) >> 4;  // tiles holding any visible key
+  // reversed-order base rows of tile j = 0 (key tile nkt-1)
+  const int row0 = nk_pad - 16 * nkt;
+  const bf16_t* kbase = Ks + (row0 + n) * KS + 8 * q4;
+  const bf16_t* vbase = Vt + vt_row(0, n) * VS + row0 + 4 * q4;
+  // MFMA row m of tile j holds key 16*(nkt-1-j) + 15 - m; the S output slot
+  // r of lane group q4 is row m = 4*q4 + r.  Visibility: key <= kg + t.
+  const int lim = kg + t - (16 * (nkt - 1) + 15 - 4 * q4);  // key <= kg+t  <=>  -r - 16j <= lim
+  bool vis0[4], vis1[4];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int r = 0; r < 4; ++r) {
+    vis0[r] = -r <= lim;
+    vis1[r] = -r - 16 <= lim;
+  }
+  // ds_bpermute byte addresses of the lanes that hold the same token
+  const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
+  const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-    for (int kt = 0; kt < nkt; ++kt) {
-      f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
-      const bf16_t* krow = Ks + (16 * kt + n) * KS + 8 * q4;
+  // heads in groups of QPF; for compile-time G every loop below unrolls
+  constexpr int HB_STEP = QPF;
+  const int hb_end = GT > 0 ? GT : G;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8_t kf = *(const bf16x8_t*)(krow + 32 * s);
-        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sacc, 0, 0, 0);
-      }
-      float sv[4];
-      const int key0 = 16 * kt + 4 * q4;
+  for (int hb = 0; hb < (GT > 0 ? GT : 1 << 30); hb += HB_STEP) {
+    if (GT == 0 && hb >= hb_end) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = (key0 + i <= vis_last) ? sacc[i] * sl2 : -INFINITY;
-      float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m, tmax);
-      const float alpha = exp2f(m - mnew);
-      m = mnew;
-      bf16x4_t pf;
-      float psum = 0.f;
+    for (int i = 0; i < QPF; ++i) {
+      const int hh = hb + i;
+      if (hh < G) {
+        // rotate this head's Q (fp32 math, bf16 for the MFMA)
+        bf16x8_t qf[NS];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 pb = (__bf16)exp2f(sv[i] - mnew);
-        pf[i] = pb;
-        psum += (float)pb;  // the denominator sums the same rounded weights
-      }
-      lsum = lsum * alpha + psum;
-      const bf16_t* vrow = Vt + 16 * kt + 4 * q4;
+        for (int s = 0; s < NP; ++s) {
+          float xl[8], xh[8], yl[8], yh[8];
+          unpack8(raw[i][s], xl);
+          unpack8(raw[i][s + NP], xh);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        o[dt] *= alpha;
-        const bf16x4_t vf = *(const bf16x4_t*)(vrow + vt_row(dt, n) * vs);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
-      }
-    }
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    const float inv = 1.f / lsum;
-    if (tvalid) {
-      bf16_t* orow = out + row;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = o[2 * s][i] * inv;
-          v[4 + i] = o[2 * s + 1][i] * inv;
+          for (int e = 0; e < 8; ++e) {
+            yl[e] = xl[e] * qc[s][e] - xh[e] * qsn[s][e];
+            yh[e] = xh[e] * qc[s][e] + xl[e] * qsn[s][e];
+          }
+          qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
+          qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
         }
-        *(uint4*)(orow + 32 * s + 8 * q4) = pack8_bf16(v);
+        // refill the slot with the head QPF further on (clamped: always a
+        // valid row, so the load is unconditional)
+        {
+          const int hn = hh + QPF < G ? hh + QPF : G - 1;
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            raw[i][s] = *(const uint4*)(qpair + qlane + (uint32_t)(hn * D + 32 * s) * 2);
+        }
+
+        // logits (already scaled by scale*log2 e) Sᵀ = K·Qᵀ
+        f32x4_t sacc[NKT];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          if (j == 0 || j < nkt) {  // an active wave has at least one tile
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            if (j < 2) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[r] = (j == 0 ? vis0[r] : vis1[r]) ? 0.f : -INFINITY;
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              const bf16x8_t kf = *(const bf16x8_t*)(kbase + 16 * KS * j + 32 * s);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+            }
+            sacc[j] = acc;
+            mx = vmax3(mx, acc[0], acc[1]);
+            mx = vmax3(mx, acc[2], acc[3]);
+          }
+        }
+        // row max across the four lanes that share a token
+        mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
+        mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
+
+        // P = exp2(s - max) in bf16; O = P·V and the row sum (P against a
+        // ones tile) both on the matrix cores
+        f32x4_t o[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < NKT; ++j) {
+          if (j == 0 || j < nkt) {
+            const uint2 pk = make_uint2(
+                pack2_bf16(__builtin_amdgcn_exp2f(sacc[j][0] - mx), __builtin_amdgcn_exp2f(sacc[j][1] - mx)),
+                pack2_bf16(__builtin_amdgcn_exp2f(sacc[j][2] - mx), __builtin_amdgcn_exp2f(sacc[j][3] - mx)));
+            const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
+            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_row(dt, 0) - vt_row(0, 0)) * VS + 16 * j);
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
+            }
+          }
+        }
+        if (tvalid) {
+          const float inv = __builtin_amdgcn_rcpf(lacc[0]);
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            float v[8];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              v[r] = o[2 * s][r] * inv;
+              v[4 + r] = o[2 * s + 1][r] * inv;
+            }
+            *(uint4*)(opair + olane + (uint32_t)(hh * D + 32 * s) * 2) = pack8_bf16(v);
+          }
+        }
       }
     }
   }
@@ -408,7 +503,7 @@ gist_fwd_valu(const FwdArgs a) {
   // query rotation at pos0 + t for this lane's channel pairs
   float qcs[E2], qsn[E2];
 #pragma unroll
-  for (int e = 0; e < E2; ++e) rope_cos_sin((double)(a.pos0 + t), a.freqs.theta[lo + e], qcs[e], qsn[e]);
+  for (int e = 0; e < E2; ++e) rope_cos_sin((double)(a.pos0 + t), a.freqs.rev[lo + e], qcs[e], qsn[e]);
 
   float qv[MAXH][2 * E2];
   float m[MAXH], l[MAXH], o[MAXH][2 * E2];
@@ -459,7 +554,7 @@ gist_fwd_valu(const FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < E2; ++e) {
           float cs = qcs[e], sn = qsn[e];
-          if (tj != t) rope_cos_sin((double)(a.pos0 + tj), a.freqs.theta[lo + e], cs, sn);
+          if (tj != t) rope_cos_sin((double)(a.pos0 + tj), a.freqs.rev[lo + e], cs, sn);
           const float xl = kv[e], xh = kv[E2 + e];
           kv[e] = xl * cs - xh * sn;
           kv[E2 + e] = xh * cs + xl * sn;
@@ -529,9 +624,6 @@ using namespace gist;
 
 namespace {
 
-size_t mfma_lds_bytes(int d, int nk_pad, int vs) {
-  return ((size_t)nk_pad * (d + 8) + (size_t)d * vs) * sizeof(bf16_t);
-}
 
 template <typename T, int D>
 void launch_valu(const FwdArgs& a, hipStream_t s) {
@@ -611,14 +703,35 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
 
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  const int vs = nk_pad + 8;
-  const size_t lds = mfma_lds_bytes(d, nk_pad, vs);
-  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && kg + ell <= 128 && lds <= 65536) {
+  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {
     const dim3 grid((unsigned)((int64_t)P * H));
-    if (d == 64)
-      hipLaunchKernelGGL(gist_fwd_mfma<64>, grid, dim3(256), lds, s, a, nk_pad, vs);
-    else
-      hipLaunchKernelGGL(gist_fwd_mfma<128>, grid, dim3(256), lds, s, a, nk_pad, vs);
+    const int nkt = nk_pad / 16;
+    const int G = a.G;
+    if (d == 64) {
+      if (nkt <= 5) {
+        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
+        if (G == 7)
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 7>), grid, dim3(256), lds, s, a, nk_pad);
+        else if (G == 8)
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 8>), grid, dim3(256), lds, s, a, nk_pad);
+        else
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0>), grid, dim3(256), lds, s, a, nk_pad);
+      } else {
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0>), grid, dim3(256),
+                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
+      }
+    } else {
+      if (nkt <= 5) {
+        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
+        if (G == 8)
+          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8>), grid, dim3(256), lds, s, a, nk_pad);
+        else
+          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0>), grid, dim3(256), lds, s, a, nk_pad);
+      } else {
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0>), grid, dim3(256),
+                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
+      }
+    }
     return check_launch("gist_attn_forward(mfma)");
   }
   if (pool->dtype == GIST_BF16) {

@@ -134,7 +134,7 @@ decode_split(const DecodeArgs a) {
     const int fi = low ? ch0 : partner;  // frequency index of the pair
     float cs[E], sn[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) rope_cos_sin(pos, a.freqs.theta[fi + e], cs[e], sn[e]);
+    for (int e = 0; e < E; ++e) rope_cos_sin(pos, a.freqs.rev[fi + e], cs[e], sn[e]);
 #pragma unroll
     for (int hh = 0; hh < MAXG; ++hh) {
       if (hh < G) {
@@ -287,7 +287,7 @@ decode_combine(const DecodeArgs a) {
     const bool low = d < D / 2;
     const int partner = low ? d + D / 2 : d - D / 2;
     float cs, sn;
-    rope_cos_sin(pos, a.freqs.theta[low ? d : partner], cs, sn);
+    rope_cos_sin(pos, a.freqs.rev[low ? d : partner], cs, sn);
     const float qd = elem_f(qr, d), qp = elem_f(qr, partner);
     const float kd = elem_f(kr, d), kpn = elem_f(kr, partner);
     const float qrot = low ? qd * cs - qp * sn : qd * cs + qp * sn;

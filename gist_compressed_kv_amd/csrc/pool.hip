@@ -64,7 +64,7 @@ pool_write_kernel(T* __restrict__ pool, int64_t layer_off, int64_t N, int k, int
       xh = ksrc[src + hi];
     }
     float cs = 1.f, sn = 0.f;
-    if (src_pos0 != 1) rope_cos_sin(shift, freqs.theta[lo], cs, sn);
+    if (src_pos0 != 1) rope_cos_sin(shift, freqs.rev[lo], cs, sn);
     const float yl = xl * cs - xh * sn;
     const float yh = xh * cs + xl * sn;
     if constexpr (sizeof(T) == 2) {
