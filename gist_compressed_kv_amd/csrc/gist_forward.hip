@@ -29,6 +29,7 @@
 //    16-lane row with DPP.  This is the ell = 1 path (EOS over item gist +
 //    query gist + itself) and the fp32 path.
 #include <cfloat>
+#include <utility>
 
 #include "common.hpp"
 
@@ -91,6 +92,16 @@ __device__ __forceinline__ T nan_value() {
 // MFMA kernel (bf16)
 // ---------------------------------------------------------------------------
 
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 in order.
+template <class F, int... I>
+__device__ __forceinline__ void for_each_const_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void for_each_const(F&& f) {
+  for_each_const_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Row of the Vᵀ tile that MFMA row r of d-tile dt stands for.  The mapping is
 // chosen so that after the P·V product each lane holds, for every 32-channel
 // step s, the eight consecutive channels 32s + 8*(lane/16) .. +8 of its token:
@@ -113,8 +124,19 @@ template <int D, int NKT>
 struct MfmaLds {
   static constexpr int KS = D + 8;          // K row stride (elements): 16*odd bytes
   static constexpr int VS = 16 * NKT + 8;   // Vᵀ row stride (elements)
-  static constexpr size_t bytes(int nk_pad) {
+  // RoPE table: one row per new token, (cos, sin) of each channel pair,
+  // rows padded by 16 bytes so 16 lanes reading 16 consecutive rows (or 4
+  // rows x 4 chunks) hit distinct banks
+  static constexpr int CS_ROW = D / 2 * 2 + 4;  // floats per table row
+  static constexpr size_t kv_bytes(int nk_pad) {
     return ((size_t)nk_pad * KS + (size_t)D * VS) * sizeof(bf16_t);
+  }
+  // after the staging barrier the table's space becomes four per-wave
+  // transpose buffers of 16 rows x 2*D bytes
+  static constexpr size_t xpose_bytes = 4 * 16 * 2 * D;
+  static constexpr size_t bytes(int nk_pad, int ell) {
+    const size_t table = (size_t)ell * CS_ROW * sizeof(float);
+    return kv_bytes(nk_pad) + (table > xpose_bytes ? table : xpose_bytes);
   }
 };
 
@@ -143,8 +165,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   constexpr int CH = D / 16;   // K staging units per row (8 channels + partners)
   constexpr int CV = D / 8;    // V staging units per key pair (8 channels)
   constexpr int IT = D / 32;   // staging units per thread (nk_pad <= 128)
+  constexpr int CS_ROW = MfmaLds<D, NKT>::CS_ROW;
   bf16_t* Ks = smem;                // [nk_pad][KS], reversed key order
   bf16_t* Vt = smem + nk_pad * KS;  // [D][VS], reversed key order
+  float* cst = (float*)((char*)smem + MfmaLds<D, NKT>::kv_bytes(nk_pad));  // [ell][CS_ROW]
 
   const int p = blockIdx.x / a.H;
   const int g = blockIdx.x - p * a.H;
@@ -215,23 +239,59 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const bool tvalid = t < ell;
   // rows past ell read the last valid token (finite values, never stored)
   const int tl = tvalid ? t : ell - 1;
-  // Q and O of this pair: a wave-uniform base plus 32-bit lane offsets (the
-  // loads and stores then take the scalar-base addressing form)
+  // Q and O move between HBM and registers in a coalesced layout: lane l
+  // covers chunk l % CPR (8 channels, 16 bytes) of token row l / CPR, so
+  // every 128-byte line of a (token, head) row is read or written whole by
+  // one instruction.  A per-wave LDS buffer converts to and from the MFMA
+  // operand layout.  Addresses are a wave-uniform base plus 32-bit lane
+  // offsets (scalar-base addressing form).
+  constexpr int CPR = D / 8;   // 16-byte chunks per (token, head) row
+  constexpr int RPI = 64 / CPR; // token rows per instruction
+  const int cl = lane % CPR, rl = lane / CPR;
   const int64_t pair_off = (int64_t)p * ell * Hq * D;
   const char* qpair = (const char*)((const bf16_t*)a.q + pair_off);
   char* opair = (char*)(out + pair_off);
-  const uint32_t qlane = (uint32_t)(((tl * Hq + g * G) * D + 8 * q4) * 2);
-  const uint32_t olane = (uint32_t)(((t * Hq + g * G) * D + 8 * q4) * 2);
-  uint4 raw[QPF][NS];
+  uint32_t qlane[NS], olane[NS];
+  bool ovalid[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int tc = t0 + rl + RPI * s;
+    ovalid[s] = tc < ell;
+    qlane[s] = (uint32_t)((((tc < ell ? tc : ell - 1) * Hq + g * G) * D + 8 * cl) * 2);
+    olane[s] = (uint32_t)(((tc * Hq + g * G) * D + 8 * cl) * 2);
+  }
+  // Q ring held in native vectors (not the HIP uint4 struct) so it always
+  // stays in registers
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t raw[QPF][NS];
 #pragma unroll
   for (int i = 0; i < QPF; ++i) {
     const int hq = i < G ? i : G - 1;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      raw[i][s] = *(const uint4*)(qpair + qlane + (uint32_t)(hq * D + 32 * s) * 2);
+      raw[i][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2);
   }
 
   __builtin_amdgcn_sched_barrier(0);
+
+  // ---- RoPE table: wave w evaluates channel pairs [w*D/8, (w+1)*D/8) for
+  // position pos0 + lane (the pair index is wave-uniform, so the frequency
+  // comes from a scalar load), while the loads above are in flight --------
+  {
+    const int wraw = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tpos = tid & 63;
+    if (tpos < ell) {
+      const double pos = (double)(a.pos0 + tpos);
+#pragma unroll
+      for (int k = 0; k < D / 8; ++k) {
+        const int i = wraw * (D / 8) + k;
+        float cs, sn;
+        rope_cos_sin(pos, a.freqs.rev[i], cs, sn);
+        *(float2*)(cst + tpos * CS_ROW + 2 * i) = make_float2(cs, sn);
+      }
+    }
+  }
+  __syncthreads();
 
   // ---- K: rotate the new rows, store; V: transpose, store (reversed) -------
 #pragma unroll
@@ -245,13 +305,12 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         float xl[8], xh[8], yl[8], yh[8];
         unpack8(lo, xl);
         unpack8(hi, xh);
-        const double pos = (double)(a.pos0 + (j - kg));
+        const float* crow = cst + (j - kg) * CS_ROW + 16 * c;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float cs, sn;
-          rope_cos_sin(pos, rev_pick<CH>(a.freqs, 0, c, e), cs, sn);
-          yl[e] = xl[e] * cs - xh[e] * sn;
-          yh[e] = xh[e] * cs + xl[e] * sn;
+          const float2 cssn = *(const float2*)(crow + 2 * e);
+          yl[e] = xl[e] * cssn.x - xh[e] * cssn.y;
+          yh[e] = xh[e] * cssn.x + xl[e] * cssn.y;
         }
         lo = pack8_bf16(yl);
         hi = pack8_bf16(yh);
@@ -283,19 +342,34 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const float sl2 = a.scale_log2;
   float qc[NP][8], qsn[NP][8];
   {
-    const double pos = (double)(a.pos0 + t);
+    const float* crow = cst + tl * CS_ROW;
 #pragma unroll
     for (int s = 0; s < NP; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float cs, sn;
-        rope_cos_sin(pos, rev_pick<4>(a.freqs, 32 * s, q4, e), cs, sn);
-        qc[s][e] = cs * sl2;
-        qsn[s][e] = sn * sl2;
+        const float2 cssn = *(const float2*)(crow + 2 * (32 * s + 8 * q4 + e));
+        qc[s][e] = cssn.x * sl2;
+        qsn[s][e] = cssn.y * sl2;
       }
   }
   __syncthreads();
   if (!wave_active) return;
+
+  // per-wave transpose buffer (the RoPE table is dead past the barrier):
+  // 16 rows of 2*D bytes, chunk c of row r stored at chunk c ^ swz(r), which
+  // keeps both the coalesced and the MFMA-layout accesses free of bank
+  // conflicts
+  char* xb = (char*)cst + (tid >> 6) * (16 * 2 * D);
+  auto xpos = [](int r, int c) -> uint32_t {
+    const int swz = D == 64 ? (r >> 1) : r;
+    return (uint32_t)(r * 2 * D + ((c ^ swz) & (CPR - 1)) * 16);
+  };
+  uint32_t xw[NS], xr[NS];  // coalesced-layout and MFMA-layout slots
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    xw[s] = xpos(rl + RPI * s, cl);
+    xr[s] = xpos(n, 4 * s + q4);
+  }
 
   const int tlast = min(t0 + 15, ell - 1);
   const int nkt = (kg + tlast + 1 + 15) >> 4;  // tiles holding any visible key
@@ -317,23 +391,25 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-  // heads in groups of QPF; for compile-time G every loop below unrolls
-  constexpr int HB_STEP = QPF;
-  const int hb_end = GT > 0 ? GT : G;
+  // One query head: i is its Q ring slot, hh the head within the group.
+  auto head = [&](auto slot, const int hh) {
+    constexpr int i = decltype(slot)::value;
+        // Q tile to the MFMA layout through the wave's LDS buffer
+        uint4 qm[NS];
 #pragma unroll
-  for (int hb = 0; hb < (GT > 0 ? GT : 1 << 30); hb += HB_STEP) {
-    if (GT == 0 && hb >= hb_end) break;
+        for (int s = 0; s < NS; ++s) *(u32x4_t*)(xb + xw[s]) = raw[i][s];
 #pragma unroll
-    for (int i = 0; i < QPF; ++i) {
-      const int hh = hb + i;
-      if (hh < G) {
+        for (int s = 0; s < NS; ++s) {
+          const u32x4_t m = *(const u32x4_t*)(xb + xr[s]);
+          qm[s] = make_uint4(m.x, m.y, m.z, m.w);
+        }
         // rotate this head's Q (fp32 math, bf16 for the MFMA)
         bf16x8_t qf[NS];
 #pragma unroll
         for (int s = 0; s < NP; ++s) {
           float xl[8], xh[8], yl[8], yh[8];
-          unpack8(raw[i][s], xl);
-          unpack8(raw[i][s + NP], xh);
+          unpack8(qm[s], xl);
+          unpack8(qm[s + NP], xh);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             yl[e] = xl[e] * qc[s][e] - xh[e] * qsn[s][e];
@@ -348,7 +424,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
           const int hn = hh + QPF < G ? hh + QPF : G - 1;
 #pragma unroll
           for (int s = 0; s < NS; ++s)
-            raw[i][s] = *(const uint4*)(qpair + qlane + (uint32_t)(hn * D + 32 * s) * 2);
+            raw[i][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hn * D) * 2);
         }
 
         // logits (already scaled by scale*log2 e) Sᵀ = K·Qᵀ
@@ -397,7 +473,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
             }
           }
         }
-        if (tvalid) {
+        // O tile back to the coalesced layout through the same buffer, then
+        // whole-line non-temporal stores (the output is not read again here)
+        {
           const float inv = __builtin_amdgcn_rcpf(lacc[0]);
 #pragma unroll
           for (int s = 0; s < NS; ++s) {
@@ -407,10 +485,28 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
               v[r] = o[2 * s][r] * inv;
               v[4 + r] = o[2 * s + 1][r] * inv;
             }
-            *(uint4*)(opair + olane + (uint32_t)(hh * D + 32 * s) * 2) = pack8_bf16(v);
+            *(uint4*)(xb + xr[s]) = pack8_bf16(v);
+          }
+#pragma unroll
+          for (int s = 0; s < NS; ++s) {
+            const u32x4_t x = *(const u32x4_t*)(xb + xw[s]);
+            if (ovalid[s])
+              __builtin_nontemporal_store(x, (u32x4_t*)(opair + olane[s] + (uint32_t)(hh * D) * 2));
           }
         }
-      }
+        };
+
+  if constexpr (GT > 0) {
+    // compile-time group size: the whole head sequence unrolls, so the ring
+    // slot of every head and every wait count is known to the compiler
+    for_each_const<GT>([&](auto h) {
+      head(std::integral_constant<int, decltype(h)::value % QPF>{}, decltype(h)::value);
+    });
+  } else {
+    for (int hb = 0; hb < G; hb += QPF) {
+      for_each_const<QPF>([&](auto slot) {
+        if (hb + decltype(slot)::value < G) head(slot, hb + decltype(slot)::value);
+      });
     }
   }
 }
@@ -703,13 +799,13 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
 
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {
+  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 101 KiB per workgroup
     const dim3 grid((unsigned)((int64_t)P * H));
     const int nkt = nk_pad / 16;
     const int G = a.G;
     if (d == 64) {
       if (nkt <= 5) {
-        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
+        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad, ell);
         if (G == 7)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 7>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8)
@@ -718,18 +814,15 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
         hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0>), grid, dim3(256),
-                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
+                           (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     } else {
       if (nkt <= 5) {
-        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
-        if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8>), grid, dim3(256), lds, s, a, nk_pad);
-        else
-          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0>), grid, dim3(256), lds, s, a, nk_pad);
+        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad, ell);
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
         hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0>), grid, dim3(256),
-                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
+                           (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     }
     return check_launch("gist_attn_forward(mfma)");
