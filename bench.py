@@ -37,12 +37,13 @@ def gist_bytes_per_pair_layer(wl) -> int:
     (and query gist, if any), Q in, K_new/V_new in, O out, the 4-byte id."""
     b = wl.dtype.itemsize
     gist = 2 * wl.k * wl.h * wl.d * b
-    qgist = 2 * wl.kq * wl.h * wl.d * b  # per pair; shared rows are re-read per pair
+    # a query's gist rows are shared by its candidates: counted once per query
+    qgist = 2 * wl.kq * wl.h * wl.d * b * wl.queries / wl.pairs
     q = wl.ell * wl.hq * wl.d * b
     kv_new = 2 * wl.ell * wl.h * wl.d * b
     o = wl.ell * wl.hq * wl.d * b
     ids = 4 * (2 if wl.kq else 1)
-    return gist + qgist + q + kv_new + o + ids
+    return int(round(gist + qgist + q + kv_new + o + ids))
 
 
 def parse():
@@ -51,7 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos", "copy"])
+                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos", "paged",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
@@ -127,6 +129,77 @@ def copy_probe(args):
                       "ms_per_step": dt * 1e3}), flush=True)
 
 
+def decode_bytes_per_request_layer(wl) -> int:
+    """Algorithmic bytes of one decode step of one request in one layer: the
+    cached K and V it attends over, q, k_new, v_new, the output, and its
+    block-table row, context length and position."""
+    b = wl.dtype.itemsize
+    cache = 2 * wl.context * wl.h * wl.d * b
+    return (cache + wl.hq * wl.d * b + 2 * wl.h * wl.d * b + wl.hq * wl.d * b
+            + 4 * wl.blocks_per_request + 8)
+
+
+def paged_bench(args):
+    """One decode step of 32 requests over 4096 cached tokens in every one of
+    32 layers (each layer its own paged cache and its own inputs)."""
+    import torch
+
+    import gist_compressed_kv_amd as G
+    from gist_compressed_kv_amd import synth
+
+    wl = synth.PAGED
+    dev = "cuda"
+    nblk = wl.requests * wl.blocks_per_request
+    print(f"[bench] generating inputs: {wl.name}", file=sys.stderr, flush=True)
+    table = synth.block_table(wl.requests, wl.blocks_per_request, nblk, wl.seed, dev)
+    lens = torch.full((wl.requests,), wl.context, dtype=torch.int32, device=dev)
+    pos = lens + 1
+    layers = []
+    for li in range(wl.layers):
+        kc = synth.randn((nblk, wl.h, wl.block_size, wl.d), synth.tensor_seed(wl.seed, 11, li), wl.dtype, dev)
+        vc = synth.randn((nblk, wl.h, wl.block_size, wl.d), synth.tensor_seed(wl.seed, 12, li), wl.dtype, dev)
+        q = synth.randn((wl.requests, wl.hq, wl.d), synth.tensor_seed(wl.seed, 13, li), wl.dtype, dev)
+        kn = synth.randn((wl.requests, wl.h, wl.d), synth.tensor_seed(wl.seed, 14, li), wl.dtype, dev)
+        vn = synth.randn((wl.requests, wl.h, wl.d), synth.tensor_seed(wl.seed, 15, li), wl.dtype, dev)
+        layers.append((kc, vc, q, kn, vn, torch.empty_like(q)))
+    ws = torch.empty(G.paged_decode_workspace_bytes(wl.requests, wl.hq, wl.blocks_per_request,
+                                                    wl.block_size, wl.d), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for kc, vc, q, kn, vn, out in layers:
+            G.paged_decode_attn(kc, vc, table, lens, q, kn, vn, pos, 10000.0, None, out=out,
+                                workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # one call = the split kernel then the combine kernel
+    avg_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
+    bytes_unit = decode_bytes_per_request_layer(wl)
+    achieved = bytes_unit * wl.requests / avg_s / 1e9
+    print(json.dumps({
+        "metric": "paged decode tokens/s (32 requests x 4096 cached tokens, 32 layers)",
+        "value": wl.requests / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic N(0,1) caches, seeded block tables",
+        "config": {"workload": wl.name},
+        "roofline": {"bound": "hbm", "kernel": "decode_split + decode_combine",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_unit": bytes_unit, "units_per_launch": wl.requests,
+                     "avg_launch_us": avg_s * 1e6}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -138,6 +211,9 @@ def main():
 
     if args.workload == "copy":
         copy_probe(args)
+        return
+    if args.workload == "paged":
+        paged_bench(args)
         return
 
     import gist_compressed_kv_amd as G
@@ -174,38 +250,31 @@ def main():
     scale = 1.0 / math.sqrt(wl.d)
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
+    def step():
         for li in range(wl.layers):
             si = li % n_sets
-            if events is not None:
-                events[li][0].record(stream)
             G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
                                 qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
-            if events is not None:
-                events[li][1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     # ---- timed region: K whole passes -------------------------------------
+    # HIP events on the launch stream bracket the region; every launch in it
+    # runs the one kernel, back to back, so region time / launches is that
+    # kernel's average launch duration
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         step()
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-
-    # ---- per-launch kernel time, HIP events on the launch stream ------------
-    launch_ms = []
-    ev_steps = max(1, min(args.steps, 50))
-    for _ in range(ev_steps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(wl.layers)]
-        step(evs)
-        torch.cuda.synchronize()
-        launch_ms.extend(a.elapsed_time(b) for a, b in evs)
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
 
     bytes_unit = gist_bytes_per_pair_layer(wl)
     bytes_launch = bytes_unit * wl.pairs
