@@ -512,6 +512,229 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 }
 
 // ---------------------------------------------------------------------------
+// EOS kernel (bf16, ell = 1): one query token per pair, the GQA group's G
+// query heads are the MFMA columns
+// ---------------------------------------------------------------------------
+
+// cos/sin of every channel pair at the single query position, computed on the
+// host (one position for the whole launch), laid out per lane group: entry
+// [q4][s][e] is channel pair 32*s + 8*q4 + e, s < D/64
+struct EosRope {
+  float2 cs[kMaxHalfDim];
+};
+
+// One wave per (pair, KV head); four per workgroup, each with its own LDS
+// slice, so no workgroup barrier is involved.
+//   keys (reversed nothing; in order): gist tiles 0..ngt-1 hold the item gist
+//   then the query gist (kg = k + k' rows, zero padded); tile ngt holds the
+//   token's own key alone at row 0.  For the gist tiles the rotated Q is used;
+//   for the self tile both the key and the query sit at pos0, so their
+//   rotations cancel and the unrotated Q and K_new give the same logit.
+// NGT: maximum number of gist tiles (kg <= 16*NGT).
+template <int D, int NGT>
+__global__ void __launch_bounds__(256)
+gist_fwd_eos(const FwdArgs a, const EosRope rc) {
+  constexpr int NS = D / 32;
+  constexpr int NP = NS / 2;
+  constexpr int NDT = D / 16;
+  constexpr int NT = NGT + 1;          // gist tiles + self tile
+  constexpr int VS = 16 * NT + 8;      // Vᵀ row stride (elements)
+  constexpr int CV = D / 8;
+  __shared__ __align__(16) bf16_t vts[4][D * VS];
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
+
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, q4 = lane >> 4;
+  const int unit = blockIdx.x * 4 + wv;
+  if (unit >= a.P * a.H) return;
+  const int p = unit / a.H, g = unit - (unit / a.H) * a.H;
+  const int G = a.G, Hq = a.Hq;
+  const int kg = a.k + a.kq;
+  const int ngt = (kg + 15) >> 4;
+  bf16_t* out = (bf16_t*)a.out;
+  const int64_t orow0 = ((int64_t)p * Hq + (int64_t)g * G) * D;
+
+  const int32_t item = a.item_ids[p];
+  int32_t qid = 0;
+  bool bad = item < 0 || item >= a.N;
+  if (a.kq) {
+    qid = a.q_ids[p];
+    bad = bad || qid < 0 || qid >= a.qN;
+  }
+  if (bad) {
+    for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<bf16_t>();
+    return;
+  }
+  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+                     (int64_t)g * a.k * D;
+  const bf16_t* qK = gK;
+  if (a.kq)
+    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+         (int64_t)g * a.kq * D;
+  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
+  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
+  // gist key j (< kg): K row, and its V row at +H*k*D (item) or +H*k'*D (query)
+  auto gist_row = [&](int j, bool v) -> const bf16_t* {
+    if (j < a.k) return gK + (int64_t)((v ? a.H * a.k : 0) + j) * D;
+    return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+  };
+
+  // ---- loads, all unconditional (clamped rows, zeroed afterwards) ----------
+  u32x4_t kr[NGT][NS];
+#pragma unroll
+  for (int kt = 0; kt < NGT; ++kt) {
+    const int j = 16 * kt + n;
+    const bf16_t* row = gist_row(j < kg ? j : 0, false);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kr[kt][s] = *(const u32x4_t*)(row + 32 * s + 8 * q4);
+  }
+  u32x4_t ks[NS], qraw[NS];
+  const int hcol = n < G ? n : G - 1;
+  const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G + hcol) * D;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    ks[s] = *(const u32x4_t*)(knew + 32 * s + 8 * q4);
+    qraw[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * q4);
+  }
+  // V rows of key pairs (2jp, 2jp+1), chunk cv: the gist keys, then the self
+  // key at column 16*NGT
+  constexpr int NPAIR = 8 * NT;
+  constexpr int VIT = (NPAIR * CV + 63) / 64;
+  u32x4_t va[VIT], vb[VIT];
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int u = lane + 64 * it;
+    const int jp = u % NPAIR, cv = (u / NPAIR) % CV;
+    const int j0 = 2 * jp, j1 = 2 * jp + 1;
+    auto vrow = [&](int j) -> const bf16_t* {
+      if (j == 16 * NGT) return vnew;
+      return gist_row(j < kg ? j : 0, true);
+    };
+    va[it] = *(const u32x4_t*)(vrow(j0) + 8 * cv);
+    vb[it] = *(const u32x4_t*)(vrow(j1) + 8 * cv);
+  }
+
+  // ---- V transposed into this wave's LDS slice ----------------------------
+  bf16_t* Vt = vts[wv];
+#pragma unroll
+  for (int it = 0; it < VIT; ++it) {
+    const int u = lane + 64 * it;
+    if (u < NPAIR * CV) {
+      const int jp = u % NPAIR, cv = u / NPAIR;
+      const int j0 = 2 * jp, j1 = 2 * jp + 1;
+      const bool ok0 = j0 < kg || j0 == 16 * NGT, ok1 = j1 < kg || j1 == 16 * NGT;
+      const u32x4_t zero = {0u, 0u, 0u, 0u};
+      const u32x4_t w0 = ok0 ? va[it] : zero, w1 = ok1 ? vb[it] : zero;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        *(uint32_t*)(Vt + (8 * cv + 2 * e) * VS + j0) = (w0[e] & 0xffffu) | (w1[e] << 16);
+        *(uint32_t*)(Vt + (8 * cv + 2 * e + 1) * VS + j0) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
+      }
+    }
+  }
+
+  // ---- rotate Q at pos0 (scale*log2 e folded in); unrotated Q for the self
+  // tile is scaled the same way ---------------------------------------------
+  const float sl2 = a.scale_log2;
+  bf16x8_t qf[NS], qu[NS];
+#pragma unroll
+  for (int s = 0; s < NP; ++s) {
+    float xl[8], xh[8], yl[8], yh[8], ul[8], uh[8];
+    unpack8(make_uint4(qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w), xl);
+    unpack8(make_uint4(qraw[s + NP].x, qraw[s + NP].y, qraw[s + NP].z, qraw[s + NP].w), xh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float2 c = rc.cs[(q4 * NP + s) * 8 + e];
+      yl[e] = (xl[e] * c.x - xh[e] * c.y) * sl2;
+      yh[e] = (xh[e] * c.x + xl[e] * c.y) * sl2;
+      ul[e] = xl[e] * sl2;
+      uh[e] = xh[e] * sl2;
+    }
+    qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
+    qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
+    qu[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(ul));
+    qu[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(uh));
+  }
+
+  // ---- logits Sᵀ[key][head] ---------------------------------------------------
+  f32x4_t sacc[NT];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < NGT; ++kt) {
+    if (kt < ngt) {
+      f32x4_t acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = (16 * kt + 4 * q4 + r < kg) ? 0.f : -INFINITY;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4_t w = (16 * kt + n < kg) ? kr[kt][s] : u32x4_t{0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qf[s], acc,
+                                                     0, 0, 0);
+      }
+      sacc[kt] = acc;
+      mx = vmax3(mx, acc[0], acc[1]);
+      mx = vmax3(mx, acc[2], acc[3]);
+    }
+  }
+  {
+    f32x4_t acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = (q4 == 0 && r == 0) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4_t w = n == 0 ? ks[s] : u32x4_t{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qu[s], acc, 0,
+                                                   0, 0);
+    }
+    sacc[NGT] = acc;
+    mx = vmax3(mx, acc[0], acc[1]);
+    mx = vmax3(mx, acc[2], acc[3]);
+  }
+  const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
+  mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
+  mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
+
+  // ---- P = exp2(s - max); O = P·V and row sums on the matrix cores ----------
+  const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    if (kt < ngt || kt == NGT) {
+      const uint2 pk = make_uint2(
+          pack2_bf16(__builtin_amdgcn_exp2f(sacc[kt][0] - mx), __builtin_amdgcn_exp2f(sacc[kt][1] - mx)),
+          pack2_bf16(__builtin_amdgcn_exp2f(sacc[kt][2] - mx), __builtin_amdgcn_exp2f(sacc[kt][3] - mx)));
+      const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
+      lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
+      const bf16_t* vrow = Vt + vt_row(0, n) * VS + 16 * kt + 4 * q4;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x4_t vf = *(const bf16x4_t*)(vrow + (vt_row(dt, 0) - vt_row(0, 0)) * VS);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
+      }
+    }
+  }
+  if (n < G) {
+    const float inv = __builtin_amdgcn_rcpf(lacc[0]);
+    bf16_t* orow = out + orow0 + (int64_t)n * D + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float v[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = o[2 * s][r] * inv;
+        v[4 + r] = o[2 * s + 1][r] * inv;
+      }
+      *(uint4*)(orow + 32 * s) = pack8_bf16(v);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // VALU kernel (any ell; bf16 or fp32)
 // ---------------------------------------------------------------------------
 
@@ -826,6 +1049,27 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
       }
     }
     return check_launch("gist_attn_forward(mfma)");
+  }
+  if (pool->dtype == GIST_BF16 && ell == 1 && a.G <= 16 && kg <= 32) {
+    // one position for the whole launch: its cos/sin come from the host
+    EosRope rc;
+    const int np = d / 64;
+    for (int q4 = 0; q4 < 4; ++q4)
+      for (int s2 = 0; s2 < np; ++s2)
+        for (int e = 0; e < 8; ++e) {
+          const int i = 32 * s2 + 8 * q4 + e;
+          const double ang = (double)pos0 * std::pow((double)rope_base, -2.0 * i / (double)d);
+          rc.cs[(q4 * np + s2) * 8 + e] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+    const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
+    if (d == 64) {
+      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<64, 1>), grid, dim3(256), 0, s, a, rc);
+      else hipLaunchKernelGGL((gist_fwd_eos<64, 2>), grid, dim3(256), 0, s, a, rc);
+    } else {
+      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<128, 1>), grid, dim3(256), 0, s, a, rc);
+      else hipLaunchKernelGGL((gist_fwd_eos<128, 2>), grid, dim3(256), 0, s, a, rc);
+    }
+    return check_launch("gist_attn_forward(eos)");
   }
   if (pool->dtype == GIST_BF16) {
     if (d == 64) launch_valu<bf16_t, 64>(a, s);

@@ -81,8 +81,14 @@ def test_mfma_path_shapes(shape):
 # VALU path (ell = 1, long ell, fp32)
 # ---------------------------------------------------------------------------
 
+# ell = 1 in bf16 with G <= 16 and k + k' <= 32 runs the MFMA EOS kernel;
+# the rest of this list runs the VALU kernel
 VALU_SHAPES = [
     # ell, k, kq, hq, h, d, pairs, dtype
+    (1, 12, 8, 16, 2, 128, 3, torch.bfloat16),
+    (1, 20, 0, 8, 1, 64, 3, torch.bfloat16),
+    (1, 8, 0, 34, 2, 64, 3, torch.bfloat16),
+    (1, 40, 0, 4, 2, 64, 2, torch.bfloat16),
     (1, 8, 0, 14, 2, 64, 5, torch.bfloat16),
     (1, 8, 8, 64, 8, 128, 4, torch.bfloat16),
     (1, 8, 8, 8, 4, 64, 4, torch.bfloat16),
