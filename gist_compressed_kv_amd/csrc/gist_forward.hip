@@ -120,16 +120,30 @@ __device__ __forceinline__ const bf16_t* key_row(const FwdArgs& a, const bf16_t*
   return base + (((int64_t)p * a.ell + (j - kg)) * a.H + g) * D;
 }
 
+// Vᵀ element (channel row r, key column c) sits at r*VS + 4*(r >> 3) + c,
+// with VS = 16 or 48 (mod 64) elements.  LDS serves 128 bytes per clock from
+// 32 four-byte banks, so the sixteen lanes of one 8-byte read phase (MFMA
+// rows n = 0..15 of one key group, same column) must cover all 32 banks.
+// Those lanes read rows r = R + 8b + a (a, b < 4; R a per-d-tile constant,
+// see vt_row): the row stride (8 or 24 dwords mod 32) puts a on banks
+// 0/8/16/24 and the 4-element pad per 8-row block puts b on 0/2/4/6.
+__device__ __forceinline__ constexpr int vt_off(int r, int c, int vs) {
+  return r * vs + 4 * (r >> 3) + c;
+}
+__device__ __host__ constexpr int vt_stride(int keys) {
+  return (keys % 64 == 16 || keys % 64 == 48) ? keys : keys + 16;
+}
+
 template <int D, int NKT>
 struct MfmaLds {
   static constexpr int KS = D + 8;          // K row stride (elements): 16*odd bytes
-  static constexpr int VS = 16 * NKT + 8;   // Vᵀ row stride (elements)
+  static constexpr int VS = vt_stride(16 * NKT);  // Vᵀ row stride (elements)
   // RoPE table: one row per new token, (cos, sin) of each channel pair,
   // rows padded by 16 bytes so 16 lanes reading 16 consecutive rows (or 4
   // rows x 4 chunks) hit distinct banks
   static constexpr int CS_ROW = D / 2 * 2 + 4;  // floats per table row
   static constexpr size_t kv_bytes(int nk_pad) {
-    return ((size_t)nk_pad * KS + (size_t)D * VS) * sizeof(bf16_t);
+    return ((size_t)nk_pad * KS + (size_t)D * VS + 4 * (D / 8)) * sizeof(bf16_t);
   }
   // after the staging barrier the table's space becomes four per-wave
   // transpose buffers of 16 rows x 2*D bytes
@@ -331,8 +345,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // channel 8cv+2e: low halves; channel 8cv+2e+1: high halves
-        *(uint32_t*)(Vt + (8 * cv + 2 * e) * VS + col) = (a1[e] & 0xffffu) | (a0[e] << 16);
-        *(uint32_t*)(Vt + (8 * cv + 2 * e + 1) * VS + col) = (a1[e] >> 16) | (a0[e] & 0xffff0000u);
+        const int r = 8 * cv + 2 * e;
+        *(uint32_t*)(Vt + vt_off(r, col, VS)) = (a1[e] & 0xffffu) | (a0[e] << 16);
+        *(uint32_t*)(Vt + vt_off(r + 1, col, VS)) = (a1[e] >> 16) | (a0[e] & 0xffff0000u);
       }
     }
   }
@@ -356,13 +371,14 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   if (!wave_active) return;
 
   // per-wave transpose buffer (the RoPE table is dead past the barrier):
-  // 16 rows of 2*D bytes, chunk c of row r stored at chunk c ^ swz(r), which
-  // keeps both the coalesced and the MFMA-layout accesses free of bank
-  // conflicts
+  // 16 rows of 2*D bytes, chunk c of row r stored at chunk c ^ r.  A 16-byte
+  // access is served eight lanes per clock; the coalesced side has those
+  // lanes on one row (distinct chunks), the MFMA side has them on rows
+  // 0..7 of one chunk, which the XOR sends to eight distinct chunks: both
+  // sides are free of bank conflicts.
   char* xb = (char*)cst + (tid >> 6) * (16 * 2 * D);
   auto xpos = [](int r, int c) -> uint32_t {
-    const int swz = D == 64 ? (r >> 1) : r;
-    return (uint32_t)(r * 2 * D + ((c ^ swz) & (CPR - 1)) * 16);
+    return (uint32_t)(r * 2 * D + ((c ^ r) & (CPR - 1)) * 16);
   };
   uint32_t xw[NS], xr[NS];  // coalesced-layout and MFMA-layout slots
 #pragma unroll
@@ -376,7 +392,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // reversed-order base rows of tile j = 0 (key tile nkt-1)
   const int row0 = nk_pad - 16 * nkt;
   const bf16_t* kbase = Ks + (row0 + n) * KS + 8 * q4;
-  const bf16_t* vbase = Vt + vt_row(0, n) * VS + row0 + 4 * q4;
+  // (the block pad of vt_off is the same for every d-tile: vt_row(dt, n) >> 3
+  // differs from vt_row(0, n) >> 3 by 4*(dt >> 1), folded into the offsets)
+  const bf16_t* vbase = Vt + vt_off(vt_row(0, n), row0 + 4 * q4, VS);
   // MFMA row m of tile j holds key 16*(nkt-1-j) + 15 - m; the S output slot
   // r of lane group q4 is row m = 4*q4 + r.  Visibility: key <= kg + t.
   const int lim = kg + t - (16 * (nkt - 1) + 15 - 4 * q4);  // key <= kg+t  <=>  -r - 16j <= lim
@@ -468,7 +486,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
             lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-              const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_row(dt, 0) - vt_row(0, 0)) * VS + 16 * j);
+              const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
               o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
             }
           }
@@ -959,6 +977,21 @@ void launch_valu(const FwdArgs& a, hipStream_t s) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// Compute units of the current device, queried once per device (a lookup
+// that fails counts as 256, the MI355X figure).
+int device_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids,
@@ -1022,17 +1055,26 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
 
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 101 KiB per workgroup
+  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 104 KiB per workgroup
     const dim3 grid((unsigned)((int64_t)P * H));
     const int nkt = nk_pad / 16;
     const int G = a.G;
     if (d == 64) {
       if (nkt <= 5) {
         const size_t lds = MfmaLds<64, 5>::bytes(nk_pad, ell);
-        if (G == 7)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 7>), grid, dim3(256), lds, s, a, nk_pad);
+        // When the whole grid is resident at once (four workgroups per CU),
+        // every workgroup issues its staging loads at the same moment and a
+        // deeper Q prefetch only delays them: prefetch one head ahead.  With
+        // several generations of workgroups, two heads ahead.
+        const bool one_generation = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
+        if (G == 7 && one_generation)
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7>), grid, dim3(256), lds, s, a, nk_pad);
+        else if (G == 7)
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7>), grid, dim3(256), lds, s, a, nk_pad);
+        else if (G == 8 && one_generation)
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 8>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8>), grid, dim3(256), lds, s, a, nk_pad);
         else
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0>), grid, dim3(256), lds, s, a, nk_pad);
       } else {

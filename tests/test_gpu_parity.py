@@ -65,6 +65,7 @@ MFMA_SHAPES = [
     (20, 8, 8, 16, 2, 128, 3),
     (63, 5, 0, 7, 1, 64, 2),
     (64, 24, 0, 32, 1, 128, 2),
+    (48, 8, 0, 16, 2, 64, 5),
 ]
 
 
@@ -134,6 +135,15 @@ def test_24_layer_workload_sampled(wl):
     rng = np.random.default_rng(wl.seed)
     sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 6)]))
     check_gist(case, sample=sample, label=f"24 layers, {wl.pairs} pairs (sampled)")
+
+
+@pytest.mark.parametrize("hq", [14, 16], ids=["G7", "G8"])
+def test_several_workgroup_generations_sampled(hq):
+    # 700 pairs x 2 KV heads = 1400 workgroups: more than the GPU holds at
+    # once, which selects the deeper Q prefetch of the unrolled instances
+    case = GistCase(1, 3000, 8, 64, hq, 2, 64, 700, torch.bfloat16, 321 + hq)
+    sample = np.array([0, 1, 349, 511, 512, 698, 699])
+    check_gist(case, sample=sample, label=f"700 pairs, Hq={hq} (sampled)")
 
 
 def test_wide_ell64_workload_sampled():
