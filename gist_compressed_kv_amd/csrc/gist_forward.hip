@@ -155,7 +155,8 @@ struct MfmaLds {
 };
 
 // D: head_dim.  NKT: maximum number of 16-key tiles (keys <= 16*NKT).
-// QPF: query heads whose Q is kept in flight ahead of use.
+// QPF: Q ring depth: once head h has taken its Q out of the ring, the
+// loads of heads h+1 .. h+QPF are in flight.
 // GT: the GQA group size when known at compile time (0 = taken from the
 // arguments).  With GT > 0 the head loop is fully unrolled, so the compiler
 // knows exactly which loads each wait has to cover and never drains the
@@ -278,6 +279,11 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // stays in registers
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t raw[QPF][NS];
+  auto load_q = [&](auto slot, const int hq) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      raw[decltype(slot)::value][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2);
+  };
 #pragma unroll
   for (int i = 0; i < QPF; ++i) {
     const int hq = i < G ? i : G - 1;
@@ -323,8 +329,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float2 cssn = *(const float2*)(crow + 2 * e);
-          yl[e] = xl[e] * cssn.x - xh[e] * cssn.y;
-          yh[e] = xh[e] * cssn.x + xl[e] * cssn.y;
+          yl[e] = __builtin_fmaf(xl[e], cssn.x, -(xh[e] * cssn.y));
+          yh[e] = __builtin_fmaf(xh[e], cssn.x, xl[e] * cssn.y);
         }
         lo = pack8_bf16(yl);
         hi = pack8_bf16(yh);
@@ -409,8 +415,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
 
-  // One query head: i is its Q ring slot, hh the head within the group.
-  auto head = [&](auto slot, const int hh) {
+  // One query head: i is its Q ring slot, hh the head within the group;
+  // refill() issues the next Q loads once the slot has been consumed.
+  auto head = [&](auto slot, const int hh, auto&& refill) {
     constexpr int i = decltype(slot)::value;
         // Q tile to the MFMA layout through the wave's LDS buffer
         uint4 qm[NS];
@@ -430,20 +437,13 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
           unpack8(qm[s + NP], xh);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            yl[e] = xl[e] * qc[s][e] - xh[e] * qsn[s][e];
-            yh[e] = xh[e] * qc[s][e] + xl[e] * qsn[s][e];
+            yl[e] = __builtin_fmaf(xl[e], qc[s][e], -(xh[e] * qsn[s][e]));
+            yh[e] = __builtin_fmaf(xh[e], qc[s][e], xl[e] * qsn[s][e]);
           }
           qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
           qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
         }
-        // refill the slot with the head QPF further on (clamped: always a
-        // valid row, so the load is unconditional)
-        {
-          const int hn = hh + QPF < G ? hh + QPF : G - 1;
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-            raw[i][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hn * D) * 2);
-        }
+        refill();
 
         // logits (already scaled by scale*log2 e) Sᵀ = K·Qᵀ
         f32x4_t sacc[NKT];
@@ -517,13 +517,21 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   if constexpr (GT > 0) {
     // compile-time group size: the whole head sequence unrolls, so the ring
     // slot of every head and every wait count is known to the compiler
-    for_each_const<GT>([&](auto h) {
-      head(std::integral_constant<int, decltype(h)::value % QPF>{}, decltype(h)::value);
+    for_each_const<GT>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      // head h + QPF into the slot just consumed; heads past the group are
+      // not loaded (their count is known here, so the waits stay exact)
+      head(std::integral_constant<int, h % QPF>{}, h, [&] {
+        if constexpr (h + QPF < GT) load_q(std::integral_constant<int, h % QPF>{}, h + QPF);
+      });
     });
   } else {
     for (int hb = 0; hb < G; hb += QPF) {
       for_each_const<QPF>([&](auto slot) {
-        if (hb + decltype(slot)::value < G) head(slot, hb + decltype(slot)::value);
+        const int hh = hb + decltype(slot)::value;
+        // refill with the head QPF further on (clamped: always a valid row,
+        // so the load is unconditional)
+        if (hh < G) head(slot, hh, [&] { load_q(slot, hh + QPF < G ? hh + QPF : G - 1); });
       });
     }
   }
@@ -665,8 +673,8 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 c = rc.cs[(q4 * NP + s) * 8 + e];
-      yl[e] = (xl[e] * c.x - xh[e] * c.y) * sl2;
-      yh[e] = (xh[e] * c.x + xl[e] * c.y) * sl2;
+      yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y)) * sl2;
+      yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y) * sl2;
       ul[e] = xl[e] * sl2;
       uh[e] = xh[e] * sl2;
     }
@@ -858,8 +866,8 @@ gist_fwd_valu(const FwdArgs a) {
       load_n<T, E2>(qr + hi, xh);
 #pragma unroll
       for (int e = 0; e < E2; ++e) {
-        qv[mh][e] = xl[e] * qcs[e] - xh[e] * qsn[e];
-        qv[mh][E2 + e] = xh[e] * qcs[e] + xl[e] * qsn[e];
+        qv[mh][e] = __builtin_fmaf(xl[e], qcs[e], -(xh[e] * qsn[e]));
+        qv[mh][E2 + e] = __builtin_fmaf(xh[e], qcs[e], xl[e] * qsn[e]);
       }
     }
   }
@@ -893,8 +901,8 @@ gist_fwd_valu(const FwdArgs a) {
           float cs = qcs[e], sn = qsn[e];
           if (tj != t) rope_cos_sin((double)(a.pos0 + tj), a.freqs.rev[lo + e], cs, sn);
           const float xl = kv[e], xh = kv[E2 + e];
-          kv[e] = xl * cs - xh * sn;
-          kv[E2 + e] = xh * cs + xl * sn;
+          kv[e] = __builtin_fmaf(xl, cs, -(xh * sn));
+          kv[E2 + e] = __builtin_fmaf(xh, cs, xl * sn);
         }
       }
 #pragma unroll

@@ -144,7 +144,7 @@ decode_split(const DecodeArgs a) {
         load_row_slice<T, E>(qr + partner, y);
 #pragma unroll
         for (int e = 0; e < E; ++e)
-          qv[hh][e] = low ? x[e] * cs[e] - y[e] * sn[e] : x[e] * cs[e] + y[e] * sn[e];
+          qv[hh][e] = __builtin_fmaf(x[e], cs[e], low ? -(y[e] * sn[e]) : y[e] * sn[e]);
       } else {
 #pragma unroll
         for (int e = 0; e < E; ++e) qv[hh][e] = 0.f;
@@ -290,8 +290,8 @@ decode_combine(const DecodeArgs a) {
     rope_cos_sin(pos, a.freqs.rev[low ? d : partner], cs, sn);
     const float qd = elem_f(qr, d), qp = elem_f(qr, partner);
     const float kd = elem_f(kr, d), kpn = elem_f(kr, partner);
-    const float qrot = low ? qd * cs - qp * sn : qd * cs + qp * sn;
-    const float krot = low ? kd * cs - kpn * sn : kd * cs + kpn * sn;
+    const float qrot = __builtin_fmaf(qd, cs, low ? -(qp * sn) : qp * sn);
+    const float krot = __builtin_fmaf(kd, cs, low ? -(kpn * sn) : kpn * sn);
     part = fmaf(qrot, krot, part);
     vself[e] = elem_f(vr, d);
   }

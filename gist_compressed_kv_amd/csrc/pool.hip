@@ -65,8 +65,8 @@ pool_write_kernel(T* __restrict__ pool, int64_t layer_off, int64_t N, int k, int
     }
     float cs = 1.f, sn = 0.f;
     if (src_pos0 != 1) rope_cos_sin(shift, freqs.rev[lo], cs, sn);
-    const float yl = xl * cs - xh * sn;
-    const float yh = xh * cs + xl * sn;
+    const float yl = __builtin_fmaf(xl, cs, -(xh * sn));
+    const float yh = __builtin_fmaf(xh, cs, xl * sn);
     if constexpr (sizeof(T) == 2) {
       const uint32_t p = pack2_bf16(yl, yh);
       rec[kdst + lo] = (T)(p & 0xffffu);
