@@ -303,7 +303,7 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
-                      ("gist_fwd_mfma<128>" if wl.ell > 1 else "gist_fwd_valu<bf16,128>"),
+                      ("gist_fwd_mfma<128>" if wl.ell > 1 else "gist_fwd_eos<128>"),
             "achieved": achieved_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -54,6 +54,9 @@ struct FwdArgs {
   int pos0;
   float scale_log2;  // softmax scale * log2(e)
   RopeFreqs freqs;
+  // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
+  // set bits b of i, for kernels that form a lane's frequency from scalars
+  double rev_step[6];
 };
 
 // ---------------------------------------------------------------------------
@@ -542,33 +545,43 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 // query heads are the MFMA columns
 // ---------------------------------------------------------------------------
 
-// cos/sin of every channel pair at the single query position, computed on the
-// host (one position for the whole launch), laid out per lane group: entry
-// [q4][s][e] is channel pair 32*s + 8*q4 + e, s < D/64
-struct EosRope {
-  float2 cs[kMaxHalfDim];
-};
+// Row-major K/V rows in LDS (one row per key, D channels) for the EOS
+// kernel.  V rows are read back as MFMA A fragments with the LDS transpose
+// read (ds_read_b64_tr_b16), which covers rows R0..R0+3 (R0 a multiple of 4)
+// and the same 8-byte half of four 16-byte chunks per pass.  With a row
+// stride of D + 4 elements (8 bytes of padding) and the chunks of row R
+// rotated by 3*((R >> 1) & 1), those 16 pieces land on 32 distinct banks, as
+// do the 16-byte row writes of the staging.
+__device__ __forceinline__ constexpr int eos_off(int R, int ch, int D) {
+  return R * (D + 4) + ((((ch >> 3) + 3 * ((R >> 1) & 1)) & (D / 8 - 1)) << 3) + (ch & 7);
+}
 
 // One wave per (pair, KV head); four per workgroup, each with its own LDS
 // slice, so no workgroup barrier is involved.
-//   keys (reversed nothing; in order): gist tiles 0..ngt-1 hold the item gist
-//   then the query gist (kg = k + k' rows, zero padded); tile ngt holds the
-//   token's own key alone at row 0.  For the gist tiles the rotated Q is used;
-//   for the self tile both the key and the query sit at pos0, so their
-//   rotations cancel and the unrotated Q and K_new give the same logit.
+//   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
+//   gist (kg = k + k' rows, padded with copies of row 0 that the mask
+//   removes); tile NGT holds the token's own key alone.  For the gist tiles
+//   the rotated Q is used; for the self tile both the key and the query sit
+//   at pos0, so their rotations cancel and the raw Q and K_new give the same
+//   logit (scaled after the product).
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
 template <int D, int NGT>
-__global__ void __launch_bounds__(256)
-gist_fwd_eos(const FwdArgs a, const EosRope rc) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+gist_fwd_eos(const FwdArgs a) {
   constexpr int NS = D / 32;
   constexpr int NP = NS / 2;
   constexpr int NDT = D / 16;
-  constexpr int NT = NGT + 1;          // gist tiles + self tile
-  constexpr int VS = 16 * NT + 8;      // Vᵀ row stride (elements)
-  constexpr int CV = D / 8;
-  __shared__ __align__(16) bf16_t vts[4][D * VS];
+  constexpr int NT = NGT + 1;            // gist tiles + self tile
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int VSELF = 16 * NGT;        // LDS row of V_new
+  constexpr int KSELF = 16 * NGT + 1;    // LDS row of K_new
+  constexpr int ROWS = 16 * NGT + 2;
+  constexpr int RIT = (ROWS * CPR + 63) / 64;  // row-staging loads per lane
+  __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
+  __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) * scale*log2 e
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
+  typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -607,7 +620,8 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
     return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
   };
 
-  // ---- loads, all unconditional (clamped rows, zeroed afterwards) ----------
+  // ---- loads, all unconditional (clamped rows) -----------------------------
+  // K: MFMA A layout straight from HBM (lane n = key, 8 channels of step s)
   u32x4_t kr[NGT][NS];
 #pragma unroll
   for (int kt = 0; kt < NGT; ++kt) {
@@ -616,75 +630,55 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) kr[kt][s] = *(const u32x4_t*)(row + 32 * s + 8 * q4);
   }
-  u32x4_t ks[NS], qraw[NS];
+  u32x4_t qraw[NS];
   const int hcol = n < G ? n : G - 1;
   const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G + hcol) * D;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    ks[s] = *(const u32x4_t*)(knew + 32 * s + 8 * q4);
-    qraw[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * q4);
-  }
-  // V rows of key pairs (2jp, 2jp+1), chunk cv: the gist keys, then the self
-  // key at column 16*NGT
-  constexpr int NPAIR = 8 * NT;
-  constexpr int VIT = (NPAIR * CV + 63) / 64;
-  u32x4_t va[VIT], vb[VIT];
+  for (int s = 0; s < NS; ++s) qraw[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * q4);
+  __builtin_amdgcn_sched_barrier(0);
+  // V rows of the gist tiles, V_new and K_new as whole rows, coalesced (lane
+  // covers chunk u % CPR of row u / CPR); issued last, so the logits of the
+  // gist tiles only wait for K and Q
+  u32x4_t rraw[RIT];
 #pragma unroll
-  for (int it = 0; it < VIT; ++it) {
+  for (int it = 0; it < RIT; ++it) {
     const int u = lane + 64 * it;
-    const int jp = u % NPAIR, cv = (u / NPAIR) % CV;
-    const int j0 = 2 * jp, j1 = 2 * jp + 1;
-    auto vrow = [&](int j) -> const bf16_t* {
-      if (j == 16 * NGT) return vnew;
-      return gist_row(j < kg ? j : 0, true);
-    };
-    va[it] = *(const u32x4_t*)(vrow(j0) + 8 * cv);
-    vb[it] = *(const u32x4_t*)(vrow(j1) + 8 * cv);
+    const int r = u / CPR, c = u - (u / CPR) * CPR;
+    const bf16_t* src = r < VSELF ? gist_row(r < kg ? r : 0, true) : (r == VSELF ? vnew : knew);
+    rraw[it] = *(const u32x4_t*)(src + 8 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- cos/sin at pos0 (scale*log2 e folded in): lane i < D/2 evaluates
+  // channel pair i; its frequency rev_0 * q^i comes from scalar arguments --
+  float2* cst = cs_lds[wv];
+  if (lane < D / 2) {
+    double rev = a.freqs.rev[0];
+#pragma unroll
+    for (int b = 0; b < 6; ++b) rev *= ((lane >> b) & 1) ? a.rev_step[b] : 1.0;
+    float c, sn;
+    rope_cos_sin((double)a.pos0, rev, c, sn);
+    cst[lane] = make_float2(c * a.scale_log2, sn * a.scale_log2);
   }
 
-  // ---- V transposed into this wave's LDS slice ----------------------------
-  bf16_t* Vt = vts[wv];
-#pragma unroll
-  for (int it = 0; it < VIT; ++it) {
-    const int u = lane + 64 * it;
-    if (u < NPAIR * CV) {
-      const int jp = u % NPAIR, cv = u / NPAIR;
-      const int j0 = 2 * jp, j1 = 2 * jp + 1;
-      const bool ok0 = j0 < kg || j0 == 16 * NGT, ok1 = j1 < kg || j1 == 16 * NGT;
-      const u32x4_t zero = {0u, 0u, 0u, 0u};
-      const u32x4_t w0 = ok0 ? va[it] : zero, w1 = ok1 ? vb[it] : zero;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *(uint32_t*)(Vt + (8 * cv + 2 * e) * VS + j0) = (w0[e] & 0xffffu) | (w1[e] << 16);
-        *(uint32_t*)(Vt + (8 * cv + 2 * e + 1) * VS + j0) = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-      }
-    }
-  }
-
-  // ---- rotate Q at pos0 (scale*log2 e folded in); unrotated Q for the self
-  // tile is scaled the same way ---------------------------------------------
-  const float sl2 = a.scale_log2;
-  bf16x8_t qf[NS], qu[NS];
+  // ---- rotate Q at pos0 ------------------------------------------------------
+  bf16x8_t qf[NS];
 #pragma unroll
   for (int s = 0; s < NP; ++s) {
-    float xl[8], xh[8], yl[8], yh[8], ul[8], uh[8];
+    float xl[8], xh[8], yl[8], yh[8];
     unpack8(make_uint4(qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w), xl);
     unpack8(make_uint4(qraw[s + NP].x, qraw[s + NP].y, qraw[s + NP].z, qraw[s + NP].w), xh);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 c = rc.cs[(q4 * NP + s) * 8 + e];
-      yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y)) * sl2;
-      yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y) * sl2;
-      ul[e] = xl[e] * sl2;
-      uh[e] = xh[e] * sl2;
+      const float2 c = cst[32 * s + 8 * q4 + e];
+      yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y));
+      yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y);
     }
     qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
     qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
-    qu[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(ul));
-    qu[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(uh));
   }
 
-  // ---- logits Sᵀ[key][head] ---------------------------------------------------
+  // ---- logits Sᵀ[key][head] of the gist tiles (scaled by scale*log2 e) ------
   f32x4_t sacc[NT];
   float mx = -INFINITY;
 #pragma unroll
@@ -694,26 +688,46 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = (16 * kt + 4 * q4 + r < kg) ? 0.f : -INFINITY;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const u32x4_t w = (16 * kt + n < kg) ? kr[kt][s] : u32x4_t{0u, 0u, 0u, 0u};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qf[s], acc,
-                                                     0, 0, 0);
-      }
+      for (int s = 0; s < NS; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kt][s]), qf[s],
+                                                     acc, 0, 0, 0);
       sacc[kt] = acc;
       mx = vmax3(mx, acc[0], acc[1]);
       mx = vmax3(mx, acc[2], acc[3]);
     }
   }
+
+  // ---- staged rows to LDS ----------------------------------------------------
+  bf16_t* Rl = rows_lds[wv];
+#pragma unroll
+  for (int it = 0; it < RIT; ++it) {
+    const int u = lane + 64 * it;
+    const int r = u / CPR, c = u - (u / CPR) * CPR;
+    if (r < ROWS) {
+      // rows are 8-byte aligned: two 8-byte stores
+      uint2* dst = (uint2*)(Rl + eos_off(r, 8 * c, D));
+      dst[0] = make_uint2(rraw[it].x, rraw[it].y);
+      dst[1] = make_uint2(rraw[it].z, rraw[it].w);
+    }
+  }
+
   {
+    // self tile: raw Q against K_new (every MFMA row holds K_new; rows other
+    // than 0 are removed by the bias), scaled after the product
     f32x4_t acc;
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = (q4 == 0 && r == 0) ? 0.f : -INFINITY;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const u32x4_t w = n == 0 ? ks[s] : u32x4_t{0u, 0u, 0u, 0u};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w), qu[s], acc, 0,
-                                                   0, 0);
+      const uint2* src = (const uint2*)(Rl + eos_off(KSELF, 32 * s + 8 * q4, D));
+      const uint2 lo = src[0], hi = src[1];
+      const u32x4_t kf = {lo.x, lo.y, hi.x, hi.y};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
+                                                   __builtin_bit_cast(bf16x8_t, qraw[s]), acc, 0, 0, 0);
     }
+    const float sl2 = a.scale_log2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] *= sl2;
     sacc[NGT] = acc;
     mx = vmax3(mx, acc[0], acc[1]);
     mx = vmax3(mx, acc[2], acc[3]);
@@ -723,6 +737,10 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
 
   // ---- P = exp2(s - max); O = P·V and row sums on the matrix cores ----------
+  // V fragment (d-tile dt, key tile kt) by transpose read: the lane supplying
+  // a piece reads key (lane >> 2) of the tile, channels
+  // 32*(dt >> 1) + 4*(dt & 1) + 8*(lane & 3) .. +3, so MFMA row r of the tile
+  // is channel vt_row(dt, r) and key k of the tile is MFMA column k
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   f32x4_t o[NDT];
 #pragma unroll
@@ -736,11 +754,15 @@ gist_fwd_eos(const FwdArgs a, const EosRope rc) {
           pack2_bf16(__builtin_amdgcn_exp2f(sacc[kt][2] - mx), __builtin_amdgcn_exp2f(sacc[kt][3] - mx)));
       const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
       lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
-      const bf16_t* vrow = Vt + vt_row(0, n) * VS + 16 * kt + 4 * q4;
+      // the self tile has one key: every lane reads the V_new row
+      const int R = kt == NGT ? VSELF : 16 * kt + (lane >> 2);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x4_t vf = *(const bf16x4_t*)(vrow + (vt_row(dt, 0) - vt_row(0, 0)) * VS);
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
+        const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(Rl + eos_off(R, ch, D)));
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pf, o[dt],
+                                                          0, 0, 0);
       }
     }
   }
@@ -1059,6 +1081,10 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
   a.pos0 = pos0;
   a.scale_log2 = scale * 1.4426950408889634f;
   make_rope_freqs(a.freqs, d, rope_base);
+  {
+    double q = std::pow((double)rope_base, -2.0 / (double)d);
+    for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
+  }
   hipStream_t s = (hipStream_t)stream;
 
   const int kg = a.k + a.kq;
@@ -1101,23 +1127,13 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
     return check_launch("gist_attn_forward(mfma)");
   }
   if (pool->dtype == GIST_BF16 && ell == 1 && a.G <= 16 && kg <= 32) {
-    // one position for the whole launch: its cos/sin come from the host
-    EosRope rc;
-    const int np = d / 64;
-    for (int q4 = 0; q4 < 4; ++q4)
-      for (int s2 = 0; s2 < np; ++s2)
-        for (int e = 0; e < 8; ++e) {
-          const int i = 32 * s2 + 8 * q4 + e;
-          const double ang = (double)pos0 * std::pow((double)rope_base, -2.0 * i / (double)d);
-          rc.cs[(q4 * np + s2) * 8 + e] = make_float2((float)std::cos(ang), (float)std::sin(ang));
-        }
     const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
     if (d == 64) {
-      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<64, 1>), grid, dim3(256), 0, s, a, rc);
-      else hipLaunchKernelGGL((gist_fwd_eos<64, 2>), grid, dim3(256), 0, s, a, rc);
+      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<64, 1>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<64, 2>), grid, dim3(256), 0, s, a);
     } else {
-      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<128, 1>), grid, dim3(256), 0, s, a, rc);
-      else hipLaunchKernelGGL((gist_fwd_eos<128, 2>), grid, dim3(256), 0, s, a, rc);
+      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<128, 1>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<128, 2>), grid, dim3(256), 0, s, a);
     }
     return check_launch("gist_attn_forward(eos)");
   }
