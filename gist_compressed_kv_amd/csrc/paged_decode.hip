@@ -20,6 +20,8 @@
 //  * decode_combine<T, D>: one wave64 per (request, query head) merges the
 //    split states with the token's own key/value (log-sum-exp weights) and
 //    writes the normalized output.
+#include <utility>
+
 #include "common.hpp"
 
 namespace gist {
@@ -46,7 +48,30 @@ struct DecodeArgs {
   int nsplit;
   void* out;
   RopeFreqs freqs;
+  // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
+  // set bits b of i (a lane's frequency from scalar arguments only)
+  double rev_step[6];
 };
+
+// revolutions per position of channel pair i (lane-dependent i < 64) from
+// scalar arguments: a lane-indexed read of the kernel-argument table would be
+// a vector load, and its wait would drain the data loads issued before it
+__device__ __forceinline__ double pair_rev(const DecodeArgs& a, int i) {
+  double rev = a.freqs.rev[0];
+#pragma unroll
+  for (int b = 0; b < 6; ++b) rev *= ((i >> b) & 1) ? a.rev_step[b] : 1.0;
+  return rev;
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 in order.
+template <class F, int... I>
+__device__ __forceinline__ void for_each_const_d_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void for_each_const_d(F&& f) {
+  for_each_const_d_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_row(float x) {
@@ -133,8 +158,12 @@ decode_split(const DecodeArgs a) {
     const int partner = low ? ch0 + D / 2 : ch0 - D / 2;
     const int fi = low ? ch0 : partner;  // frequency index of the pair
     float cs[E], sn[E];
+    double rev = pair_rev(a, fi);
 #pragma unroll
-    for (int e = 0; e < E; ++e) rope_cos_sin(pos, a.freqs.rev[fi + e], cs[e], sn[e]);
+    for (int e = 0; e < E; ++e) {
+      rope_cos_sin(pos, rev, cs[e], sn[e]);
+      rev *= a.rev_step[0];
+    }
 #pragma unroll
     for (int hh = 0; hh < MAXG; ++hh) {
       if (hh < G) {
@@ -160,54 +189,75 @@ decode_split(const DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) o[hh][e] = 0.f;
   }
-  bool blk_bad = false;
-
-  if (kbeg < kend) {
-    // 16 keys of one row lie in one block (block_size is a multiple of 16)
-    const int32_t phys = a.table[(int64_t)r * a.max_blk + kbeg / a.bs];
-    if (phys < 0 || phys >= a.nblk) {
-      blk_bad = true;
+  // ---- this row's 16 keys: unconditional loads (rows past the context, or
+  // of a row with no keys, read a valid row and are masked), PD keys in
+  // flight, fully unrolled so every wait covers exactly the loads it needs
+  const int nkeys = kend > kbeg ? kend - kbeg : 0;
+  int32_t phys = 0;
+  if (nkeys > 0) phys = a.table[(int64_t)r * a.max_blk + kbeg / a.bs];
+  const bool row_ok = nkeys > 0 && phys >= 0 && phys < a.nblk;
+  const bool blk_bad = nkeys > 0 && !row_ok;
+  // 16 keys of one row lie in one block (block_size is a multiple of 16)
+  const int64_t base =
+      row_ok ? (((int64_t)phys * a.H + g) * a.bs + (kbeg % a.bs)) * D + E * c : (int64_t)E * c;
+  const int nvalid = row_ok ? nkeys : 0;
+  const int klast = nvalid > 0 ? nvalid - 1 : 0;
+  const T* kp = (const T*)a.kc + base;
+  const T* vp = (const T*)a.vc + base;
+  constexpr int NW = E * (int)sizeof(T) / 4;  // 32-bit words per lane and key
+  typedef unsigned int rawv_t __attribute__((ext_vector_type(NW)));
+  // keys in flight per lane: 8, or 4 when the per-head state of a wide group
+  // already takes most of the registers
+  constexpr int PD = MAXG * E >= 32 ? 4 : 8;
+  rawv_t kb[PD], vb[PD];
+  auto issue = [&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    const int64_t off = (int64_t)(t < klast ? t : klast) * D;
+    kb[t % PD] = *(const rawv_t*)(kp + off);
+    vb[t % PD] = *(const rawv_t*)(vp + off);
+  };
+  auto unpack = [](const rawv_t& w, float* f) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        f[2 * i] = __uint_as_float(w[i] << 16);
+        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      }
     } else {
-      const int64_t base = (((int64_t)phys * a.H + g) * a.bs + (kbeg % a.bs)) * D + E * c;
-      const T* kp = (const T*)a.kc + base;
-      const T* vp = (const T*)a.vc + base;
-      const int nkeys = kend - kbeg;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float kr[8][E], vr[8][E];
+      for (int i = 0; i < NW; ++i) f[i] = __uint_as_float(w[i]);
+    }
+  };
+  for_each_const_d<PD>([&](auto tc) { issue(tc); });
+  for_each_const_d<16>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    float kf[E], vf[E];
+    unpack(kb[t % PD], kf);
+    unpack(vb[t % PD], vf);
+    if constexpr (t + PD < 16) issue(std::integral_constant<int, t + PD>{});
+    const bool valid = t < nvalid;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = 8 * half + i;
-          if (kk < nkeys) {
-            load_row_slice<T, E>(kp + (int64_t)kk * D, kr[i]);
-            load_row_slice<T, E>(vp + (int64_t)kk * D, vr[i]);
-          }
-        }
+    for (int hh = 0; hh < MAXG; ++hh) {
+      if (hh == 0 || hh < G) {  // head 0 always exists: no branch around it
+        float part = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int kk = 8 * half + i;
-          if (kk < nkeys) {
+        for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kf[e], part);
+        // the logit is formed for every key and masked by selects (no branch,
+        // so the loads stay where they were issued)
+        const float dot = row16_sum_d(part) * a.scale_log2;
+        const float sc = valid ? dot : -INFINITY;
+        const float mnew = fmaxf(m[hh], sc);
+        // exponents never see -inf - -inf: an all-masked state keeps alpha = 1,
+        // a masked key gets weight exp2(-inf) = 0
+        const float alpha = __builtin_amdgcn_exp2f(mnew == -INFINITY ? 0.f : m[hh] - mnew);
+        const float pw = __builtin_amdgcn_exp2f(valid ? sc - mnew : -INFINITY);
+        m[hh] = mnew;
+        l[hh] = l[hh] * alpha + pw;
 #pragma unroll
-            for (int hh = 0; hh < MAXG; ++hh) {
-              if (hh < G) {
-                float part = 0.f;
-#pragma unroll
-                for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kr[i][e], part);
-                const float sc = row16_sum_d(part) * a.scale_log2;
-                const float mnew = fmaxf(m[hh], sc);
-                const float alpha = exp2f(m[hh] - mnew);
-                const float pw = exp2f(sc - mnew);
-                m[hh] = mnew;
-                l[hh] = l[hh] * alpha + pw;
-#pragma unroll
-                for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pw, vr[i][e], o[hh][e] * alpha);
-              }
-            }
-          }
-        }
+        for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pw, vf[e], o[hh][e] * alpha);
       }
     }
-  }
+  });
 
   // merge the four rows of the wave (lane ^ 16, lane ^ 32)
 #pragma unroll
@@ -287,7 +337,7 @@ decode_combine(const DecodeArgs a) {
     const bool low = d < D / 2;
     const int partner = low ? d + D / 2 : d - D / 2;
     float cs, sn;
-    rope_cos_sin(pos, a.freqs.rev[low ? d : partner], cs, sn);
+    rope_cos_sin(pos, pair_rev(a, low ? d : partner), cs, sn);
     const float qd = elem_f(qr, d), qp = elem_f(qr, partner);
     const float kd = elem_f(kr, d), kpn = elem_f(kr, partner);
     const float qrot = __builtin_fmaf(qd, cs, low ? -(qp * sn) : qp * sn);
@@ -418,6 +468,10 @@ extern "C" gist_status paged_decode_attn(const void* k_cache, const void* v_cach
   a.Hq = Hq;
   a.H = H;
   a.G = Hq / H;
+  {
+    double qs = std::pow((double)rope_base, -2.0 / (double)d);
+    for (int b = 0; b < 6; ++b, qs *= qs) a.rev_step[b] = qs;
+  }
   a.scale_log2 = scale * 1.4426950408889634f;
   a.ws = (float*)workspace;
   a.nsplit = nsplit;
