@@ -28,8 +28,15 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
 METRIC = "pairs/s + % of HBM peak, gist-KV attention (24L, GQA 14:2, k=8, ℓ=64)"
-KERNEL_SOURCE = os.path.join(ROOT, "gist_compressed_kv_amd", "csrc", "gist_forward.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "gist_fwd_mfma_d64_24L_b500_counters.json")
+CSRC = os.path.join(ROOT, "gist_compressed_kv_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# counter summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated) per
+# workload, and the kernel source they were taken on
+COUNTER_FILES = {
+    "24L_b500": ("gist_fwd_mfma_d64_24L_b500_counters.json", "gist_forward.hip"),
+    "wide_eos": ("gist_fwd_eos_d128_wide_eos_counters.json", "gist_forward.hip"),
+    "paged": ("paged_decode_32x4096_counters.json", "paged_decode.hip"),
+}
 
 
 def gist_bytes_per_pair_layer(wl) -> int:
@@ -59,20 +66,23 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_hash(source: str) -> str:
+    with open(os.path.join(CSRC, source), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def measured_traffic(workload_name: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, only if they
     were taken on the current kernel source."""
+    if workload_name not in COUNTER_FILES:
+        return None
+    fname, source = COUNTER_FILES[workload_name]
     try:
-        with open(COUNTERS) as f:
+        with open(os.path.join(PROFILES, fname)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha256_16") != kernel_source_hash() or c.get("workload") != workload_name:
+    if c.get("kernel_source_sha256_16") != kernel_source_hash(source) or c.get("workload") != workload_name:
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -195,7 +205,7 @@ def paged_bench(args):
         "config": {"workload": wl.name},
         "roofline": {"bound": "hbm", "kernel": "decode_split + decode_combine",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("paged"),
                      "bytes_per_unit": bytes_unit, "units_per_launch": wl.requests,
                      "avg_launch_us": avg_s * 1e6}}), flush=True)
 
@@ -283,7 +293,8 @@ def main():
     traffic = measured_traffic(args.workload)
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == "24L_b500" else
+                  f"pairs/s + % of HBM peak, gist-KV attention ({args.workload})",
         "value": pairs_per_s,
         "unit": "pairs/s",
         "n_gpus": 1,
