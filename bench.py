@@ -247,9 +247,11 @@ def main():
                               synth.tensor_seed(wl.seed, 2), wl.dtype, dev)
         qpool = G.GistPool(qpool_t)
         q_ids = (torch.arange(wl.pairs, device=dev) // (wl.pairs // wl.queries)).to(torch.int32)
-    # one distinct activation set per layer (wide workloads reuse one set:
-    # 4.8 GB per layer already dwarfs every cache)
-    n_sets = wl.layers if wl.d == 64 else 1
+    # one distinct activation set per layer, and at least four for the
+    # single-layer workload (one 133 MB set would stay in the 256 MB
+    # Infinity Cache); consecutive passes walk through the sets.  The wide
+    # workloads reuse one set: 4.8 GB per layer already dwarfs every cache.
+    n_sets = max(wl.layers, 4) if wl.d == 64 else 1
     qs, kns, vns, outs = [], [], [], []
     for li in range(n_sets):
         qs.append(synth.randn((wl.pairs, wl.ell, wl.hq, wl.d), synth.tensor_seed(wl.seed, 3, li), wl.dtype, dev))
@@ -260,11 +262,15 @@ def main():
     scale = 1.0 / math.sqrt(wl.d)
     stream = torch.cuda.current_stream()
 
+    passes = [0]
+
     def step():
+        base = passes[0] * wl.layers
         for li in range(wl.layers):
-            si = li % n_sets
+            si = (base + li) % n_sets
             G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
                                 qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
+        passes[0] += 1
 
     for _ in range(args.warmup):
         step()
