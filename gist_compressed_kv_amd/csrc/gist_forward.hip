@@ -197,53 +197,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const int Hq = a.Hq, G = GT > 0 ? GT : a.G;
   bf16_t* out = (bf16_t*)a.out;
 
-  // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
-  const int32_t item = a.item_ids[p];
-  int32_t qid = 0;
-  bool bad = item < 0 || item >= a.N;
-  if (a.kq) {
-    qid = a.q_ids[p];
-    bad = bad || qid < 0 || qid >= a.qN;
-  }
-  if (bad) {
-    const int per_t = G * D;
-    for (int u = tid; u < ell * per_t; u += 256) {
-      const int t = u / per_t, r = u - t * per_t;
-      out[((int64_t)p * ell + t) * Hq * D + (int64_t)g * G * D + r] = nan_value<bf16_t>();
-    }
-    return;
-  }
-  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-                     (int64_t)g * a.k * D;
-  const bf16_t* qK = nullptr;
-  if (a.kq)
-    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
-         (int64_t)g * a.kq * D;
-
-  // ---- issue every staging load of this thread ----------------------------
-  // Every load below is unconditional (out-of-range units read row 0 and
-  // are zeroed afterwards), so the compiler can count the loads in flight
-  // exactly and later waits never have to drain the Q prefetch.
-  uint4 klo[IT], khi[IT], v0[IT], v1[IT];
-  const int npairs = nk_pad >> 1;
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int u = tid + 256 * it;
-    const int j = u / CH, c = u - j * CH;
-    const bf16_t* src = key_row(a, gK, qK, p, g, j < nk ? j : 0, kg, D, false);
-    klo[it] = *(const uint4*)(src + 8 * c);
-    khi[it] = *(const uint4*)(src + D / 2 + 8 * c);
-    const int cv = u / npairs, jp = u - cv * npairs;
-    const int cvc = cv < CV ? cv : 0;
-    v0[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp < nk ? 2 * jp : 0, kg, D, true) + 8 * cvc);
-    v1[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp + 1 < nk ? 2 * jp + 1 : 0, kg, D, true) + 8 * cvc);
-  }
-
-  // keep the issue order: staging loads first, then the Q prefetch, so the
-  // wait before the LDS stores covers the staging loads only
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- issue the first QPF heads' Q loads of this wave ----------------------
+  // ---- issue the first QPF heads' Q loads of this wave first: they do not
+  // depend on the item id, so HBM traffic starts while the id is in flight --
   // (wave index read through readfirstlane so every per-wave quantity below
   // is a scalar and the tile loops branch on SGPRs)
   // The token block of a wave rotates with the workgroup index: later blocks
@@ -295,6 +250,52 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       raw[i][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2);
   }
 
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
+  const int32_t item = a.item_ids[p];
+  int32_t qid = 0;
+  bool bad = item < 0 || item >= a.N;
+  if (a.kq) {
+    qid = a.q_ids[p];
+    bad = bad || qid < 0 || qid >= a.qN;
+  }
+  if (bad) {
+    const int per_t = G * D;
+    for (int u = tid; u < ell * per_t; u += 256) {
+      const int t = u / per_t, r = u - t * per_t;
+      out[((int64_t)p * ell + t) * Hq * D + (int64_t)g * G * D + r] = nan_value<bf16_t>();
+    }
+    return;
+  }
+  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+                     (int64_t)g * a.k * D;
+  const bf16_t* qK = nullptr;
+  if (a.kq)
+    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+         (int64_t)g * a.kq * D;
+
+  // ---- issue every staging load of this thread ----------------------------
+  // Every load below is unconditional (out-of-range units read row 0 and
+  // are zeroed afterwards), so the compiler can count the loads in flight
+  // exactly and later waits never have to drain the Q prefetch.
+  uint4 klo[IT], khi[IT], v0[IT], v1[IT];
+  const int npairs = nk_pad >> 1;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int u = tid + 256 * it;
+    const int j = u / CH, c = u - j * CH;
+    const bf16_t* src = key_row(a, gK, qK, p, g, j < nk ? j : 0, kg, D, false);
+    klo[it] = *(const uint4*)(src + 8 * c);
+    khi[it] = *(const uint4*)(src + D / 2 + 8 * c);
+    const int cv = u / npairs, jp = u - cv * npairs;
+    const int cvc = cv < CV ? cv : 0;
+    v0[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp < nk ? 2 * jp : 0, kg, D, true) + 8 * cvc);
+    v1[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp + 1 < nk ? 2 * jp + 1 : 0, kg, D, true) + 8 * cvc);
+  }
+
+  // keep the staging loads together (the Q prefetch above was issued first
+  // and has returned by the time the LDS stores wait for them)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- RoPE table: wave w evaluates channel pairs [w*D/8, (w+1)*D/8) for

@@ -350,21 +350,49 @@ decode_combine(const DecodeArgs a) {
   const float sself = row16_sum_d(part) * a.scale_log2;
 
   const float* ws = a.ws + ((int64_t)r * a.Hq + h) * a.nsplit * (D + kWsPad);
-  float mm = sself;
-  for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, ws[s * (D + kWsPad) + D]);
-  const float wself = exp2f(sself - mm);
+  const int ns = a.nsplit;
+  // split maxima: lane s covers splits s, s + 64, ... (independent loads),
+  // then a wave reduction
+  float mloc = sself;
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) mloc = fmaxf(mloc, ws[(int64_t)(s0 + lane) * (D + kWsPad) + D]);
+#pragma unroll
+  for (int sh = 32; sh >= 1; sh >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, sh));
+  const float mm = mloc;
+  const float wself = __builtin_amdgcn_exp2f(sself - mm);
   float ll = wself;
   float acc[EC];
 #pragma unroll
   for (int e = 0; e < EC; ++e) acc[e] = wself * vself[e];
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float* row = ws + s * (D + kWsPad);
-    const float ms = row[D];
-    const float ls = row[D + 1];
-    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mm);
-    ll = fmaf(ls, w, ll);  // NaN l (bad block/context) poisons the output
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    // weight of split s0 + lane; a NaN l (bad block or context) poisons the sum
+    float wl = 0.f, lterm = 0.f;
+    if (s0 + lane < ns) {
+      const float* row = ws + (int64_t)(s0 + lane) * (D + kWsPad);
+      const float ms = row[D], ls = row[D + 1];
+      wl = (ms == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ms - mm);
+      lterm = ls * wl;  // NaN l stays NaN even where the weight is 0
+    }
 #pragma unroll
-    for (int e = 0; e < EC; ++e) acc[e] = fmaf(row[lane + 64 * e], w, acc[e]);
+    for (int sh = 32; sh >= 1; sh >>= 1) lterm += __shfl_xor(lterm, sh);
+    ll += lterm;
+    // weighted split outputs, eight splits per round of independent loads
+    const int n = ns - s0 < 64 ? ns - s0 : 64;
+    for (int i0 = 0; i0 < n; i0 += 8) {
+      float v[8][EC];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int si = s0 + (i0 + i < n ? i0 + i : n - 1);
+#pragma unroll
+        for (int e = 0; e < EC; ++e) v[i][e] = ws[(int64_t)si * (D + kWsPad) + lane + 64 * e];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = i0 + i < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i0 + i)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EC; ++e) acc[e] = fmaf(v[i][e], w, acc[e]);
+      }
+    }
   }
   const float inv = 1.f / ll;
   T* orow = (T*)a.out + ((int64_t)r * a.Hq + h) * D;
