@@ -362,8 +362,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     }
   }
 
-  // ---- RoPE angles of this lane's token (channels 32s + 8*q4 + e), with the
-  // softmax scale and log2(e) folded in: logits come out ready for exp2 ----
+  // ---- RoPE angles of this lane's token (channels 32s + 8*q4 + e).  The
+  // softmax scale (with log2 e) is applied to the fp32 logits inside the
+  // exponent, so Q is rounded to bf16 as the rotated Q itself, the rounding
+  // point of an unfused RoPE-then-attention pipeline ----------------------
   const float sl2 = a.scale_log2;
   float qc[NP][8], qsn[NP][8];
   {
@@ -373,8 +375,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float2 cssn = *(const float2*)(crow + 2 * (32 * s + 8 * q4 + e));
-        qc[s][e] = cssn.x * sl2;
-        qsn[s][e] = cssn.y * sl2;
+        qc[s][e] = cssn.x;
+        qsn[s][e] = cssn.y;
       }
   }
   __syncthreads();
@@ -449,7 +451,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         }
         refill();
 
-        // logits (already scaled by scale*log2 e) Sᵀ = K·Qᵀ
+        // logits Sᵀ = K·Qᵀ (unscaled; scale*log2 e is applied in the exponent)
         f32x4_t sacc[NKT];
         float mx = -INFINITY;
 #pragma unroll
@@ -474,8 +476,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
         mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
 
-        // P = exp2(s - max) in bf16; O = P·V and the row sum (P against a
-        // ones tile) both on the matrix cores
+        // P = exp2((s - max) * scale*log2 e) in bf16, the product as one fma;
+        // O = P·V and the row sum (P against a ones tile) both on the matrix
+        // cores
+        const float nmx = -mx * sl2;
         f32x4_t o[NDT];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -484,8 +488,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         for (int j = 0; j < NKT; ++j) {
           if (j == 0 || j < nkt) {
             const uint2 pk = make_uint2(
-                pack2_bf16(__builtin_amdgcn_exp2f(sacc[j][0] - mx), __builtin_amdgcn_exp2f(sacc[j][1] - mx)),
-                pack2_bf16(__builtin_amdgcn_exp2f(sacc[j][2] - mx), __builtin_amdgcn_exp2f(sacc[j][3] - mx)));
+                pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][0], sl2, nmx)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][1], sl2, nmx))),
+                pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][2], sl2, nmx)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][3], sl2, nmx))));
             const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
             lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
 #pragma unroll
@@ -561,10 +567,9 @@ __device__ __forceinline__ constexpr int eos_off(int R, int ch, int D) {
 // slice, so no workgroup barrier is involved.
 //   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
 //   gist (kg = k + k' rows, padded with copies of row 0 that the mask
-//   removes); tile NGT holds the token's own key alone.  For the gist tiles
-//   the rotated Q is used; for the self tile both the key and the query sit
-//   at pos0, so their rotations cancel and the raw Q and K_new give the same
-//   logit (scaled after the product).
+//   removes); tile NGT holds the token's own key alone, rotated at pos0 like
+//   the query.  Rotated Q and K_new are rounded to bf16 for the MFMAs, and
+//   the softmax scale is applied to the fp32 logits in the exponent.
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
 template <int D, int NGT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
@@ -579,7 +584,7 @@ gist_fwd_eos(const FwdArgs a) {
   constexpr int ROWS = 16 * NGT + 2;
   constexpr int RIT = (ROWS * CPR + 63) / 64;  // row-staging loads per lane
   __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
-  __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) * scale*log2 e
+  __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) at pos0
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -650,7 +655,7 @@ gist_fwd_eos(const FwdArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- cos/sin at pos0 (scale*log2 e folded in): lane i < D/2 evaluates
+  // ---- cos/sin at pos0: lane i < D/2 evaluates
   // channel pair i; its frequency rev_0 * q^i comes from scalar arguments --
   float2* cst = cs_lds[wv];
   if (lane < D / 2) {
@@ -659,7 +664,7 @@ gist_fwd_eos(const FwdArgs a) {
     for (int b = 0; b < 6; ++b) rev *= ((lane >> b) & 1) ? a.rev_step[b] : 1.0;
     float c, sn;
     rope_cos_sin((double)a.pos0, rev, c, sn);
-    cst[lane] = make_float2(c * a.scale_log2, sn * a.scale_log2);
+    cst[lane] = make_float2(c, sn);
   }
 
   // ---- rotate Q at pos0 ------------------------------------------------------
@@ -679,7 +684,8 @@ gist_fwd_eos(const FwdArgs a) {
     qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
   }
 
-  // ---- logits Sᵀ[key][head] of the gist tiles (scaled by scale*log2 e) ------
+  // ---- logits Sᵀ[key][head] of the gist tiles (unscaled: scale*log2 e is
+  // applied in the exponent, so Q is rounded to bf16 as the rotated Q) ------
   f32x4_t sacc[NT];
   float mx = -INFINITY;
 #pragma unroll
@@ -713,22 +719,37 @@ gist_fwd_eos(const FwdArgs a) {
   }
 
   {
-    // self tile: raw Q against K_new (every MFMA row holds K_new; rows other
-    // than 0 are removed by the bias), scaled after the product
-    f32x4_t acc;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = (q4 == 0 && r == 0) ? 0.f : -INFINITY;
+    // self tile: K_new rotated at pos0 (every MFMA row holds it; rows other
+    // than 0 are removed by the bias) against the rotated Q, both rounded to
+    // bf16 like every other key and query
+    u32x4_t kraw[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const uint2* src = (const uint2*)(Rl + eos_off(KSELF, 32 * s + 8 * q4, D));
       const uint2 lo = src[0], hi = src[1];
-      const u32x4_t kf = {lo.x, lo.y, hi.x, hi.y};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf),
-                                                   __builtin_bit_cast(bf16x8_t, qraw[s]), acc, 0, 0, 0);
+      kraw[s] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
     }
-    const float sl2 = a.scale_log2;
+    bf16x8_t kf[NS];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] *= sl2;
+    for (int s = 0; s < NP; ++s) {
+      float xl[8], xh[8], yl[8], yh[8];
+      unpack8(make_uint4(kraw[s].x, kraw[s].y, kraw[s].z, kraw[s].w), xl);
+      unpack8(make_uint4(kraw[s + NP].x, kraw[s + NP].y, kraw[s + NP].z, kraw[s + NP].w), xh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = cst[32 * s + 8 * q4 + e];
+        yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y));
+        yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y);
+      }
+      kf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
+      kf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
+    }
+    f32x4_t acc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = (q4 == 0 && r == 0) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], acc, 0, 0, 0);
     sacc[NGT] = acc;
     mx = vmax3(mx, acc[0], acc[1]);
     mx = vmax3(mx, acc[2], acc[3]);
@@ -737,12 +758,13 @@ gist_fwd_eos(const FwdArgs a) {
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
 
-  // ---- P = exp2(s - max); O = P·V and row sums on the matrix cores ----------
-  // V fragment (d-tile dt, key tile kt) by transpose read: the lane supplying
+  // ---- P = exp2((s - max) * scale*log2 e); O = P·V and row sums on the
+  // matrix cores; V fragment (d-tile dt, key tile kt) by transpose read: the lane supplying
   // a piece reads key (lane >> 2) of the tile, channels
   // 32*(dt >> 1) + 4*(dt & 1) + 8*(lane & 3) .. +3, so MFMA row r of the tile
   // is channel vt_row(dt, r) and key k of the tile is MFMA column k
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  const float sl2 = a.scale_log2, nmx = -mx * sl2;
   f32x4_t o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -751,8 +773,10 @@ gist_fwd_eos(const FwdArgs a) {
   for (int kt = 0; kt < NT; ++kt) {
     if (kt < ngt || kt == NGT) {
       const uint2 pk = make_uint2(
-          pack2_bf16(__builtin_amdgcn_exp2f(sacc[kt][0] - mx), __builtin_amdgcn_exp2f(sacc[kt][1] - mx)),
-          pack2_bf16(__builtin_amdgcn_exp2f(sacc[kt][2] - mx), __builtin_amdgcn_exp2f(sacc[kt][3] - mx)));
+          pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][0], sl2, nmx)),
+                     __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][1], sl2, nmx))),
+          pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][2], sl2, nmx)),
+                     __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][3], sl2, nmx))));
       const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
       lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
       // the self tile has one key: every lane reads the V_new row

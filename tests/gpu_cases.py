@@ -60,9 +60,9 @@ class GistCase:
                                    self.vn[layer], self.pos0, ROPE_BASE, self.scale,
                                    qpool=self.qpool, q_ids=self.q_ids, out=out)
 
-    def oracle(self, layer, sample):
+    def oracle(self, layer, sample, rounded=False):
         """Oracle rows for the sampled pairs; only the referenced pool rows are
-        copied back."""
+        copied back.  rounded: round the rotated Q and new K to bf16 first."""
         sample = np.asarray(sample)
         idx = torch.as_tensor(sample, device=self.ids.device)
         ids = self.ids[idx].long()
@@ -74,10 +74,11 @@ class GistCase:
             qids = np.arange(len(sample))
         return O.gist_attn_forward(pool, 0, np.arange(len(sample)), f64(self.q[layer][idx]),
                                    f64(self.kn[layer][idx]), f64(self.vn[layer][idx]),
-                                   self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids)
+                                   self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids,
+                                   round_rotated=rounded)
 
-    def max_err(self, layer, out, sample):
-        ref = self.oracle(layer, sample)
+    def max_err(self, layer, out, sample, rounded=False):
+        ref = self.oracle(layer, sample, rounded)
         got = f64(out[torch.as_tensor(np.asarray(sample), device=out.device)])
         assert np.isfinite(got).all(), "non-finite output"
         return float(np.abs(got - ref).max())

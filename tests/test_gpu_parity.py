@@ -23,14 +23,14 @@ def _cleanup():
     torch.cuda.empty_cache()
 
 
-def check_gist(case, layers=None, sample=None, label=""):
+def check_gist(case, layers=None, sample=None, label="", rounded=False):
     layers = range(case.layers) if layers is None else layers
     worst = 0.0
     for li in layers:
         out = case.run(li)
         torch.cuda.synchronize()
         s = np.arange(case.pairs) if sample is None else sample
-        err = case.max_err(li, out, s)
+        err = case.max_err(li, out, s, rounded)
         worst = max(worst, err)
         assert err <= TOL[case.dtype], f"{label} layer {li}: max-abs err {err}"
     say(f"{label}: max-abs err {worst:.3g}")
@@ -280,3 +280,65 @@ def test_pool_write_matches_oracle(dtype, src_pos0):
     assert np.abs(got - ref).max() <= tol
     if src_pos0 == 1:
         assert np.array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# Robustness: peaky softmax (Q scaled by 8) and outlier K channels (x10).
+# The oracle reads the same scaled device tensors back.  With logits this
+# large, rounding the rotated Q and new K to bf16 (what the MFMA operands
+# are, and what an unfused RoPE-then-attention pipeline stores) moves the
+# outputs by more than 2e-2 by itself, so the bf16 paths are held to 2e-2
+# against the oracle with those two rounding points; the distance to the
+# exact oracle is printed beside it.  Paged decode keeps Q and K in fp32 and
+# is held to 2e-2 against the exact oracle.
+# ---------------------------------------------------------------------------
+
+OUTLIER_CH = [3, 17, 40]
+
+
+def _boost(case, layer, peaky, outliers):
+    if peaky:
+        case.q[layer].mul_(8)  # a power of two: exact in bf16
+    if outliers:
+        case.kn[layer][..., OUTLIER_CH] *= 10
+        case.pool_t[layer][:, 0, :, :, OUTLIER_CH] *= 10  # K half of every record
+
+
+@pytest.mark.parametrize("peaky,outliers", [(True, False), (False, True), (True, True)],
+                         ids=["peaky", "outlier_k", "both"])
+def test_robust_mfma(peaky, outliers):
+    case = GistCase(1, 40, 8, 64, 14, 2, 64, 24, torch.bfloat16, 501)
+    _boost(case, 0, peaky, outliers)
+    out = case.run(0)
+    torch.cuda.synchronize()
+    say(f"mfma robust peaky={peaky} outliers={outliers}: vs exact oracle "
+        f"{case.max_err(0, out, np.arange(case.pairs)):.3g}")
+    check_gist(case, label=f"mfma robust peaky={peaky} outliers={outliers} (rounded oracle)",
+               rounded=True)
+
+
+@pytest.mark.parametrize("peaky,outliers", [(True, False), (False, True)], ids=["peaky", "outlier_k"])
+def test_robust_eos(peaky, outliers):
+    qids = torch.arange(8) % 2
+    case = GistCase(1, 30, 8, 1, 64, 8, 128, 8, torch.bfloat16, 502, kq=8, n_qrows=2, q_ids=qids)
+    _boost(case, 0, peaky, outliers)
+    if outliers:
+        case.qpool_t[0][:, 0, :, :, OUTLIER_CH] *= 10
+    out = case.run(0)
+    torch.cuda.synchronize()
+    say(f"eos robust peaky={peaky} outliers={outliers}: vs exact oracle "
+        f"{case.max_err(0, out, np.arange(case.pairs)):.3g}")
+    check_gist(case, label=f"eos robust peaky={peaky} outliers={outliers} (rounded oracle)",
+               rounded=True)
+
+
+def test_robust_paged_decode():
+    case = DecodeCase(48, 4, 256, 128, 8, [1500, 777, 3000], torch.bfloat16, 503)
+    case.q.mul_(8)
+    case.kc[..., OUTLIER_CH] *= 10
+    case.kn[..., OUTLIER_CH] *= 10
+    out = case.run()
+    torch.cuda.synchronize()
+    err = float(np.abs(f64(out) - case.oracle()).max())
+    say(f"paged robust: max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]

@@ -500,3 +500,40 @@ def test_multi_token_block_equals_successive_decode_steps():
         assert np.allclose(step[0], block[t], atol=1e-12)
         kc[0, :, k + t] = O.rope(kn[0, t], [k + 1 + t] * h, 1e4)
         vc[0, :, k + t] = vn[0, t]
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding helper (used by the robustness parity cases)
+# ---------------------------------------------------------------------------
+
+
+def test_round_bf16_matches_torch_conversion():
+    # fp32-representable values: torch's fp32 -> bf16 conversion (round to
+    # nearest even) is an independent implementation of the same rounding
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        [0.0, -0.0, 1.0, -3.5]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
+
+
+def test_round_bf16_ties_to_even():
+    # bf16 spacing just above 1 is 2**-7: halfway points go to the even
+    # significand, others to the nearest
+    assert O.round_bf16(np.array(1.0 + 2.0 ** -8)) == 1.0
+    assert O.round_bf16(np.array(1.0 + 3 * 2.0 ** -8)) == 1.0 + 2.0 ** -6
+    assert O.round_bf16(np.array(1.0 + 2.0 ** -8 + 2.0 ** -20)) == 1.0 + 2.0 ** -7
+    assert O.round_bf16(np.array(-(1.0 + 3 * 2.0 ** -8))) == -(1.0 + 2.0 ** -6)
+
+
+def test_round_rotated_changes_only_rounding():
+    # on bf16-representable inputs the rounded oracle differs from the exact
+    # one (the rotated values are not bf16 values), but only by what rounding
+    # the rotated Q and new K can move a softmax-weighted average
+    rng = np.random.default_rng(12)
+    gk, gv = rng.standard_normal((4, 8)), rng.standard_normal((4, 8))
+    q, kn, vn = (O.round_bf16(rng.standard_normal((3, 8))) for _ in range(3))
+    exact = O.gist_pair_attention(gk, gv, q, kn, vn, 5, 1e4, 0.35)
+    rounded = O.gist_pair_attention(gk, gv, q, kn, vn, 5, 1e4, 0.35, round_rotated=True)
+    assert not np.array_equal(exact, rounded)
+    assert np.abs(exact - rounded).max() < 2e-2
