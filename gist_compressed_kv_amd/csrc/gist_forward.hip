@@ -218,6 +218,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // one instruction.  A per-wave LDS buffer converts to and from the MFMA
   // operand layout.  Addresses are a wave-uniform base plus 32-bit lane
   // offsets (scalar-base addressing form).
+  // Q is read once, in whole lines: its loads are non-temporal (the staging
+  // loads are not: they touch parts of lines that other loads then reuse)
   constexpr int CPR = D / 8;   // 16-byte chunks per (token, head) row
   constexpr int RPI = 64 / CPR; // token rows per instruction
   const int cl = lane % CPR, rl = lane / CPR;
@@ -240,14 +242,15 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   auto load_q = [&](auto slot, const int hq) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      raw[decltype(slot)::value][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2);
+      raw[decltype(slot)::value][s] =
+          __builtin_nontemporal_load((const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2));
   };
 #pragma unroll
   for (int i = 0; i < QPF; ++i) {
     const int hq = i < G ? i : G - 1;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      raw[i][s] = *(const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2);
+      raw[i][s] = __builtin_nontemporal_load((const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2));
   }
 
   __builtin_amdgcn_sched_barrier(0);

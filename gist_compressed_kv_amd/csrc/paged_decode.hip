@@ -213,8 +213,9 @@ decode_split(const DecodeArgs a) {
   auto issue = [&](auto tc) {
     constexpr int t = decltype(tc)::value;
     const int64_t off = (int64_t)(t < klast ? t : klast) * D;
-    kb[t % PD] = *(const rawv_t*)(kp + off);
-    vb[t % PD] = *(const rawv_t*)(vp + off);
+    // the cache is streamed once per step, in whole rows: non-temporal loads
+    kb[t % PD] = __builtin_nontemporal_load((const rawv_t*)(kp + off));
+    vb[t % PD] = __builtin_nontemporal_load((const rawv_t*)(vp + off));
   };
   auto unpack = [](const rawv_t& w, float* f) {
     if constexpr (sizeof(T) == 2) {
