@@ -36,6 +36,7 @@ COUNTER_FILES = {
     "24L_b500": ("gist_fwd_mfma_d64_24L_b500_counters.json", "gist_forward.hip"),
     "wide_eos": ("gist_fwd_eos_d128_wide_eos_counters.json", "gist_forward.hip"),
     "paged": ("paged_decode_32x4096_counters.json", "paged_decode.hip"),
+    "paged_fp8": ("paged_decode_fp8_32x4096_counters.json", "paged_decode.hip"),
 }
 
 
@@ -60,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
                     choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos", "paged",
-                             "copy"])
+                             "paged_fp8", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
@@ -139,25 +140,30 @@ def copy_probe(args):
                       "ms_per_step": dt * 1e3}), flush=True)
 
 
-def decode_bytes_per_request_layer(wl) -> int:
+def decode_bytes_per_request_layer(wl, fp8: bool = False) -> int:
     """Algorithmic bytes of one decode step of one request in one layer: the
-    cached K and V it attends over, q, k_new, v_new, the output, and its
-    block-table row, context length and position."""
+    cached K and V it attends over (1 byte per element plus one fp32 scale per
+    block and head for each of K and V when the cache is fp8), q, k_new, v_new,
+    the output, and its block-table row, context length and position."""
     b = wl.dtype.itemsize
-    cache = 2 * wl.context * wl.h * wl.d * b
+    if fp8:
+        cache = 2 * wl.context * wl.h * wl.d + 2 * 4 * wl.blocks_per_request * wl.h
+    else:
+        cache = 2 * wl.context * wl.h * wl.d * b
     return (cache + wl.hq * wl.d * b + 2 * wl.h * wl.d * b + wl.hq * wl.d * b
             + 4 * wl.blocks_per_request + 8)
 
 
-def paged_bench(args):
+def paged_bench(args, fp8: bool = False):
     """One decode step of 32 requests over 4096 cached tokens in every one of
-    32 layers (each layer its own paged cache and its own inputs)."""
+    32 layers (each layer its own paged cache and its own inputs); with fp8
+    the cache holds E4M3 codes with per-(block, head) scales."""
     import torch
 
     import gist_compressed_kv_amd as G
     from gist_compressed_kv_amd import synth
 
-    wl = synth.PAGED
+    wl = synth.PAGED_FP8 if fp8 else synth.PAGED
     dev = "cuda"
     nblk = wl.requests * wl.blocks_per_request
     print(f"[bench] generating inputs: {wl.name}", file=sys.stderr, flush=True)
@@ -166,8 +172,13 @@ def paged_bench(args):
     pos = lens + 1
     layers = []
     for li in range(wl.layers):
-        kc = synth.randn((nblk, wl.h, wl.block_size, wl.d), synth.tensor_seed(wl.seed, 11, li), wl.dtype, dev)
-        vc = synth.randn((nblk, wl.h, wl.block_size, wl.d), synth.tensor_seed(wl.seed, 12, li), wl.dtype, dev)
+        shape = (nblk, wl.h, wl.block_size, wl.d)
+        if fp8:
+            kc = synth.randn_fp8_blocks(shape, synth.tensor_seed(wl.seed, 11, li), dev)
+            vc = synth.randn_fp8_blocks(shape, synth.tensor_seed(wl.seed, 12, li), dev)
+        else:
+            kc = synth.randn(shape, synth.tensor_seed(wl.seed, 11, li), wl.dtype, dev)
+            vc = synth.randn(shape, synth.tensor_seed(wl.seed, 12, li), wl.dtype, dev)
         q = synth.randn((wl.requests, wl.hq, wl.d), synth.tensor_seed(wl.seed, 13, li), wl.dtype, dev)
         kn = synth.randn((wl.requests, wl.h, wl.d), synth.tensor_seed(wl.seed, 14, li), wl.dtype, dev)
         vn = synth.randn((wl.requests, wl.h, wl.d), synth.tensor_seed(wl.seed, 15, li), wl.dtype, dev)
@@ -179,8 +190,12 @@ def paged_bench(args):
 
     def step():
         for kc, vc, q, kn, vn, out in layers:
-            G.paged_decode_attn(kc, vc, table, lens, q, kn, vn, pos, 10000.0, None, out=out,
-                                workspace=ws, stream=stream)
+            if fp8:
+                G.paged_decode_attn_fp8(kc[0], vc[0], kc[1], vc[1], table, lens, q, kn, vn, pos,
+                                        10000.0, None, out=out, workspace=ws, stream=stream)
+            else:
+                G.paged_decode_attn(kc, vc, table, lens, q, kn, vn, pos, 10000.0, None, out=out,
+                                    workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -195,17 +210,22 @@ def paged_bench(args):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     # one call = the split kernel then the combine kernel
     avg_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
-    bytes_unit = decode_bytes_per_request_layer(wl)
+    bytes_unit = decode_bytes_per_request_layer(wl, fp8)
     achieved = bytes_unit * wl.requests / avg_s / 1e9
     print(json.dumps({
-        "metric": "paged decode tokens/s (32 requests x 4096 cached tokens, 32 layers)",
+        "metric": "paged decode tokens/s (32 requests x 4096 cached tokens, 32 layers"
+                  + (", fp8 E4M3 cache)" if fp8 else ")"),
         "value": wl.requests / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic N(0,1) caches, seeded block tables",
+        "vs_baseline": None, "dtype": "fp8 cache, bf16 activations" if fp8 else "bf16",
+        "data": "synthetic N(0,1) caches" + (" quantized per (block, head)" if fp8 else "")
+                + ", seeded block tables",
         "config": {"workload": wl.name},
-        "roofline": {"bound": "hbm", "kernel": "decode_split + decode_combine",
+        "roofline": {"bound": "hbm",
+                     "kernel": "decode_split<fp8> + decode_combine" if fp8 else "decode_split + decode_combine",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": measured_traffic("paged"),
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("paged_fp8" if fp8 else "paged"),
                      "bytes_per_unit": bytes_unit, "units_per_launch": wl.requests,
                      "avg_launch_us": avg_s * 1e6}}), flush=True)
 
@@ -222,8 +242,8 @@ def main():
     if args.workload == "copy":
         copy_probe(args)
         return
-    if args.workload == "paged":
-        paged_bench(args)
+    if args.workload in ("paged", "paged_fp8"):
+        paged_bench(args, fp8=args.workload == "paged_fp8")
         return
 
     import gist_compressed_kv_amd as G

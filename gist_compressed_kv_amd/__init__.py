@@ -165,3 +165,38 @@ def paged_decode_attn(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table:
         ptrs[7], Hq, H, d, _code(dt), rope_base, scale, ptrs[8], ptrs[9],
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)), "paged_decode_attn")
     return out
+
+
+def paged_decode_attn_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                          v_scale: torch.Tensor, block_table: torch.Tensor,
+                          context_lens: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                          v_new: torch.Tensor, positions: torch.Tensor,
+                          rope_base: float = 10000.0, scale: float | None = None,
+                          out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """k_cache, v_cache uint8 E4M3 codes [n_blocks, H, block_size, d]; k_scale, v_scale
+    fp32 [n_blocks, H]; q [R, Hq, d], k_new, v_new [R, H, d] bf16; returns out [R, Hq, d]."""
+    n_blocks, H, bs, d = k_cache.shape
+    R, Hq, _ = q.shape
+    max_blocks = block_table.shape[1] if block_table.dim() == 2 else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    need = paged_decode_workspace_bytes(R, Hq, max(max_blocks, 1), bs, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    bf = torch.bfloat16
+    ptrs = (_dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8, k_cache.shape),
+            _dev(k_scale, "k_scale", torch.float32, (n_blocks, H)),
+            _dev(v_scale, "v_scale", torch.float32, (n_blocks, H)),
+            _dev(block_table, "block_table", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32, (R,)),
+            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (R, H, d)), _dev(v_new, "v_new", bf, (R, H, d)),
+            _dev(positions, "positions", torch.int32, (R,)), _dev(out, "out", bf, q.shape),
+            _dev(workspace, "workspace"))
+    _lib.check(_lib.lib().paged_decode_attn_fp8(
+        ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], max_blocks, ptrs[5], R, ptrs[6],
+        ptrs[7], ptrs[8], ptrs[9], Hq, H, d, rope_base, scale, ptrs[10], ptrs[11],
+        workspace.numel() * workspace.element_size(), _stream_ptr(stream)), "paged_decode_attn_fp8")
+    return out

@@ -44,6 +44,9 @@ SIGNATURES = {
     "paged_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "paged_decode_attn": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp,
                                  _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _sz, _vp]),
+    "paged_decode_attn_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp,
+                                     _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _sz,
+                                     _vp]),
     "gist_last_error": (ctypes.c_char_p, []),
 }
 

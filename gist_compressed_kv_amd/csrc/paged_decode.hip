@@ -20,6 +20,7 @@
 //  * decode_combine<T, D>: one wave64 per (request, query head) merges the
 //    split states with the token's own key/value (log-sum-exp weights) and
 //    writes the normalized output.
+#include <type_traits>
 #include <utility>
 
 #include "common.hpp"
@@ -47,6 +48,9 @@ struct DecodeArgs {
   float* ws;
   int nsplit;
   void* out;
+  // fp8 cache only: one fp32 scale per (physical block, KV head), [nblk][H]
+  const float* ksc;
+  const float* vsc;
   RopeFreqs freqs;
   // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
   // set bits b of i (a lane's frequency from scalar arguments only)
@@ -128,7 +132,24 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float* o, float 
   m = mm;
 }
 
-template <typename T, int D, int MAXG>
+// 32-bit words of one lane's slice of a cache row, as a vector (one word: a
+// plain scalar)
+template <int N>
+struct words {
+  typedef unsigned int type __attribute__((ext_vector_type(N)));
+  static __device__ __forceinline__ unsigned int at(const type& w, int i) { return w[i]; }
+};
+template <>
+struct words<1> {
+  typedef unsigned int type;
+  static __device__ __forceinline__ unsigned int at(const type& w, int) { return w; }
+};
+
+// T: element type of q, k_new, v_new and out (and of the cache unless FP8).
+// FP8: the cache holds OCP E4M3 codes (1 sign, 4 exponent bits with bias 7,
+// 3 mantissa bits; gfx950's v_cvt_pk_f32_fp8 decodes exactly this format),
+// element = decode(code) * scale[block][KV head].
+template <typename T, int D, int MAXG, bool FP8 = false>
 __global__ void __launch_bounds__(256)
 decode_split(const DecodeArgs a) {
   constexpr int E = D / 16;  // channels per lane
@@ -202,10 +223,19 @@ decode_split(const DecodeArgs a) {
       row_ok ? (((int64_t)phys * a.H + g) * a.bs + (kbeg % a.bs)) * D + E * c : (int64_t)E * c;
   const int nvalid = row_ok ? nkeys : 0;
   const int klast = nvalid > 0 ? nvalid - 1 : 0;
-  const T* kp = (const T*)a.kc + base;
-  const T* vp = (const T*)a.vc + base;
-  constexpr int NW = E * (int)sizeof(T) / 4;  // 32-bit words per lane and key
-  typedef unsigned int rawv_t __attribute__((ext_vector_type(NW)));
+  typedef std::conditional_t<FP8, uint8_t, T> C;  // cache element
+  const C* kp = (const C*)a.kc + base;
+  const C* vp = (const C*)a.vc + base;
+  constexpr int NW = E * (int)sizeof(C) / 4;  // 32-bit words per lane and key
+  typedef typename words<NW>::type rawv_t;
+  // fp8: the row's block scales, folded into the logit and into the weight
+  // that multiplies V (not into the softmax sum)
+  float kmul = a.scale_log2, vmul = 1.f;
+  if constexpr (FP8) {
+    const int64_t si = row_ok ? (int64_t)phys * a.H + g : 0;
+    kmul *= a.ksc[si];
+    vmul = a.vsc[si];
+  }
   // keys in flight per lane: 8, or 4 when the per-head state of a wide group
   // already takes most of the registers
   constexpr int PD = MAXG * E >= 32 ? 4 : 8;
@@ -218,15 +248,26 @@ decode_split(const DecodeArgs a) {
     vb[t % PD] = __builtin_nontemporal_load((const rawv_t*)(vp + off));
   };
   auto unpack = [](const rawv_t& w, float* f) {
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (FP8) {
+      typedef float f2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
       for (int i = 0; i < NW; ++i) {
-        f[2 * i] = __uint_as_float(w[i] << 16);
-        f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)words<NW>::at(w, i), false);
+        const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)words<NW>::at(w, i), true);
+        f[4 * i] = lo.x;
+        f[4 * i + 1] = lo.y;
+        f[4 * i + 2] = hi.x;
+        f[4 * i + 3] = hi.y;
+      }
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        f[2 * i] = __uint_as_float(words<NW>::at(w, i) << 16);
+        f[2 * i + 1] = __uint_as_float(words<NW>::at(w, i) & 0xffff0000u);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NW; ++i) f[i] = __uint_as_float(w[i]);
+      for (int i = 0; i < NW; ++i) f[i] = __uint_as_float(words<NW>::at(w, i));
     }
   };
   for_each_const_d<PD>([&](auto tc) { issue(tc); });
@@ -245,7 +286,7 @@ decode_split(const DecodeArgs a) {
         for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kf[e], part);
         // the logit is formed for every key and masked by selects (no branch,
         // so the loads stay where they were issued)
-        const float dot = row16_sum_d(part) * a.scale_log2;
+        const float dot = row16_sum_d(part) * kmul;
         const float sc = valid ? dot : -INFINITY;
         const float mnew = fmaxf(m[hh], sc);
         // exponents never see -inf - -inf: an all-masked state keeps alpha = 1,
@@ -254,8 +295,9 @@ decode_split(const DecodeArgs a) {
         const float pw = __builtin_amdgcn_exp2f(valid ? sc - mnew : -INFINITY);
         m[hh] = mnew;
         l[hh] = l[hh] * alpha + pw;
+        const float pv = pw * vmul;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pw, vf[e], o[hh][e] * alpha);
+        for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pv, vf[e], o[hh][e] * alpha);
       }
     }
   });
@@ -418,17 +460,17 @@ int num_splits(int max_blocks, int block_size) {
 }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-template <typename T, int D>
+template <typename T, int D, bool FP8 = false>
 void launch_decode(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid1((unsigned)((int64_t)a.R * a.H * a.nsplit));
   if (a.G <= 1)
-    hipLaunchKernelGGL((decode_split<T, D, 1>), grid1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split<T, D, 1, FP8>), grid1, dim3(256), 0, s, a);
   else if (a.G <= 2)
-    hipLaunchKernelGGL((decode_split<T, D, 2>), grid1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split<T, D, 2, FP8>), grid1, dim3(256), 0, s, a);
   else if (a.G <= 4)
-    hipLaunchKernelGGL((decode_split<T, D, 4>), grid1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split<T, D, 4, FP8>), grid1, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_split<T, D, 8>), grid1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_split<T, D, 8, FP8>), grid1, dim3(256), 0, s, a);
   hipLaunchKernelGGL((decode_combine<T, D>), dim3((unsigned)((int64_t)a.R * a.Hq)), dim3(64), 0,
                      s, a);
 }
@@ -440,46 +482,51 @@ extern "C" size_t paged_decode_workspace_bytes(int R, int Hq, int max_blocks, in
   return (size_t)R * Hq * num_splits(max_blocks, block_size) * (d + kWsPad) * sizeof(float);
 }
 
-extern "C" gist_status paged_decode_attn(const void* k_cache, const void* v_cache,
-                                         int64_t n_blocks, int block_size,
-                                         const int32_t* block_table, int max_blocks,
-                                         const int32_t* context_lens, int R, const void* q,
-                                         const void* k_new, const void* v_new,
-                                         const int32_t* positions, int Hq, int H, int d,
-                                         gist_dtype dtype, float rope_base, float scale, void* out,
-                                         void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+// Shared by both entry points: fp8 selects the E4M3 cache with per-(block,
+// KV head) scales (activations in bf16); `fn` names the entry point in errors.
+gist_status decode_call(const char* fn, bool fp8, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, int64_t n_blocks,
+                        int block_size, const int32_t* block_table, int max_blocks,
+                        const int32_t* context_lens, int R, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* positions, int Hq, int H, int d,
+                        gist_dtype dtype, float rope_base, float scale, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   clear_error();
+  const std::string name(fn);
   if (dtype != GIST_BF16 && dtype != GIST_F32)
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: unknown dtype");
-  if (R < 0) return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: R < 0");
+    return fail(GIST_ERR_INVALID_ARG, name + ": unknown dtype");
+  if (R < 0) return fail(GIST_ERR_INVALID_ARG, name + ": R < 0");
   if (H <= 0 || Hq < H || Hq % H != 0)
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: Hq must be a positive multiple of H");
-  if (Hq / H > 8) return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: Hq/H must be <= 8");
+    return fail(GIST_ERR_INVALID_ARG, name + ": Hq must be a positive multiple of H");
+  if (Hq / H > 8) return fail(GIST_ERR_UNSUPPORTED, name + ": Hq/H must be <= 8");
   if (d != 64 && d != 128)
-    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: head_dim must be 64 or 128");
+    return fail(GIST_ERR_UNSUPPORTED, name + ": head_dim must be 64 or 128");
   if (block_size <= 0 || block_size % 16 != 0)
-    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: block_size must be a multiple of 16");
+    return fail(GIST_ERR_UNSUPPORTED, name + ": block_size must be a multiple of 16");
   if (n_blocks <= 0 || max_blocks <= 0)
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: n_blocks and max_blocks must be > 0");
+    return fail(GIST_ERR_INVALID_ARG, name + ": n_blocks and max_blocks must be > 0");
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: scale must be positive and finite");
+    return fail(GIST_ERR_INVALID_ARG, name + ": scale must be positive and finite");
   if (!(rope_base > 0.f) || !std::isfinite(rope_base))
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: rope_base must be positive");
+    return fail(GIST_ERR_INVALID_ARG, name + ": rope_base must be positive");
   if (R == 0) return GIST_OK;
   if (!k_cache || !v_cache || !block_table || !context_lens || !q || !k_new || !v_new ||
-      !positions || !out || !workspace)
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: NULL pointer argument");
+      !positions || !out || !workspace || (fp8 && (!k_scale || !v_scale)))
+    return fail(GIST_ERR_INVALID_ARG, name + ": NULL pointer argument");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
       !aligned16(v_new) || !aligned16(out) || !aligned16(workspace))
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: tensors must be 16-byte aligned");
+    return fail(GIST_ERR_INVALID_ARG, name + ": tensors must be 16-byte aligned");
+  if (fp8 && ((((uintptr_t)k_scale) & 3) != 0 || (((uintptr_t)v_scale) & 3) != 0))
+    return fail(GIST_ERR_INVALID_ARG, name + ": scales must be 4-byte aligned");
   const size_t need = paged_decode_workspace_bytes(R, Hq, max_blocks, block_size, d);
   if (workspace_bytes < need)
-    return fail(GIST_ERR_INVALID_ARG, "paged_decode_attn: workspace too small (" +
+    return fail(GIST_ERR_INVALID_ARG, name + ": workspace too small (" +
                                           std::to_string(workspace_bytes) + " < " +
                                           std::to_string(need) + ")");
   const int nsplit = num_splits(max_blocks, block_size);
   if ((int64_t)R * H * nsplit > INT32_MAX)
-    return fail(GIST_ERR_UNSUPPORTED, "paged_decode_attn: too many splits for one launch");
+    return fail(GIST_ERR_UNSUPPORTED, name + ": too many splits for one launch");
 
   DecodeArgs a;
   a.kc = k_cache;
@@ -505,14 +552,50 @@ extern "C" gist_status paged_decode_attn(const void* k_cache, const void* v_cach
   a.ws = (float*)workspace;
   a.nsplit = nsplit;
   a.out = out;
+  a.ksc = k_scale;
+  a.vsc = v_scale;
   make_rope_freqs(a.freqs, d, rope_base);
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == GIST_BF16) {
+  if (fp8) {
+    if (d == 64) launch_decode<bf16_t, 64, true>(a, s);
+    else launch_decode<bf16_t, 128, true>(a, s);
+  } else if (dtype == GIST_BF16) {
     if (d == 64) launch_decode<bf16_t, 64>(a, s);
     else launch_decode<bf16_t, 128>(a, s);
   } else {
     if (d == 64) launch_decode<float, 64>(a, s);
     else launch_decode<float, 128>(a, s);
   }
-  return check_launch("paged_decode_attn");
+  return check_launch(fn);
+}
+}  // namespace
+
+extern "C" gist_status paged_decode_attn(const void* k_cache, const void* v_cache,
+                                         int64_t n_blocks, int block_size,
+                                         const int32_t* block_table, int max_blocks,
+                                         const int32_t* context_lens, int R, const void* q,
+                                         const void* k_new, const void* v_new,
+                                         const int32_t* positions, int Hq, int H, int d,
+                                         gist_dtype dtype, float rope_base, float scale, void* out,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call("paged_decode_attn", false, k_cache, v_cache, nullptr, nullptr, n_blocks,
+                     block_size, block_table, max_blocks, context_lens, R, q, k_new, v_new,
+                     positions, Hq, H, d, dtype, rope_base, scale, out, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" gist_status paged_decode_attn_fp8(const void* k_cache, const void* v_cache,
+                                             const float* k_scale, const float* v_scale,
+                                             int64_t n_blocks, int block_size,
+                                             const int32_t* block_table, int max_blocks,
+                                             const int32_t* context_lens, int R, const void* q,
+                                             const void* k_new, const void* v_new,
+                                             const int32_t* positions, int Hq, int H, int d,
+                                             float rope_base, float scale, void* out,
+                                             void* workspace, size_t workspace_bytes,
+                                             void* stream) {
+  return decode_call("paged_decode_attn_fp8", true, k_cache, v_cache, k_scale, v_scale,
+                     n_blocks, block_size, block_table, max_blocks, context_lens, R, q, k_new,
+                     v_new, positions, Hq, H, d, GIST_BF16, rope_base, scale, out, workspace,
+                     workspace_bytes, stream);
 }

@@ -44,6 +44,26 @@ def randn(shape, seed: int, dtype: torch.dtype, device, chunk_elems: int = 1 << 
     return out
 
 
+def randn_fp8_blocks(shape, seed: int, device):
+    """A synthetic fp8 paged cache [n_blocks][H][block][d]: N(0,1) values (as
+    ``randn``) stored as OCP E4M3 codes with one fp32 scale per (block, head),
+    scale = amax / 448, quantized by torch's own E4M3 conversion.  Returns
+    (codes uint8, scales fp32 [n_blocks][H])."""
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scales = torch.empty(shape[:2], dtype=torch.float32, device=device)
+    g = generator(seed, device)
+    per_block = shape[1] * shape[2] * shape[3]
+    step = max(1, (1 << 27) // per_block)
+    for b0 in range(0, shape[0], step):
+        b1 = min(shape[0], b0 + step)
+        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        amax = x.abs().amax(dim=(2, 3))
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        codes[b0:b1] = (x / sc[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales[b0:b1] = sc
+    return codes, scales
+
+
 def item_ids_per_query(n_queries: int, n_candidates: int, n_items: int, seed: int,
                        device) -> torch.Tensor:
     """Candidate ids, query-major: each query draws n_candidates distinct items
@@ -121,3 +141,7 @@ WIDE_EOS = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query gis
 PAGED = DecodeWorkload("paged decode: 32 requests x 4096 cached tokens in 256-token blocks, "
                        "Hq=H=32, d=128, 32 layers, bf16", 32, 32, 4096, 256, 32, 32, 128,
                        torch.bfloat16, 5)
+
+PAGED_FP8 = DecodeWorkload("paged decode, fp8 E4M3 cache with per-(block, head) scales: 32 requests "
+                           "x 4096 cached tokens in 256-token blocks, Hq=H=32, d=128, 32 layers, "
+                           "bf16 activations", 32, 32, 4096, 256, 32, 32, 128, torch.bfloat16, 6)

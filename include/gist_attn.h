@@ -162,6 +162,29 @@ gist_status paged_decode_attn(const void* k_cache, const void* v_cache, int64_t 
                               float scale, void* out, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * paged_decode_attn_fp8 — paged_decode_attn over a KV cache stored as fp8
+ * codes (OCP FP8 E4M3: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+ * bits; largest finite value 448; codes 0x7F and 0xFF are NaN) with one fp32
+ * scale per (physical block, KV head) for K and one for V.  The pages fix no
+ * quantized format; this one halves the cache bytes the decode step streams
+ * ([KVC] Memory: M_KV = 2*B*L*T*h_kv*d_h*b with b = 1).
+ *   k_cache, v_cache  device uint8 codes [n_blocks][H][block_size][d];
+ *                     element = decode(code) * k_scale[block][head] (resp. v)
+ *   k_scale, v_scale  device fp32 [n_blocks][H], 4-byte aligned
+ *   q, k_new, v_new, out  bf16, as in paged_decode_attn (the new token's own
+ *                     key and value are not quantized)
+ * Every other argument, the workspace size and the error behaviour are those
+ * of paged_decode_attn.
+ */
+gist_status paged_decode_attn_fp8(const void* k_cache, const void* v_cache, const float* k_scale,
+                                  const float* v_scale, int64_t n_blocks, int block_size,
+                                  const int32_t* block_table, int max_blocks,
+                                  const int32_t* context_lens, int R, const void* q,
+                                  const void* k_new, const void* v_new, const int32_t* positions,
+                                  int Hq, int H, int d, float rope_base, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* gist_last_error — message of the last failed call on this thread ("" if none). */
 const char* gist_last_error(void);
 

@@ -230,6 +230,26 @@ def pool_write(pool: np.ndarray, layer: int, ids, k_src: np.ndarray,
 # ---------------------------------------------------------------------------
 
 
+def decode_e4m3(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (uint8): 1 sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent 0 holds the subnormals m * 2**-9;
+    exponent 15 with mantissa 7 is NaN (there is no infinity), so the largest
+    finite value is 1.75 * 2**8 = 448."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    val = np.where((e == 15) & (c & 7 == 7), np.nan, val)
+    return sign * val
+
+
+def dequantize_blocks(codes, scales) -> np.ndarray:
+    """Paged cache of E4M3 codes [n_blocks][H][block][d] with one scale per
+    (block, head) [n_blocks][H]: element = decode(code) * scale."""
+    return decode_e4m3(codes) * np.asarray(scales, np.float64)[:, :, None, None]
+
+
 def gather_logical(cache: np.ndarray, block_row, n_tokens: int, g: int) -> np.ndarray:
     """Rows 0..n_tokens-1 of one request, KV head g, in logical order.
 

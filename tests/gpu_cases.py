@@ -86,9 +86,17 @@ class GistCase:
 
 class DecodeCase:
     def __init__(self, n_blocks, h, bs, d, hq, lens, dtype, seed, table=None, max_blocks=None,
-                 device="cuda"):
-        self.kc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 11), dtype, device)
-        self.vc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 12), dtype, device)
+                 device="cuda", fp8=False):
+        self.fp8 = fp8
+        if fp8:  # E4M3 codes with per-(block, head) scales; activations in bf16
+            dtype = torch.bfloat16
+            self.kc, self.ksc = synth.randn_fp8_blocks((n_blocks, h, bs, d),
+                                                       synth.tensor_seed(seed, 11), device)
+            self.vc, self.vsc = synth.randn_fp8_blocks((n_blocks, h, bs, d),
+                                                       synth.tensor_seed(seed, 12), device)
+        else:
+            self.kc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 11), dtype, device)
+            self.vc = synth.randn((n_blocks, h, bs, d), synth.tensor_seed(seed, 12), dtype, device)
         R = len(lens)
         if max_blocks is None:
             max_blocks = max(1, -(-max(lens) // bs))
@@ -104,6 +112,10 @@ class DecodeCase:
         self.dtype = dtype
 
     def run(self, out=None, workspace=None):
+        if self.fp8:
+            return G.paged_decode_attn_fp8(self.kc, self.vc, self.ksc, self.vsc, self.table,
+                                           self.lens, self.q, self.kn, self.vn, self.positions,
+                                           ROPE_BASE, self.scale, out=out, workspace=workspace)
         return G.paged_decode_attn(self.kc, self.vc, self.table, self.lens, self.q, self.kn,
                                    self.vn, self.positions, ROPE_BASE, self.scale, out=out,
                                    workspace=workspace)
@@ -118,8 +130,12 @@ class DecodeCase:
                        for b in table[r][: -(-int(lens[r]) // self.kc.shape[2])]} | {0})
         remap = {b: i for i, b in enumerate(used)}
         used_t = torch.as_tensor(used, device=self.kc.device)
-        kc = f64(self.kc[used_t])
-        vc = f64(self.vc[used_t])
+        if self.fp8:
+            kc = O.dequantize_blocks(self.kc[used_t].cpu().numpy(), self.ksc[used_t].cpu().numpy())
+            vc = O.dequantize_blocks(self.vc[used_t].cpu().numpy(), self.vsc[used_t].cpu().numpy())
+        else:
+            kc = f64(self.kc[used_t])
+            vc = f64(self.vc[used_t])
         t2 = np.vectorize(lambda b: remap.get(int(b), 0))(table)
         idx = torch.as_tensor(reqs, device=self.q.device)
         return O.paged_decode(kc, vc, t2, lens, f64(self.q[idx]), f64(self.kn[idx]),

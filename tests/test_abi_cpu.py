@@ -27,7 +27,7 @@ def L():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_]+)\s*\(", text)) - {"sizeof"})
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
 
 
 def test_every_declared_symbol_is_exported_and_bound(L):
@@ -167,3 +167,24 @@ def test_paged_decode_validation(L):
     assert _dec(L, ws_bytes=16) == _lib.GIST_ERR_INVALID_ARG
     assert "workspace too small" in L.gist_last_error().decode()
     assert _dec(L, R=0, ptr=None) == _lib.GIST_OK
+
+
+def _dec8(L, R=2, Hq=4, H=2, d=64, bs=16, max_blk=4, nblk=8, ws_bytes=None, ptr=FAKE, sptr=FAKE,
+          scale=0.125):
+    if ws_bytes is None:
+        ws_bytes = L.paged_decode_workspace_bytes(R, Hq, max_blk, bs, d)
+    return L.paged_decode_attn_fp8(ptr, ptr, sptr, sptr, nblk, bs, ptr, max_blk, ptr, R, ptr, ptr,
+                                   ptr, ptr, Hq, H, d, 1e4, scale, ptr, ptr, ws_bytes, None)
+
+
+def test_paged_decode_fp8_validation(L):
+    assert _dec8(L, R=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec8(L, Hq=5) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec8(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _dec8(L, bs=24) == _lib.GIST_ERR_UNSUPPORTED
+    assert _dec8(L, sptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert "paged_decode_attn_fp8" in L.gist_last_error().decode()
+    assert _dec8(L, sptr=ctypes.c_void_p((1 << 20) + 2)) == _lib.GIST_ERR_INVALID_ARG
+    assert "4-byte aligned" in L.gist_last_error().decode()
+    assert _dec8(L, ws_bytes=16) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec8(L, R=0, ptr=None, sptr=None) == _lib.GIST_OK

@@ -342,3 +342,53 @@ def test_robust_paged_decode():
     err = float(np.abs(f64(out) - case.oracle()).max())
     say(f"paged robust: max-abs err {err:.3g}")
     assert err <= TOL[torch.bfloat16]
+
+
+# ---------------------------------------------------------------------------
+# Paged decode over an fp8 (E4M3) cache with per-(block, head) scales.  The
+# oracle decodes the same codes exactly, so the bar is the bf16 one.
+# ---------------------------------------------------------------------------
+
+FP8_SHAPES = [
+    # n_blocks, h, bs, d, hq, lens
+    (70, 4, 256, 128, 4, [4096 - 7, 1, 255, 257]),
+    (70, 2, 64, 64, 8, [640, 1000, 0, 16]),
+    (80, 8, 16, 128, 32, [120, 384, 33]),
+    (30, 1, 128, 64, 2, [1500, 77]),
+]
+
+
+@pytest.mark.parametrize("shape", FP8_SHAPES, ids=lambda s: "h%d_bs%d_d%d_hq%d" % s[1:5])
+def test_paged_decode_fp8_shapes(shape):
+    n_blocks, h, bs, d, hq, lens = shape
+    max_blocks = max(1, -(-max(lens) // bs))
+    case = DecodeCase(n_blocks, h, bs, d, hq, lens, torch.bfloat16, 600 + d + hq, fp8=True,
+                      max_blocks=max_blocks)
+    out = case.run()
+    torch.cuda.synchronize()
+    err = float(np.abs(f64(out) - case.oracle()).max())
+    say(f"paged fp8 {shape[:5]}: max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_paged_decode_fp8_workload():
+    wl = synth.PAGED_FP8
+    n_blocks = wl.requests * wl.blocks_per_request
+    case = DecodeCase(n_blocks, wl.h, wl.block_size, wl.d, wl.hq, [wl.context] * wl.requests,
+                      wl.dtype, wl.seed, fp8=True)
+    out = case.run()
+    torch.cuda.synchronize()
+    err = float(np.abs(f64(out) - case.oracle()).max())
+    say(f"paged fp8 workload (one layer, all 32 requests): max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_paged_decode_fp8_bad_block_is_nan():
+    case = DecodeCase(20, 2, 64, 64, 4, [200, 200], torch.bfloat16, 604, fp8=True)
+    case.table[1, 1] = 999  # out of range for request 1 only
+    out = case.run().float()
+    torch.cuda.synchronize()
+    assert torch.isnan(out[1]).all() and torch.isfinite(out[0]).all()
+    err = float(np.abs(f64(out[0:1]) - case.oracle([0])).max())
+    assert err <= TOL[torch.bfloat16]
+

@@ -537,3 +537,33 @@ def test_round_rotated_changes_only_rounding():
     rounded = O.gist_pair_attention(gk, gv, q, kn, vn, 5, 1e4, 0.35, round_rotated=True)
     assert not np.array_equal(exact, rounded)
     assert np.abs(exact - rounded).max() < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# fp8 (OCP E4M3) cache decode
+# ---------------------------------------------------------------------------
+
+
+def test_decode_e4m3_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.decode_e4m3(codes), ref)
+
+
+def test_decode_e4m3_landmarks():
+    v = O.decode_e4m3(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x7E, 0x7F, 0x80, 0xB8, 0xFE],
+                               np.uint8))
+    assert v[0] == 0.0 and v[1] == 2.0 ** -9 and v[2] == 7 * 2.0 ** -9
+    assert v[3] == 2.0 ** -6 and v[4] == 1.0 and v[5] == 448.0
+    assert np.isnan(v[6]) and v[7] == 0.0 and np.signbit(v[7])
+    assert v[8] == -1.0 and v[9] == -448.0
+
+
+def test_dequantize_blocks_applies_one_scale_per_block_and_head():
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 0x7E, (3, 2, 4, 5)).astype(np.uint8)
+    scales = np.array([[1.0, 2.0], [0.5, 4.0], [3.0, 0.25]])
+    d = O.dequantize_blocks(codes, scales)
+    for b in range(3):
+        for h in range(2):
+            np.testing.assert_array_equal(d[b, h], O.decode_e4m3(codes[b, h]) * scales[b, h])
