@@ -35,6 +35,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 COUNTER_FILES = {
     "24L_b500": ("gist_fwd_mfma_d64_24L_b500_counters.json", "gist_forward.hip"),
     "wide_eos": ("gist_fwd_eos_d128_wide_eos_counters.json", "gist_forward.hip"),
+    "wide_eos_fp8": ("gist_fwd_eos_fp8_d128_wide_eos_counters.json", "gist_forward.hip"),
     "paged": ("paged_decode_32x4096_counters.json", "paged_decode.hip"),
     "paged_fp8": ("paged_decode_fp8_32x4096_counters.json", "paged_decode.hip"),
 }
@@ -42,11 +43,19 @@ COUNTER_FILES = {
 
 def gist_bytes_per_pair_layer(wl) -> int:
     """Algorithmic HBM bytes one (pair, layer) must move: the item's gist K/V
-    (and query gist, if any), Q in, K_new/V_new in, O out, the 4-byte id."""
+    (and query gist, if any), Q in, K_new/V_new in, O out, the 4-byte id.
+    An fp8 gist record is one byte per element plus a 4-byte scale per (K or
+    V, head)."""
     b = wl.dtype.itemsize
-    gist = 2 * wl.k * wl.h * wl.d * b
+
+    def record(rows):
+        if wl.fp8:
+            return 2 * rows * wl.h * wl.d + 2 * wl.h * 4
+        return 2 * rows * wl.h * wl.d * b
+
+    gist = record(wl.k)
     # a query's gist rows are shared by its candidates: counted once per query
-    qgist = 2 * wl.kq * wl.h * wl.d * b * wl.queries / wl.pairs
+    qgist = record(wl.kq) * wl.queries / wl.pairs if wl.kq else 0
     q = wl.ell * wl.hq * wl.d * b
     kv_new = 2 * wl.ell * wl.h * wl.d * b
     o = wl.ell * wl.hq * wl.d * b
@@ -60,8 +69,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos", "paged",
-                             "paged_fp8", "copy"])
+                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos",
+                             "wide_eos_fp8", "paged", "paged_fp8", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
@@ -251,21 +260,31 @@ def main():
 
     wl = {"24L_b500": synth.L24_B500, "24L_b2000": synth.L24_B2000,
           "1L_b500": synth.SINGLE_LAYER, "wide_ell64": synth.WIDE_ELL64,
-          "wide_eos": synth.WIDE_EOS}[args.workload]
+          "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
     dev = "cuda"
     torch.cuda.init()
 
     # ---- inputs, all resident in HBM ------------------------------------
     print(f"[bench] generating inputs: {wl.name}", file=sys.stderr, flush=True)
-    pool_t = synth.randn((wl.layers, wl.n_items, 2, wl.h, wl.k, wl.d),
-                         synth.tensor_seed(wl.seed, 1), wl.dtype, dev)
-    pool = G.GistPool(pool_t)
+    if wl.fp8:
+        pool_t = synth.randn_fp8_gist_pool(wl.layers, wl.n_items, wl.k, wl.h, wl.d,
+                                           synth.tensor_seed(wl.seed, 1), dev)
+        pool = G.GistPool(pool_t, shape=(wl.layers, wl.n_items, wl.k, wl.h, wl.d))
+    else:
+        pool_t = synth.randn((wl.layers, wl.n_items, 2, wl.h, wl.k, wl.d),
+                             synth.tensor_seed(wl.seed, 1), wl.dtype, dev)
+        pool = G.GistPool(pool_t)
     ids = synth.item_ids_per_query(wl.queries, wl.pairs // wl.queries, wl.n_items, wl.seed, dev)
     qpool = q_ids = None
     if wl.kq:
-        qpool_t = synth.randn((wl.layers, wl.queries, 2, wl.h, wl.kq, wl.d),
-                              synth.tensor_seed(wl.seed, 2), wl.dtype, dev)
-        qpool = G.GistPool(qpool_t)
+        if wl.fp8:
+            qpool_t = synth.randn_fp8_gist_pool(wl.layers, wl.queries, wl.kq, wl.h, wl.d,
+                                                synth.tensor_seed(wl.seed, 2), dev)
+            qpool = G.GistPool(qpool_t, shape=(wl.layers, wl.queries, wl.kq, wl.h, wl.d))
+        else:
+            qpool_t = synth.randn((wl.layers, wl.queries, 2, wl.h, wl.kq, wl.d),
+                                  synth.tensor_seed(wl.seed, 2), wl.dtype, dev)
+            qpool = G.GistPool(qpool_t)
         q_ids = (torch.arange(wl.pairs, device=dev) // (wl.pairs // wl.queries)).to(torch.int32)
     # one distinct activation set per layer, and at least four for the
     # single-layer workload (one 133 MB set would stay in the 256 MB
@@ -331,7 +350,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic: N(0,1) pools, Q/K/V; seeded item ids (50 distinct candidates per query)",
+        "data": "synthetic: N(0,1) pools" + (" (E4M3 codes, scale amax/448 per block)" if wl.fp8 else "")
+                + ", Q/K/V; seeded item ids (50 distinct candidates per query)",
         "config": {"workload": wl.name, "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
                    "h": wl.h, "head_dim": wl.d, "k": wl.k, "k_query_gist": wl.kq, "ell": wl.ell,
                    "pool_items": wl.n_items, "parallelism": "single GPU"},
@@ -340,7 +360,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
-                      ("gist_fwd_mfma<128>" if wl.ell > 1 else "gist_fwd_eos<128>"),
+                      ("gist_fwd_mfma<128>" if wl.ell > 1 else
+                       ("gist_fwd_eos<128, fp8 gist>" if wl.fp8 else "gist_fwd_eos<128>")),
             "achieved": achieved_gbps,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

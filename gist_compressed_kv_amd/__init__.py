@@ -13,10 +13,11 @@ import math
 import torch
 
 from . import _lib
-from ._lib import GIST_BF16, GIST_F32, GistError  # noqa: F401
+from ._lib import GIST_BF16, GIST_F32, GIST_FP8_E4M3, GistError  # noqa: F401
 
 __all__ = [
-    "GistPool", "GistError", "gist_pool_bytes", "gist_pool_create", "gist_pool_write",
+    "GistPool", "GistError", "gist_pool_bytes", "gist_pool_fp8_storage", "gist_pool_create",
+    "gist_pool_write",
     "gist_attn_forward", "paged_decode_workspace_bytes", "paged_decode_attn",
 ]
 
@@ -49,23 +50,52 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
     return t.data_ptr()
 
 
-def gist_pool_bytes(L: int, N: int, k: int, H: int, d: int, dtype: torch.dtype) -> int:
-    return _lib.lib().gist_pool_bytes(L, N, k, H, d, _code(dtype))
+def gist_pool_bytes(L: int, N: int, k: int, H: int, d: int, dtype) -> int:
+    """dtype: torch.bfloat16, torch.float32, or "fp8" (E4M3 codes + fp32 scales)."""
+    code = GIST_FP8_E4M3 if dtype == "fp8" else _code(dtype)
+    return _lib.lib().gist_pool_bytes(L, N, k, H, d, code)
+
+
+def gist_pool_fp8_storage(L: int, N: int, k: int, H: int, d: int, device="cuda") -> torch.Tensor:
+    """Uninitialised uint8 device storage for an fp8 pool of this shape."""
+    n = gist_pool_bytes(L, N, k, H, d, "fp8")
+    if n == 0:
+        raise ValueError("invalid fp8 pool shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 class GistPool:
-    """A gist pool over a caller-owned device tensor [L][N][2][H][k][d]."""
+    """A gist pool over caller-owned device storage.
 
-    def __init__(self, storage: torch.Tensor):
-        if storage.dim() != 6 or storage.shape[2] != 2:
-            raise ValueError("storage must have shape [L, N, 2, H, k, d]")
-        L, N, _, H, k, d = storage.shape
+    bf16 / fp32: a tensor [L][N][2][H][k][d].  fp8: a flat uint8 tensor of
+    gist_pool_bytes(L, N, k, H, d, "fp8") bytes plus ``shape=(L, N, k, H, d)``;
+    ``codes`` [L][N][2][H][k][d] (uint8) and ``scales`` [L][N][2][H] (fp32)
+    are views of it.  Calls on an fp8 pool take bf16 activations."""
+
+    def __init__(self, storage: torch.Tensor, shape=None):
+        self.fp8 = storage.dtype == torch.uint8
+        if self.fp8:
+            if shape is None or len(shape) != 5:
+                raise ValueError("an fp8 pool needs shape=(L, N, k, H, d)")
+            L, N, k, H, d = (int(x) for x in shape)
+            if storage.dim() != 1:
+                raise ValueError("fp8 pool storage must be a flat uint8 tensor")
+            ncode = L * N * 2 * H * k * d
+            if storage.numel() == ncode + L * N * 2 * H * 4:
+                self.codes = storage[:ncode].view(L, N, 2, H, k, d)
+                self.scales = storage[ncode:].view(torch.float32).view(L, N, 2, H)
+            code, self.act_dtype = GIST_FP8_E4M3, torch.bfloat16
+        else:
+            if storage.dim() != 6 or storage.shape[2] != 2:
+                raise ValueError("storage must have shape [L, N, 2, H, k, d]")
+            L, N, _, H, k, d = storage.shape
+            code, self.act_dtype = _code(storage.dtype), storage.dtype
         self.storage = storage
         self.L, self.N, self.H, self.k, self.d = L, N, H, k, d
         self.dtype = storage.dtype
         handle = _lib.ctypes.c_void_p()
         _lib.check(_lib.lib().gist_pool_create(
-            _lib.ctypes.byref(handle), L, N, k, H, d, _code(storage.dtype),
+            _lib.ctypes.byref(handle), L, N, k, H, d, code,
             _dev(storage, "storage"), storage.numel() * storage.element_size()),
             "gist_pool_create")
         self._handle = handle
@@ -86,8 +116,8 @@ class GistPool:
             pass
 
 
-def gist_pool_create(storage: torch.Tensor) -> GistPool:
-    return GistPool(storage)
+def gist_pool_create(storage: torch.Tensor, shape=None) -> GistPool:
+    return GistPool(storage, shape)
 
 
 def gist_pool_write(pool: GistPool, layer: int, ids: torch.Tensor, k_src: torch.Tensor,
@@ -95,8 +125,8 @@ def gist_pool_write(pool: GistPool, layer: int, ids: torch.Tensor, k_src: torch.
                     stream=None) -> None:
     n = ids.numel()
     shape = (n, pool.k, pool.H, pool.d)
-    args = (_dev(ids, "ids", torch.int32), _dev(k_src, "k_src", pool.dtype, shape),
-            _dev(v_src, "v_src", pool.dtype, shape))
+    args = (_dev(ids, "ids", torch.int32), _dev(k_src, "k_src", pool.act_dtype, shape),
+            _dev(v_src, "v_src", pool.act_dtype, shape))
     _lib.check(_lib.lib().gist_pool_write(pool.handle, layer, args[0], n, args[1], args[2],
                                           src_pos0, rope_base, _stream_ptr(stream)),
                "gist_pool_write")
@@ -118,9 +148,10 @@ def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: tor
     if out is None:
         out = torch.empty_like(q)
     kv_shape = (P, ell, pool.H, pool.d)
-    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q, "q", pool.dtype),
-            _dev(k_new, "k_new", pool.dtype, kv_shape), _dev(v_new, "v_new", pool.dtype, kv_shape),
-            _dev(out, "out", pool.dtype, q.shape))
+    dt = pool.act_dtype
+    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q, "q", dt),
+            _dev(k_new, "k_new", dt, kv_shape), _dev(v_new, "v_new", dt, kv_shape),
+            _dev(out, "out", dt, q.shape))
     qh, qi = None, None
     if qpool is not None:
         qh = qpool.handle

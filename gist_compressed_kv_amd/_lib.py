@@ -19,6 +19,7 @@ GIST_ERR_HIP = -4
 
 GIST_F32 = 0
 GIST_BF16 = 1
+GIST_FP8_E4M3 = 2
 
 STATUS_NAMES = {
     GIST_OK: "GIST_OK",

@@ -59,6 +59,19 @@ __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
                     pack2_bf16(f[6], f[7]));
 }
 
+// Four OCP FP8 E4M3 codes (one dword, lowest byte first) to floats.  gfx950's
+// v_cvt_pk_f32_fp8 decodes exactly this format (bias 7, subnormals, 0x7F and
+// 0xFF NaN).
+__device__ __forceinline__ void decode4_e4m3(uint32_t w, float* f) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo.x;
+  f[1] = lo.y;
+  f[2] = hi.x;
+  f[3] = hi.y;
+}
+
 // ---------------------------------------------------------------------------
 // RoPE angles.  The host computes theta_i / (2*pi) = base^(-2i/d) / (2*pi)
 // (revolutions per position) in double.  The device forms pos * rev in double,
@@ -126,7 +139,16 @@ struct gist_pool {
 };
 
 namespace gist {
-inline size_t elem_size(gist_dtype t) { return t == GIST_BF16 ? 2 : 4; }
+inline size_t elem_size(gist_dtype t) { return t == GIST_F32 ? 4 : (t == GIST_BF16 ? 2 : 1); }
 // elements of one (layer, item) record: [2][H][k][d]
 inline int64_t record_elems(const gist_pool* p) { return 2LL * p->H * p->k * p->d; }
+// fp8 pools: byte offset of the scale array [L][N][2][H] behind the codes
+inline int64_t fp8_scales_offset(const gist_pool* p) {
+  return (int64_t)p->L * p->N * record_elems(p);
+}
+// fp8 pools: the scales of one layer, [N][2][H]
+inline const float* fp8_layer_scales(const gist_pool* p, int layer) {
+  return (const float*)((const char*)p->storage + fp8_scales_offset(p)) +
+         (int64_t)layer * p->N * 2 * p->H;
+}
 }  // namespace gist

@@ -29,6 +29,7 @@
 //    16-lane row with DPP.  This is the ell = 1 path (EOS over item gist +
 //    query gist + itself) and the fp32 path.
 #include <cfloat>
+#include <type_traits>
 #include <utility>
 
 #include "common.hpp"
@@ -44,6 +45,10 @@ struct FwdArgs {
   int64_t qpool_layer_off;
   int64_t qN;
   int kq;  // 0 when there is no query gist
+  // fp8 pools: this layer's scales [N][2][H] (and [qN][2][H]); pool offsets
+  // are then in bytes
+  const float* pool_scales;
+  const float* qpool_scales;
   const int32_t* item_ids;
   const int32_t* q_ids;
   const void* q;
@@ -574,7 +579,10 @@ __device__ __forceinline__ constexpr int eos_off(int R, int ch, int D) {
 //   the query.  Rotated Q and K_new are rounded to bf16 for the MFMAs, and
 //   the softmax scale is applied to the fp32 logits in the exponent.
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
-template <int D, int NGT>
+// FP8: the gist pools hold E4M3 codes; each gist row is decoded, multiplied
+// by its (item or query, K or V, head) scale and rounded to bf16 as it is
+// loaded, so everything after the loads is the bf16 kernel.
+template <int D, int NGT, bool FP8>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 gist_fwd_eos(const FwdArgs a) {
   constexpr int NS = D / 32;
@@ -615,29 +623,48 @@ gist_fwd_eos(const FwdArgs a) {
     for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<bf16_t>();
     return;
   }
-  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-                     (int64_t)g * a.k * D;
-  const bf16_t* qK = gK;
+  typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
+  const C* gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+                (int64_t)g * a.k * D;
+  const C* qK = gK;
   if (a.kq)
-    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+    qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
          (int64_t)g * a.kq * D;
   const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
   const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
   // gist key j (< kg): K row, and its V row at +H*k*D (item) or +H*k'*D (query)
-  auto gist_row = [&](int j, bool v) -> const bf16_t* {
+  auto gist_row = [&](int j, bool v) -> const C* {
     if (j < a.k) return gK + (int64_t)((v ? a.H * a.k : 0) + j) * D;
     return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
   };
+  // fp8: scales of the item and query gist (K, V); wave-uniform scalars
+  float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
+  if constexpr (FP8) {
+    const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+    ski = si[g];
+    svi = si[a.H + g];
+    if (a.kq) {
+      const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+      skq = sq[g];
+      svq = sq[a.H + g];
+    }
+  }
 
   // ---- loads, all unconditional (clamped rows) -----------------------------
   // K: MFMA A layout straight from HBM (lane n = key, 8 channels of step s)
   u32x4_t kr[NGT][NS];
+  uint2 kr8[NGT][NS];
 #pragma unroll
   for (int kt = 0; kt < NGT; ++kt) {
     const int j = 16 * kt + n;
-    const bf16_t* row = gist_row(j < kg ? j : 0, false);
+    const C* row = gist_row(j < kg ? j : 0, false);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kr[kt][s] = *(const u32x4_t*)(row + 32 * s + 8 * q4);
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (FP8)
+        kr8[kt][s] = *(const uint2*)(row + 32 * s + 8 * q4);
+      else
+        kr[kt][s] = *(const u32x4_t*)(row + 32 * s + 8 * q4);
+    }
   }
   u32x4_t qraw[NS];
   const int hcol = n < G ? n : G - 1;
@@ -647,14 +674,28 @@ gist_fwd_eos(const FwdArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   // V rows of the gist tiles, V_new and K_new as whole rows, coalesced (lane
   // covers chunk u % CPR of row u / CPR); issued last, so the logits of the
-  // gist tiles only wait for K and Q
+  // gist tiles only wait for K and Q.  The gist rows fill exactly the first
+  // RITG iterations (16 rows of CPR chunks each are a multiple of 64 units)
+  // and the two rows of the token itself the last one.
+  constexpr int RITG = 16 * NGT * CPR / 64;
+  static_assert(RITG + 1 == RIT, "gist rows fill whole staging iterations");
   u32x4_t rraw[RIT];
+  uint2 rraw8[RITG];
 #pragma unroll
   for (int it = 0; it < RIT; ++it) {
     const int u = lane + 64 * it;
     const int r = u / CPR, c = u - (u / CPR) * CPR;
-    const bf16_t* src = r < VSELF ? gist_row(r < kg ? r : 0, true) : (r == VSELF ? vnew : knew);
-    rraw[it] = *(const u32x4_t*)(src + 8 * c);
+    if constexpr (FP8) {
+      if (it < RITG) {
+        rraw8[it] = *(const uint2*)(gist_row(r < kg ? r : 0, true) + 8 * c);
+      } else {
+        const bf16_t* src = r == VSELF ? vnew : knew;  // rows past KSELF read K_new
+        rraw[it] = *(const u32x4_t*)(src + 8 * c);
+      }
+    } else {
+      const bf16_t* src = r < VSELF ? gist_row(r < kg ? r : 0, true) : (r == VSELF ? vnew : knew);
+      rraw[it] = *(const u32x4_t*)(src + 8 * c);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -687,6 +728,24 @@ gist_fwd_eos(const FwdArgs a) {
     qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
   }
 
+  if constexpr (FP8) {
+    // K codes -> value * scale (item rows j < k, query rows after) -> bf16
+#pragma unroll
+    for (int kt = 0; kt < NGT; ++kt) {
+      const float sk = 16 * kt + n < a.k ? ski : skq;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        float f[8];
+        decode4_e4m3(kr8[kt][s].x, f);
+        decode4_e4m3(kr8[kt][s].y, f + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] *= sk;
+        const uint4 b = pack8_bf16(f);
+        kr[kt][s] = u32x4_t{b.x, b.y, b.z, b.w};
+      }
+    }
+  }
+
   // ---- logits Sᵀ[key][head] of the gist tiles (unscaled: scale*log2 e is
   // applied in the exponent, so Q is rounded to bf16 as the rotated Q) ------
   f32x4_t sacc[NT];
@@ -714,10 +773,23 @@ gist_fwd_eos(const FwdArgs a) {
     const int u = lane + 64 * it;
     const int r = u / CPR, c = u - (u / CPR) * CPR;
     if (r < ROWS) {
+      u32x4_t w = rraw[it];
+      if constexpr (FP8) {
+        if (it < RITG) {
+          float f[8];
+          decode4_e4m3(rraw8[it].x, f);
+          decode4_e4m3(rraw8[it].y, f + 4);
+          const float sv = r < a.k ? svi : svq;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] *= sv;
+          const uint4 b = pack8_bf16(f);
+          w = u32x4_t{b.x, b.y, b.z, b.w};
+        }
+      }
       // rows are 8-byte aligned: two 8-byte stores
       uint2* dst = (uint2*)(Rl + eos_off(r, 8 * c, D));
-      dst[0] = make_uint2(rraw[it].x, rraw[it].y);
-      dst[1] = make_uint2(rraw[it].z, rraw[it].w);
+      dst[0] = make_uint2(w.x, w.y);
+      dst[1] = make_uint2(w.z, w.w);
     }
   }
 
@@ -1078,6 +1150,10 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
                   "gist_attn_forward: qpool must match pool in L, H, d and dtype");
     if (!q_ids) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward: q_ids is NULL");
   }
+  const bool fp8 = pool->dtype == GIST_FP8_E4M3;
+  if (fp8 && !(ell == 1 && Hq / H <= 16 && pool->k + (qpool ? qpool->k : 0) <= 32))
+    return fail(GIST_ERR_UNSUPPORTED,
+                "gist_attn_forward: fp8 pools support ell == 1, Hq/H <= 16 and k + k' <= 32 only");
   if (P == 0) return GIST_OK;
   if (!item_ids || !q || !k_new || !v_new || !out)
     return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward: NULL tensor argument");
@@ -1095,6 +1171,8 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
   a.qpool_layer_off = qpool ? (int64_t)layer * qpool->N * record_elems(qpool) : 0;
   a.qN = qpool ? qpool->N : 0;
   a.kq = qpool ? qpool->k : 0;
+  a.pool_scales = fp8 ? fp8_layer_scales(pool, layer) : nullptr;
+  a.qpool_scales = fp8 && qpool ? fp8_layer_scales(qpool, layer) : nullptr;
   a.item_ids = item_ids;
   a.q_ids = qpool ? q_ids : nullptr;
   a.q = q;
@@ -1154,14 +1232,23 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
     }
     return check_launch("gist_attn_forward(mfma)");
   }
-  if (pool->dtype == GIST_BF16 && ell == 1 && a.G <= 16 && kg <= 32) {
+  if ((pool->dtype == GIST_BF16 || fp8) && ell == 1 && a.G <= 16 && kg <= 32) {
     const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
+    auto go = [&](auto d_c, auto ngt_c) {
+      constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
+      if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false>), grid, dim3(256), 0, s, a);
+    };
+    using I64 = std::integral_constant<int, 64>;
+    using I128 = std::integral_constant<int, 128>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     if (d == 64) {
-      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<64, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<64, 2>), grid, dim3(256), 0, s, a);
+      if (kg <= 16) go(I64{}, I1{});
+      else go(I64{}, I2{});
     } else {
-      if (kg <= 16) hipLaunchKernelGGL((gist_fwd_eos<128, 1>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<128, 2>), grid, dim3(256), 0, s, a);
+      if (kg <= 16) go(I128{}, I1{});
+      else go(I128{}, I2{});
     }
     return check_launch("gist_attn_forward(eos)");
   }

@@ -64,6 +64,28 @@ def randn_fp8_blocks(shape, seed: int, device):
     return codes, scales
 
 
+def randn_fp8_gist_pool(L: int, N: int, k: int, H: int, d: int, seed: int, device) -> torch.Tensor:
+    """Flat storage of a synthetic fp8 gist pool: the codes [L][N][2][H][k][d]
+    of N(0,1) values (as ``randn``) followed by their fp32 scales [L][N][2][H],
+    one per (layer, item, K or V, head) block, scale = amax / 448, quantized
+    by torch's own E4M3 conversion."""
+    ncode = L * N * 2 * H * k * d
+    storage = torch.empty(ncode + L * N * 2 * H * 4, dtype=torch.uint8, device=device)
+    codes = storage[:ncode].view(L, N, 2, H, k, d)
+    scales = storage[ncode:].view(torch.float32).view(L, N, 2, H)
+    g = generator(seed, device)
+    step = max(1, (1 << 27) // (2 * H * k * d))
+    for li in range(L):
+        for i0 in range(0, N, step):
+            i1 = min(N, i0 + step)
+            x = torch.randn((i1 - i0, 2, H, k, d), generator=g, device=device, dtype=torch.float32)
+            amax = x.abs().amax(dim=(3, 4))
+            sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+            codes[li, i0:i1] = (x / sc[..., None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+            scales[li, i0:i1] = sc
+    return storage
+
+
 def item_ids_per_query(n_queries: int, n_candidates: int, n_items: int, seed: int,
                        device) -> torch.Tensor:
     """Candidate ids, query-major: each query draws n_candidates distinct items
@@ -101,6 +123,7 @@ class GistWorkload:
     dtype: torch.dtype
     seed: int
     kq: int = 0  # query-gist positions (0 = no query gist)
+    fp8: bool = False  # gist pools in fp8 E4M3 (activations stay in dtype)
 
     @property
     def pos0(self) -> int:
@@ -141,6 +164,11 @@ WIDE_EOS = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query gis
 PAGED = DecodeWorkload("paged decode: 32 requests x 4096 cached tokens in 256-token blocks, "
                        "Hq=H=32, d=128, 32 layers, bf16", 32, 32, 4096, 256, 32, 32, 128,
                        torch.bfloat16, 5)
+
+WIDE_EOS_FP8 = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query gist k'=8 + EOS "
+                            "(ell=1), 2000 pairs, fp8 E4M3 gist pools with per-(item, K/V, head) "
+                            "scales, bf16 activations", 28, 100_000, 8, 1, 64, 8, 128, 2000, 40,
+                            torch.bfloat16, 7, kq=8, fp8=True)
 
 PAGED_FP8 = DecodeWorkload("paged decode, fp8 E4M3 cache with per-(block, head) scales: 32 requests "
                            "x 4096 cached tokens in 256-token blocks, Hq=H=32, d=128, 32 layers, "

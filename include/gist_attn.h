@@ -48,7 +48,16 @@ typedef enum {
   GIST_ERR_HIP = -4           /* the HIP runtime reported an error */
 } gist_status;
 
-typedef enum { GIST_F32 = 0, GIST_BF16 = 1 } gist_dtype;
+/*
+ * Element types.  GIST_FP8_E4M3 is a pool-only storage type: OCP FP8 E4M3
+ * codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; largest
+ * finite value 448; codes 0x7F and 0xFF are NaN) with one fp32 scale per
+ * (layer, item, K or V, KV head).  The pages name KV quantization as a lever
+ * without fixing a scheme ([GIST] 收益有多大：存储; [KVC] Memory: the
+ * per-element byte count b = 1); the activations of calls on such a pool
+ * are bf16.
+ */
+typedef enum { GIST_F32 = 0, GIST_BF16 = 1, GIST_FP8_E4M3 = 2 } gist_dtype;
 
 /* Opaque handle describing a caller-owned gist pool (host metadata only). */
 typedef struct gist_pool gist_pool;
@@ -56,8 +65,9 @@ typedef struct gist_pool gist_pool;
 /*
  * gist_pool_bytes — bytes of a pool holding N items, each with k gist
  * positions in each of L layers: N * 2*L*k*H*d * sizeof(dtype), the per-item
- * size 2·L·k·H·h·b of [GIST] 在线的一次 attention / 收益有多大：存储.
- * Returns 0 for invalid shapes.
+ * size 2·L·k·H·h·b of [GIST] 在线的一次 attention / 收益有多大：存储.  For
+ * GIST_FP8_E4M3: N * L * (2*k*H*d + 2*H*4) (one byte per element plus the
+ * fp32 scales).  Returns 0 for invalid shapes.
  */
 size_t gist_pool_bytes(int L, int64_t N, int k, int H, int d, gist_dtype dtype);
 
@@ -72,6 +82,12 @@ size_t gist_pool_bytes(int L, int64_t N, int k, int H, int d, gist_dtype dtype);
  *   gist, as in training).  The handle is immutable and may be shared by
  *   concurrent streams.  Requires d in {64, 128}, 1 <= k <= 64, H >= 1.
  *   Writes the new handle to *out (host memory, freed by gist_pool_destroy).
+ */
+/*
+ * GIST_FP8_E4M3 storage: the codes [L][N][2][H][k][d] (uint8, same order as
+ * above) followed by the scales [L][N][2][H] (fp32; index 0 of the "2" axis
+ * scales K, index 1 scales V).  Element value = decode(code) * scale of its
+ * (layer, item, K/V, head).
  */
 gist_status gist_pool_create(gist_pool** out, int L, int64_t N, int k, int H, int d,
                              gist_dtype dtype, void* storage, size_t storage_bytes);
@@ -90,6 +106,11 @@ gist_status gist_pool_destroy(gist_pool* pool);
  *   v_src    device [n][k][H][d], pool dtype, copied unchanged.
  *   rope_base RoPE base used for the re-rotation.
  * Duplicate ids in one call race (one of the writes wins).  n == 0 is a no-op.
+ * GIST_FP8_E4M3 pools take bf16 k_src/v_src and quantize each (item, K or V,
+ * head) block of k*d values x (K after the re-rotation, in fp32): amax =
+ * max |x|, scale = amax / 448 in fp32 (1 when amax is 0), code = x / scale
+ * (fp32 quotient) rounded to the nearest E4M3 value, ties to even mantissa,
+ * clamped to +-448.  Inputs must be finite.
  */
 gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids, int64_t n,
                             const void* k_src, const void* v_src, int src_pos0,
@@ -118,7 +139,12 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  *   out       device [P][ell][Hq][d], pool dtype; must not alias the inputs
  * Limits: 1 <= ell <= 1024, Hq % H == 0, Hq / H <= 32.  P == 0 is a no-op.
  * bf16 with 2 <= ell <= 64 and k + k' + ell <= 128 runs the MFMA kernel;
- * every other case runs the VALU kernel.
+ * bf16 with ell == 1, Hq / H <= 16 and k + k' <= 32 the EOS kernel; every
+ * other case runs the VALU kernel.
+ * GIST_FP8_E4M3 pools: q, k_new, v_new and out are bf16, qpool must be fp8
+ * too, and only the EOS kernel's shapes (ell == 1, Hq / H <= 16,
+ * k + k' <= 32) are implemented; other shapes return GIST_ERR_UNSUPPORTED.
+ * The gist rows are decoded, scaled and rounded to bf16 as they are loaded.
  */
 gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                               int ell, int Hq, const void* q, const void* k_new,

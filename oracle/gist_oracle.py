@@ -39,6 +39,10 @@ library makes identically):
   rotated Q and the rotated new K are rounded to bf16, as an unfused
   RoPE-then-attention pipeline stores them; the stored gist K and every V
   are bf16 inputs already.
+* fp8 storage (the pages name KV quantization as a lever but fix no scheme):
+  OCP FP8 E4M3 codes with one fp32 scale per block (a paged-cache (block,
+  head); a gist pool's (item, K or V, head)), scale = amax / 448, codes the
+  nearest E4M3 value of x / scale, ties to even, decided in fp32.
 """
 
 from __future__ import annotations
@@ -248,6 +252,62 @@ def dequantize_blocks(codes, scales) -> np.ndarray:
     """Paged cache of E4M3 codes [n_blocks][H][block][d] with one scale per
     (block, head) [n_blocks][H]: element = decode(code) * scale."""
     return decode_e4m3(codes) * np.asarray(scales, np.float64)[:, :, None, None]
+
+
+def encode_e4m3(y) -> np.ndarray:
+    """E4M3 code of the finite value nearest to y.  A tie goes to the code with
+    the even mantissa (round to nearest even), |y| is clamped to 448 first and
+    the sign bit is kept (a negative y that rounds to zero gives 0x80, -0).
+
+    Written as a nearest-neighbour search over the 127 non-negative finite
+    values (codes 0x00..0x7E, increasing in value), so every step can be
+    checked against the format's definition in decode_e4m3."""
+    y = np.asarray(y, np.float64)
+    table = decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    a = np.minimum(np.abs(y), 448.0)
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - table[lo], table[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_e4m3_block(x):
+    """One block of values quantized the way the fp8 pool writer does it, in
+    fp32 (the precision in which the codes are decided): amax = max |x|,
+    scale = amax / 448 (1 for an all-zero block), codes = nearest E4M3 value
+    of the fp32 quotient x / scale.  Returns (codes uint8, scale float32)."""
+    x32 = np.asarray(x, np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    scale = np.float32(amax / np.float32(448)) if amax > 0 else np.float32(1)
+    return encode_e4m3((x32 / scale).astype(np.float64)), scale
+
+
+def pool_write_fp8(codes: np.ndarray, scales: np.ndarray, layer: int, ids, k_src: np.ndarray,
+                   v_src: np.ndarray, src_pos0: int, base: float):
+    """pool_write into an fp8 pool: codes [L][N][2][H][k][d], scales
+    [L][N][2][H] (returns updated copies).  K is re-rotated as in pool_write
+    (here in fp64, then taken to fp32) and every (item, K or V, head) block of
+    k*d values is quantized by quantize_e4m3_block."""
+    codes = np.array(codes, dtype=np.uint8, copy=True)
+    scales = np.array(scales, dtype=np.float32, copy=True)
+    k_src = np.asarray(k_src, np.float64)
+    v_src = np.asarray(v_src, np.float64)
+    n, k, h_kv, d = k_src.shape
+    shift = np.full(k, 1 - src_pos0, dtype=np.float64)
+    for i in range(n):
+        for g in range(h_kv):
+            for kv, x in ((0, rope(k_src[i, :, g, :], shift, base)), (1, v_src[i, :, g, :])):
+                c, sc = quantize_e4m3_block(x)
+                codes[layer, int(ids[i]), kv, g] = c
+                scales[layer, int(ids[i]), kv, g] = sc
+    return codes, scales
+
+
+def dequantize_gist(codes, scales) -> np.ndarray:
+    """fp8 gist records [...][2][H][k][d] with scales [...][2][H]: element =
+    decode(code) * scale of its (item, K or V, head)."""
+    return decode_e4m3(codes) * np.asarray(scales, np.float64)[..., None, None]
 
 
 def gather_logical(cache: np.ndarray, block_row, n_tokens: int, g: int) -> np.ndarray:

@@ -31,18 +31,30 @@ class GistCase:
     """One layer-set of gist attention inputs on the GPU."""
 
     def __init__(self, layers, n_items, k, ell, hq, h, d, pairs, dtype, seed, kq=0,
-                 n_qrows=0, ids=None, q_ids=None, device="cuda"):
+                 n_qrows=0, ids=None, q_ids=None, device="cuda", fp8=False):
         self.layers, self.n_items, self.k, self.ell = layers, n_items, k, ell
         self.hq, self.h, self.d, self.pairs, self.dtype, self.kq = hq, h, d, pairs, dtype, kq
-        self.pool_t = synth.randn((layers, n_items, 2, h, k, d), synth.tensor_seed(seed, 1),
-                                  dtype, device)
-        self.pool = G.GistPool(self.pool_t)
+        self.fp8 = fp8
+        if fp8:  # E4M3 gist pools; activations in bf16
+            self.dtype = dtype = torch.bfloat16
+            self.pool_t = synth.randn_fp8_gist_pool(layers, n_items, k, h, d,
+                                                    synth.tensor_seed(seed, 1), device)
+            self.pool = G.GistPool(self.pool_t, shape=(layers, n_items, k, h, d))
+        else:
+            self.pool_t = synth.randn((layers, n_items, 2, h, k, d), synth.tensor_seed(seed, 1),
+                                      dtype, device)
+            self.pool = G.GistPool(self.pool_t)
         if ids is None:
             ids = torch.randint(0, n_items, (pairs,), generator=synth.generator(seed, "cpu"),
                                 dtype=torch.int32)
         self.ids = ids.to(device=device, dtype=torch.int32)
         self.qpool_t = self.qpool = self.q_ids = None
-        if kq:
+        if kq and fp8:
+            self.qpool_t = synth.randn_fp8_gist_pool(layers, n_qrows, kq, h, d,
+                                                     synth.tensor_seed(seed, 2), device)
+            self.qpool = G.GistPool(self.qpool_t, shape=(layers, n_qrows, kq, h, d))
+            self.q_ids = q_ids.to(device=device, dtype=torch.int32)
+        elif kq:
             self.qpool_t = synth.randn((layers, n_qrows, 2, h, kq, d), synth.tensor_seed(seed, 2),
                                        dtype, device)
             self.qpool = G.GistPool(self.qpool_t)
@@ -66,16 +78,25 @@ class GistCase:
         sample = np.asarray(sample)
         idx = torch.as_tensor(sample, device=self.ids.device)
         ids = self.ids[idx].long()
-        pool = f64(self.pool_t[layer][ids])[None]  # [1][S][2][H][k][d]
+        pool = self._rows(self.pool, layer, ids)  # [1][S][2][H][k][d]
         qpool = qids = None
         if self.qpool is not None:
             qr = self.q_ids[idx].long()
-            qpool = f64(self.qpool_t[layer][qr])[None]
+            qpool = self._rows(self.qpool, layer, qr)
             qids = np.arange(len(sample))
         return O.gist_attn_forward(pool, 0, np.arange(len(sample)), f64(self.q[layer][idx]),
                                    f64(self.kn[layer][idx]), f64(self.vn[layer][idx]),
                                    self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids,
                                    round_rotated=rounded)
+
+    @staticmethod
+    def _rows(pool, layer, rows):
+        """Pool records of the given rows of one layer, as fp64 values
+        [1][S][2][H][k][d] (fp8 pools: decoded and scaled by the oracle)."""
+        if pool.fp8:
+            return O.dequantize_gist(pool.codes[layer][rows].cpu().numpy(),
+                                     pool.scales[layer][rows].cpu().numpy())[None]
+        return f64(pool.storage[layer][rows])[None]
 
     def max_err(self, layer, out, sample, rounded=False):
         ref = self.oracle(layer, sample, rounded)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gist_attn.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "byte_counts.json")
 
-BF16, F32 = _lib.GIST_BF16, _lib.GIST_F32
+BF16, F32, FP8 = _lib.GIST_BF16, _lib.GIST_F32, _lib.GIST_FP8_E4M3
 FAKE = ctypes.c_void_p(1 << 20)  # an aligned address that is never dereferenced
 
 
@@ -162,6 +162,7 @@ def test_paged_decode_validation(L):
     assert _dec(L, nblk=0) == _lib.GIST_ERR_INVALID_ARG
     assert _dec(L, max_blk=0) == _lib.GIST_ERR_INVALID_ARG
     assert _dec(L, dt=3) == _lib.GIST_ERR_INVALID_ARG
+    assert _dec(L, dt=FP8) == _lib.GIST_ERR_INVALID_ARG  # fp8 caches have their own entry point
     assert _dec(L, scale=-1.0) == _lib.GIST_ERR_INVALID_ARG
     assert _dec(L, ptr=None) == _lib.GIST_ERR_INVALID_ARG
     assert _dec(L, ws_bytes=16) == _lib.GIST_ERR_INVALID_ARG
@@ -188,3 +189,34 @@ def test_paged_decode_fp8_validation(L):
     assert "4-byte aligned" in L.gist_last_error().decode()
     assert _dec8(L, ws_bytes=16) == _lib.GIST_ERR_INVALID_ARG
     assert _dec8(L, R=0, ptr=None, sptr=None) == _lib.GIST_OK
+
+
+def test_fp8_pool_bytes_and_create(L):
+    # codes (one byte per element) plus one fp32 scale per (layer, item, K/V, head)
+    assert L.gist_pool_bytes(28, 1, 8, 8, 128, FP8) == 28 * (2 * 8 * 8 * 128 + 2 * 8 * 4)
+    assert L.gist_pool_bytes(2, 10, 8, 2, 64, FP8) == 2 * 10 * (2 * 8 * 2 * 64 + 16)
+    nbytes = L.gist_pool_bytes(2, 10, 8, 2, 64, FP8)
+    st, h = _create(L, 2, 10, 8, 2, 64, FP8, FAKE, nbytes)
+    assert st == _lib.GIST_OK and h.value
+    L.gist_pool_destroy(h)
+    st, h = _create(L, 2, 10, 8, 2, 64, FP8, FAKE, nbytes + 1)
+    assert st == _lib.GIST_ERR_INVALID_ARG and "storage_bytes" in L.gist_last_error().decode()
+
+
+def test_fp8_pool_forward_limits(L):
+    pool = _pool(L, dt=FP8)
+    qp8 = _pool(L, k=8, dt=FP8)
+    qbf = _pool(L, k=8, dt=BF16)
+    big = _pool(L, k=30, dt=FP8)  # k + k' = 38 > 32
+    try:
+        # only the ell = 1 (EOS) shapes are implemented for fp8 pools
+        assert _fwd(L, pool, ell=16) == _lib.GIST_ERR_UNSUPPORTED
+        assert "fp8" in L.gist_last_error().decode()
+        assert _fwd(L, pool, ell=1, Hq=34) == _lib.GIST_ERR_UNSUPPORTED
+        assert _fwd(L, pool, ell=1, qpool=big, qids=FAKE) == _lib.GIST_ERR_UNSUPPORTED
+        # the query-gist pool must be fp8 too
+        assert _fwd(L, pool, ell=1, qpool=qbf, qids=FAKE) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ell=1, P=0, qpool=qp8, qids=FAKE, ptr=None, ids=None) == _lib.GIST_OK
+    finally:
+        for h in (pool, qp8, qbf, big):
+            L.gist_pool_destroy(h)

@@ -392,3 +392,107 @@ def test_paged_decode_fp8_bad_block_is_nan():
     err = float(np.abs(f64(out[0:1]) - case.oracle([0])).max())
     assert err <= TOL[torch.bfloat16]
 
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) gist pools: the EOS kernel decodes each gist row, scales it by
+# its (item or query, K or V, head) scale and rounds it to bf16 on load.  The
+# oracle decodes the same codes exactly (fp64), so the comparison is the bf16
+# one; quantization error is not part of it.
+# ---------------------------------------------------------------------------
+
+EOS_FP8_SHAPES = [
+    # k, kq, hq, h, d, pairs
+    (8, 8, 64, 8, 128, 40),
+    (8, 0, 14, 2, 64, 30),
+    (12, 12, 16, 2, 128, 9),
+    (20, 0, 8, 1, 64, 7),
+    (3, 0, 3, 1, 128, 5),
+    (16, 16, 32, 2, 64, 11),
+    (1, 0, 1, 1, 64, 3),
+]
+
+
+@pytest.mark.parametrize("shape", EOS_FP8_SHAPES,
+                         ids=lambda s: "k%d_kq%d_hq%d_h%d_d%d_p%d" % s)
+def test_eos_fp8_pool_shapes(shape):
+    k, kq, hq, h, d, P = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(2, 7, k, 1, hq, h, d, P, torch.bfloat16, 600 + k + kq + hq, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    check_gist(case, label=f"eos fp8 {shape}")
+
+
+def test_wide_eos_fp8_workload_sampled():
+    wl = synth.WIDE_EOS_FP8
+    qids = torch.arange(wl.pairs) // (wl.pairs // wl.queries)
+    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids, fp8=True)
+    rng = np.random.default_rng(8)
+    sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 62)]))
+    check_gist(case, sample=sample, label="wide EOS, fp8 item+query gist, 2000 pairs")
+
+
+def test_eos_fp8_out_of_range_ids_give_nan_rows_only():
+    case = GistCase(1, 6, 8, 1, 64, 8, 128, 5, torch.bfloat16, 610, kq=8, n_qrows=2,
+                    ids=torch.tensor([0, 6, 2, 5, -3]), q_ids=torch.tensor([0, 1, 2, 1, 0]),
+                    fp8=True)
+    o = f64(case.run(0))
+    torch.cuda.synchronize()
+    assert np.isnan(o[1]).all() and np.isnan(o[2]).all() and np.isnan(o[4]).all()
+    assert np.isfinite(o[[0, 3]]).all()
+    assert case.max_err(0, case.run(0), [0, 3]) <= 2e-2
+
+
+@pytest.mark.parametrize("src_pos0", [1, 38])
+def test_pool_write_fp8_matches_oracle(src_pos0):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    L, N, k, h, d, n = 2, 9, 8, 2, 128, 4
+    st = G.gist_pool_fp8_storage(L, N, k, h, d)
+    st.zero_()
+    pool = G.GistPool(st, shape=(L, N, k, h, d))
+    ids = torch.tensor([3, 0, 8, 5], dtype=torch.int32, device="cuda")
+    ks = synth.randn((n, k, h, d), 520, torch.bfloat16, "cuda")
+    vs = synth.randn((n, k, h, d), 521, torch.bfloat16, "cuda")
+    ks[1, :, 1] = 0          # an all-zero block: scale 1, codes 0
+    vs[2, :, 0] *= 1e-4      # small values: subnormal codes
+    vs[3, :, 1] *= 300.0     # large values
+    G.gist_pool_write(pool, 1, ids, ks, vs, src_pos0=src_pos0, rope_base=10000.0)
+    torch.cuda.synchronize()
+    rc, rs = O.pool_write_fp8(np.zeros((L, N, 2, h, k, d), np.uint8), np.zeros((L, N, 2, h), np.float32),
+                              1, ids.cpu().numpy(), f64(ks), f64(vs), src_pos0, 10000.0)
+    gc, gs = pool.codes.cpu().numpy(), pool.scales.cpu().numpy()
+    # V blocks and untouched items: bit-exact (the codes are decided in fp32 on both sides)
+    assert np.array_equal(gc[:, :, 1], rc[:, :, 1]) and np.array_equal(gs[:, :, 1], rs[:, :, 1])
+    assert np.array_equal(gc[0], rc[0]) and not gc[1, [1, 2, 4, 6, 7]].any()
+    if src_pos0 == 1:  # no re-rotation: K is bit-exact too
+        assert np.array_equal(gc, rc) and np.array_equal(gs, rs)
+    else:
+        # K is re-rotated in fp32 on the GPU and in fp64 by the oracle: the
+        # scales agree to a few ulps, and a code may differ only by one step,
+        # where the value sits on the midpoint between the two codes
+        kg, kr = gs[1, :, 0], rs[1, :, 0]
+        assert np.allclose(kg, kr, rtol=1e-6, atol=0)
+        a, b = gc[1, :, 0].astype(np.int64), rc[1, :, 0].astype(np.int64)
+        diff = a != b
+        say(f"fp8 pool write, src_pos0={src_pos0}: {int(diff.sum())} of {a.size} K codes differ")
+        assert diff.sum() <= a.size // 1000
+        assert ((a[diff] & 0x80) == (b[diff] & 0x80)).all()
+        assert (np.abs((a[diff] & 0x7F) - (b[diff] & 0x7F)) == 1).all()
+    # the written pool read by the EOS kernel, against the oracle on its decoded contents
+    q = synth.randn((n, 1, 4, d), 522, torch.bfloat16, "cuda")
+    kn = synth.randn((n, 1, h, d), 523, torch.bfloat16, "cuda")
+    vn = synth.randn((n, 1, h, d), 524, torch.bfloat16, "cuda")
+    out = G.gist_attn_forward(pool, 1, ids, q, kn, vn, k + 1, 10000.0, d ** -0.5)
+    torch.cuda.synchronize()
+    deq = O.dequantize_gist(gc, gs)
+    ref = O.gist_attn_forward(deq, 1, ids.cpu().numpy(), f64(q), f64(kn), f64(vn), k + 1, 10000.0,
+                              d ** -0.5)
+    # outputs are convex combinations of V rows: the error is measured in units
+    # of the largest |V| the query head can see (the x300 block makes outputs
+    # of a few hundred, whose bf16 rounding alone is about 1)
+    vmax = np.maximum(np.abs(deq[1, ids.cpu().numpy(), 1]).max(axis=(2, 3)),
+                      np.abs(f64(vn)).max(axis=(1, 3)))                # [n][h]
+    vmax = np.repeat(np.maximum(vmax, 1.0), 4 // h, axis=1)[:, None, :, None]  # per query head
+    assert (np.abs(f64(out) - ref) / vmax).max() <= 2e-2

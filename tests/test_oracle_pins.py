@@ -567,3 +567,97 @@ def test_dequantize_blocks_applies_one_scale_per_block_and_head():
     for b in range(3):
         for h in range(2):
             np.testing.assert_array_equal(d[b, h], O.decode_e4m3(codes[b, h]) * scales[b, h])
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) encoding and the fp8 gist pool writer
+# ---------------------------------------------------------------------------
+
+
+def _torch_e4m3(y):
+    """torch's own fp32 -> float8_e4m3fn conversion (round to nearest even)."""
+    return torch.from_numpy(np.asarray(y, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_encode_e4m3_matches_torch_on_values_ties_and_neighbours():
+    t = O.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    mids = (t[:-1] + t[1:]) / 2  # exact in fp32: one more mantissa bit than E4M3
+    m32 = mids.astype(np.float32)
+    ys = np.concatenate([
+        t, -t, mids, -mids,
+        np.nextafter(m32, np.float32(np.inf)), np.nextafter(m32, np.float32(0)),
+        rng(30).choice([-1.0, 1.0], 50000) * np.exp2(rng(31).uniform(-13, 8.8, 50000)),
+    ]).astype(np.float32)
+    ys = ys[np.abs(ys) <= 448]
+    np.testing.assert_array_equal(O.encode_e4m3(ys.astype(np.float64)), _torch_e4m3(ys))
+
+
+def test_encode_e4m3_is_a_nearest_value_by_brute_force():
+    t = O.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    y = rng(32).uniform(-448, 448, 4000) * np.exp2(rng(33).integers(-14, 1, 4000))
+    got = O.decode_e4m3(O.encode_e4m3(y))
+    best = np.min(np.abs(np.abs(y)[:, None] - t[None, :]), axis=1)
+    assert np.array_equal(np.abs(np.abs(got) - np.abs(y)), best)
+    assert np.array_equal(np.signbit(got), np.signbit(y))
+
+
+def test_encode_e4m3_landmarks_and_clamp():
+    e = O.encode_e4m3
+    assert e([0.0])[0] == 0x00 and e([-0.0])[0] == 0x80 and e([-1e-9])[0] == 0x80
+    assert e([2.0 ** -9])[0] == 0x01 and e([2.0 ** -10])[0] == 0x00  # tie -> even (0)
+    assert e([3 * 2.0 ** -10])[0] == 0x02                             # tie 1.5 -> 2
+    assert e([1.0])[0] == 0x38 and e([1.0625])[0] == 0x38 and e([1.1875])[0] == 0x3A
+    assert e([448.0])[0] == 0x7E and e([-448.0])[0] == 0xFE
+    # beyond the largest finite value: clamped (torch's conversion gives NaN there)
+    assert e([464.0])[0] == 0x7E and e([1e9])[0] == 0x7E and e([-500.0])[0] == 0xFE
+
+
+def test_quantize_block_scale_and_error_bound():
+    x = rng(34).standard_normal((8, 128)) * 3.0
+    codes, scale = O.quantize_e4m3_block(x)
+    x32 = x.astype(np.float32)
+    amax = float(np.max(np.abs(x32)))
+    assert scale.dtype == np.float32 and scale == np.float32(np.float32(amax) / np.float32(448))
+    deq = O.decode_e4m3(codes) * float(scale)
+    # the largest element lands on +-448 * scale
+    i = np.argmax(np.abs(x32))
+    assert abs(O.decode_e4m3(codes.reshape(-1)[i:i + 1])[0]) == 448.0
+    # normal range: half a step of 2^-3 relative; subnormal range: 2^-10 * scale absolute
+    err = np.abs(deq - x32)
+    bound = np.maximum(2.0 ** -4 * np.abs(x32), 2.0 ** -10 * float(scale)) * (1 + 1e-6)
+    assert (err <= bound).all()
+    zc, zs = O.quantize_e4m3_block(np.zeros((4, 64)))
+    assert zs == np.float32(1) and not zc.any()
+
+
+def test_pool_write_fp8_quantizes_each_block_after_rerotation():
+    r = rng(35)
+    n, k, h, d = 3, 8, 2, 64
+    ks = r.standard_normal((n, k, h, d))
+    vs = r.standard_normal((n, k, h, d)) * 0.01
+    codes = np.zeros((2, 5, 2, h, k, d), np.uint8)
+    scales = np.zeros((2, 5, 2, h), np.float32)
+    c2, s2 = O.pool_write_fp8(codes, scales, 1, [4, 0, 2], ks, vs, 11, 1e4)
+    rot = O.pool_write(np.zeros((2, 5, 2, h, k, d)), 1, [4, 0, 2], ks, vs, 11, 1e4)
+    for i, item in enumerate([4, 0, 2]):
+        for g in range(h):
+            for kv in range(2):
+                x = rot[1, item, kv, g]
+                amax = np.max(np.abs(x.astype(np.float32)))
+                assert s2[1, item, kv, g] == np.float32(amax / np.float32(448))
+                deq = O.dequantize_gist(c2[1, item], s2[1, item])[kv, g]
+                assert np.abs(deq - x).max() <= 2.0 ** -4 * amax * (1 + 1e-6)
+    untouched = [1, 3]
+    assert not c2[1, untouched].any() and not s2[1, untouched].any() and not c2[0].any()
+
+
+def test_dequantize_gist_scales_each_k_v_head_block():
+    r = rng(36)
+    codes = r.integers(0, 0x7E, (2, 2, 3, 4, 8)).astype(np.uint8)   # [items][2][H][k][d]
+    scales = r.uniform(0.1, 4.0, (2, 2, 3)).astype(np.float32)
+    d = O.dequantize_gist(codes, scales)
+    for i in range(2):
+        for kv in range(2):
+            for g in range(3):
+                np.testing.assert_array_equal(
+                    d[i, kv, g], O.decode_e4m3(codes[i, kv, g]) * float(scales[i, kv, g]))
