@@ -579,10 +579,13 @@ __device__ __forceinline__ constexpr int eos_off(int R, int ch, int D) {
 //   the query.  Rotated Q and K_new are rounded to bf16 for the MFMAs, and
 //   the softmax scale is applied to the fp32 logits in the exponent.
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
-// FP8: the gist pools hold E4M3 codes; each gist row is decoded, multiplied
-// by its (item or query, K or V, head) scale and rounded to bf16 as it is
-// loaded, so everything after the loads is the bf16 kernel.
-template <int D, int NGT, bool FP8>
+// FP8: the gist pools hold E4M3 codes.  Every E4M3 value is also a bf16
+// value, so the codes are decoded exactly into the bf16 MFMA operands; the K
+// scale of a gist key multiplies its fp32 logit, and the V scale its softmax
+// weight before that weight is rounded for the P·V product (the row sum takes
+// the unscaled weight).
+// QU: Q staging units per lane, G*D/16 units over 64 lanes (1 or 2).
+template <int D, int NGT, bool FP8, int QU>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 gist_fwd_eos(const FwdArgs a) {
   constexpr int NS = D / 32;
@@ -593,12 +596,15 @@ gist_fwd_eos(const FwdArgs a) {
   constexpr int VSELF = 16 * NGT;        // LDS row of V_new
   constexpr int KSELF = 16 * NGT + 1;    // LDS row of K_new
   constexpr int ROWS = 16 * NGT + 2;
-  constexpr int RIT = (ROWS * CPR + 63) / 64;  // row-staging loads per lane
+  constexpr int RITG = 16 * NGT * CPR / 64;  // gist V row chunks per lane
+  static_assert(16 * NGT * CPR % 64 == 0 && 2 * CPR <= 64, "staging layout");
   __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
   __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) at pos0
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+  typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
+  typedef std::conditional_t<FP8, uint2, u32x4_t> CV;   // 8 gist elements
 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -607,36 +613,79 @@ gist_fwd_eos(const FwdArgs a) {
   if (unit >= a.P * a.H) return;
   const int p = unit / a.H, g = unit - (unit / a.H) * a.H;
   const int G = a.G, Hq = a.Hq;
-  const int kg = a.k + a.kq;
+  const int kg = a.k + a.kq;  // >= 1
   const int ngt = (kg + 15) >> 4;
   bf16_t* out = (bf16_t*)a.out;
   const int64_t orow0 = ((int64_t)p * Hq + (int64_t)g * G) * D;
 
-  const int32_t item = a.item_ids[p];
-  int32_t qid = 0;
-  bool bad = item < 0 || item >= a.N;
-  if (a.kq) {
-    qid = a.q_ids[p];
-    bad = bad || qid < 0 || qid >= a.qN;
+  // ---- the token's own rows first: they do not depend on the ids, so their
+  // HBM traffic starts while the ids are in flight ------------------------
+  // Q, coalesced: unit u = lane + 64*i covers head u / (D/16) and its chunk
+  // pair (channels 8c..8c+7 and their RoPE partners D/2 + 8c..), so each
+  // head's row is read whole and once; units past the group read its last
+  // head's first pair
+  constexpr int QCH = D / 16;  // chunk pairs per head
+  const bf16_t* qgrp = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G) * D;
+  u32x4_t qlo[QU], qhi[QU];
+#pragma unroll
+  for (int i = 0; i < QU; ++i) {
+    const int u = lane + 64 * i;
+    const int uc = u < G * QCH ? u : (G - 1) * QCH;
+    const bf16_t* src = qgrp + (uc / QCH) * D + 8 * (uc % QCH);
+    qlo[i] = *(const u32x4_t*)src;
+    qhi[i] = *(const u32x4_t*)(src + D / 2);
   }
+  // V_new and K_new as whole rows: lane l covers chunk l % CPR of row l / CPR
+  // (0 = V_new, 1 = K_new; lanes past the two rows read K_new again)
+  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
+  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
+  const int sr = lane / CPR, sc = lane - (lane / CPR) * CPR;
+  const u32x4_t rself = *(const u32x4_t*)((sr == 0 ? vnew : knew) + 8 * sc);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN); the
+  // two loads are issued before either is waited on -----------------------
+  const int32_t item = a.item_ids[p];
+  const int32_t qid = *(a.kq ? a.q_ids + p : a.item_ids + p);
+  bool bad = item < 0 || item >= a.N;
+  if (a.kq) bad = bad || qid < 0 || qid >= a.qN;
   if (bad) {
     for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<bf16_t>();
     return;
   }
-  typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
   const C* gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
                 (int64_t)g * a.k * D;
   const C* qK = gK;
   if (a.kq)
     qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
          (int64_t)g * a.kq * D;
-  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
-  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
   // gist key j (< kg): K row, and its V row at +H*k*D (item) or +H*k'*D (query)
   auto gist_row = [&](int j, bool v) -> const C* {
     if (j < a.k) return gK + (int64_t)((v ? a.H * a.k : 0) + j) * D;
     return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
   };
+
+  // ---- gist loads, all unconditional (clamped rows) ------------------------
+  // K: MFMA A layout straight from HBM (lane n = key, 8 channels of step s)
+  CV kraw[NGT][NS];
+#pragma unroll
+  for (int kt = 0; kt < NGT; ++kt) {
+    const int j = 16 * kt + n;
+    const C* row = gist_row(j < kg ? j : 0, false);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kraw[kt][s] = *(const CV*)(row + 32 * s + 8 * q4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // V rows, coalesced (lane covers chunk u % CPR of row u / CPR); issued
+  // last, so the logits of the gist tiles only wait for K and Q
+  CV graw[RITG];
+#pragma unroll
+  for (int it = 0; it < RITG; ++it) {
+    const int u = lane + 64 * it;
+    const int r = u / CPR, c = u - (u / CPR) * CPR;
+    graw[it] = *(const CV*)(gist_row(r < kg ? r : 0, true) + 8 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // fp8: scales of the item and query gist (K, V); wave-uniform scalars
   float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
   if constexpr (FP8) {
@@ -649,101 +698,64 @@ gist_fwd_eos(const FwdArgs a) {
       svq = sq[a.H + g];
     }
   }
-
-  // ---- loads, all unconditional (clamped rows) -----------------------------
-  // K: MFMA A layout straight from HBM (lane n = key, 8 channels of step s)
-  u32x4_t kr[NGT][NS];
-  uint2 kr8[NGT][NS];
-#pragma unroll
-  for (int kt = 0; kt < NGT; ++kt) {
-    const int j = 16 * kt + n;
-    const C* row = gist_row(j < kg ? j : 0, false);
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (FP8)
-        kr8[kt][s] = *(const uint2*)(row + 32 * s + 8 * q4);
-      else
-        kr[kt][s] = *(const u32x4_t*)(row + 32 * s + 8 * q4);
-    }
-  }
-  u32x4_t qraw[NS];
-  const int hcol = n < G ? n : G - 1;
-  const bf16_t* qrow = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G + hcol) * D;
-#pragma unroll
-  for (int s = 0; s < NS; ++s) qraw[s] = *(const u32x4_t*)(qrow + 32 * s + 8 * q4);
-  __builtin_amdgcn_sched_barrier(0);
-  // V rows of the gist tiles, V_new and K_new as whole rows, coalesced (lane
-  // covers chunk u % CPR of row u / CPR); issued last, so the logits of the
-  // gist tiles only wait for K and Q.  The gist rows fill exactly the first
-  // RITG iterations (16 rows of CPR chunks each are a multiple of 64 units)
-  // and the two rows of the token itself the last one.
-  constexpr int RITG = 16 * NGT * CPR / 64;
-  static_assert(RITG + 1 == RIT, "gist rows fill whole staging iterations");
-  u32x4_t rraw[RIT];
-  uint2 rraw8[RITG];
-#pragma unroll
-  for (int it = 0; it < RIT; ++it) {
-    const int u = lane + 64 * it;
-    const int r = u / CPR, c = u - (u / CPR) * CPR;
+  // eight gist elements -> eight bf16 (exact for E4M3 codes)
+  auto to_bf16x8 = [](const CV& w) -> u32x4_t {
     if constexpr (FP8) {
-      if (it < RITG) {
-        rraw8[it] = *(const uint2*)(gist_row(r < kg ? r : 0, true) + 8 * c);
-      } else {
-        const bf16_t* src = r == VSELF ? vnew : knew;  // rows past KSELF read K_new
-        rraw[it] = *(const u32x4_t*)(src + 8 * c);
-      }
+      float f[8];
+      decode4_e4m3(w.x, f);
+      decode4_e4m3(w.y, f + 4);
+      const uint4 b = pack8_bf16(f);
+      return u32x4_t{b.x, b.y, b.z, b.w};
     } else {
-      const bf16_t* src = r < VSELF ? gist_row(r < kg ? r : 0, true) : (r == VSELF ? vnew : knew);
-      rraw[it] = *(const u32x4_t*)(src + 8 * c);
+      return w;
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // ---- cos/sin at pos0: lane i < D/2 evaluates
-  // channel pair i; its frequency rev_0 * q^i comes from scalar arguments --
+  // ---- cos/sin at pos0: lane i < D/2 evaluates channel pair i; its
+  // frequency rev_0 * q^i comes from scalar arguments --------------------
   float2* cst = cs_lds[wv];
+  float csc = 1.f, css = 0.f;
   if (lane < D / 2) {
     double rev = a.freqs.rev[0];
 #pragma unroll
     for (int b = 0; b < 6; ++b) rev *= ((lane >> b) & 1) ? a.rev_step[b] : 1.0;
-    float c, sn;
-    rope_cos_sin((double)a.pos0, rev, c, sn);
-    cst[lane] = make_float2(c, sn);
+    rope_cos_sin((double)a.pos0, rev, csc, css);
+    cst[lane] = make_float2(csc, css);
   }
 
-  // ---- rotate Q at pos0 ------------------------------------------------------
-  bf16x8_t qf[NS];
+  // ---- rotate Q at pos0 in the coalesced layout, then turn it into the MFMA
+  // B layout (lane n = query head, 8 channels of step s) through this wave's
+  // row buffer, whose rows are written only after the B fragments are read.
+  // Row h holds head h; chunk c sits at chunk c ^ h, so the eight lanes of a
+  // 16-byte access phase hit distinct banks on both sides.
+  bf16_t* Rl = rows_lds[wv];
+  static_assert(16 * D <= ROWS * (D + 4), "Q staging fits the row buffer");
+  auto qpos = [](int h, int c) { return h * D + (((c ^ h) & (CPR - 1)) << 3); };
 #pragma unroll
-  for (int s = 0; s < NP; ++s) {
+  for (int i = 0; i < QU; ++i) {
+    const int u = lane + 64 * i;
+    const int h = u / QCH, c = u - (u / QCH) * QCH;
     float xl[8], xh[8], yl[8], yh[8];
-    unpack8(make_uint4(qraw[s].x, qraw[s].y, qraw[s].z, qraw[s].w), xl);
-    unpack8(make_uint4(qraw[s + NP].x, qraw[s + NP].y, qraw[s + NP].z, qraw[s + NP].w), xh);
+    unpack8(make_uint4(qlo[i].x, qlo[i].y, qlo[i].z, qlo[i].w), xl);
+    unpack8(make_uint4(qhi[i].x, qhi[i].y, qhi[i].z, qhi[i].w), xh);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 c = cst[32 * s + 8 * q4 + e];
-      yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y));
-      yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y);
+      const float2 cs = cst[8 * c + e];
+      yl[e] = __builtin_fmaf(xl[e], cs.x, -(xh[e] * cs.y));
+      yh[e] = __builtin_fmaf(xh[e], cs.x, xl[e] * cs.y);
     }
-    qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
-    qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
+    if (u < G * QCH) {
+      *(uint4*)(Rl + qpos(h, c)) = pack8_bf16(yl);
+      *(uint4*)(Rl + qpos(h, c + QCH)) = pack8_bf16(yh);
+    }
   }
-
-  if constexpr (FP8) {
-    // K codes -> value * scale (item rows j < k, query rows after) -> bf16
+  bf16x8_t qf[NS];
+  {
+    // columns past the group read its last head (finite, never stored)
+    const int hcol = n < G ? n : G - 1;
 #pragma unroll
-    for (int kt = 0; kt < NGT; ++kt) {
-      const float sk = 16 * kt + n < a.k ? ski : skq;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        float f[8];
-        decode4_e4m3(kr8[kt][s].x, f);
-        decode4_e4m3(kr8[kt][s].y, f + 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] *= sk;
-        const uint4 b = pack8_bf16(f);
-        kr[kt][s] = u32x4_t{b.x, b.y, b.z, b.w};
-      }
-    }
+    for (int s = 0; s < NS; ++s)
+      qf[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
   }
 
   // ---- logits Sᵀ[key][head] of the gist tiles (unscaled: scale*log2 e is
@@ -752,72 +764,61 @@ gist_fwd_eos(const FwdArgs a) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kt = 0; kt < NGT; ++kt) {
-    if (kt < ngt) {
+    if (kt == 0 || kt < ngt) {
       f32x4_t acc;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = (16 * kt + 4 * q4 + r < kg) ? 0.f : -INFINITY;
+      for (int r = 0; r < 4; ++r) acc[r] = (FP8 || 16 * kt + 4 * q4 + r < kg) ? 0.f : -INFINITY;
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[kt][s]), qf[s],
-                                                     acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, to_bf16x8(kraw[kt][s])), qf[s], acc, 0, 0, 0);
+      if constexpr (FP8) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * kt + 4 * q4 + r;
+          acc[r] = row < kg ? acc[r] * (row < a.k ? ski : skq) : -INFINITY;
+        }
+      }
       sacc[kt] = acc;
       mx = vmax3(mx, acc[0], acc[1]);
       mx = vmax3(mx, acc[2], acc[3]);
     }
   }
 
-  // ---- staged rows to LDS ----------------------------------------------------
-  bf16_t* Rl = rows_lds[wv];
+  // ---- rows to LDS: the gist V rows, then V_new and K_new -------------------
+  auto put = [&](int r, int c, const u32x4_t& w) {
+    // rows are 8-byte aligned: two 8-byte stores
+    uint2* dst = (uint2*)(Rl + eos_off(r, 8 * c, D));
+    dst[0] = make_uint2(w.x, w.y);
+    dst[1] = make_uint2(w.z, w.w);
+  };
 #pragma unroll
-  for (int it = 0; it < RIT; ++it) {
+  for (int it = 0; it < RITG; ++it) {
     const int u = lane + 64 * it;
-    const int r = u / CPR, c = u - (u / CPR) * CPR;
-    if (r < ROWS) {
-      u32x4_t w = rraw[it];
-      if constexpr (FP8) {
-        if (it < RITG) {
-          float f[8];
-          decode4_e4m3(rraw8[it].x, f);
-          decode4_e4m3(rraw8[it].y, f + 4);
-          const float sv = r < a.k ? svi : svq;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] *= sv;
-          const uint4 b = pack8_bf16(f);
-          w = u32x4_t{b.x, b.y, b.z, b.w};
-        }
-      }
-      // rows are 8-byte aligned: two 8-byte stores
-      uint2* dst = (uint2*)(Rl + eos_off(r, 8 * c, D));
-      dst[0] = make_uint2(w.x, w.y);
-      dst[1] = make_uint2(w.z, w.w);
-    }
+    put(u / CPR, u - (u / CPR) * CPR, to_bf16x8(graw[it]));
+  }
+  if (sr < 2) put(VSELF + sr, sc, rself);
+  // K_new rotated at pos0 in place: lane i < D/2 turns channel pair
+  // (i, i + D/2) with its own cos/sin and rounds the pair to bf16
+  if (lane < D / 2) {
+    bf16_t* kl = Rl + eos_off(KSELF, lane, D);
+    bf16_t* kh = Rl + eos_off(KSELF, lane + D / 2, D);
+    const float xl = bf16_bits_to_f32(*kl), xh = bf16_bits_to_f32(*kh);
+    const uint32_t pk = pack2_bf16(__builtin_fmaf(xl, csc, -(xh * css)),
+                                   __builtin_fmaf(xh, csc, xl * css));
+    *kl = (bf16_t)(pk & 0xffffu);
+    *kh = (bf16_t)(pk >> 16);
   }
 
   {
-    // self tile: K_new rotated at pos0 (every MFMA row holds it; rows other
-    // than 0 are removed by the bias) against the rotated Q, both rounded to
-    // bf16 like every other key and query
-    u32x4_t kraw[NS];
+    // self tile: the rotated K_new in every MFMA row (rows other than 0 are
+    // removed by the bias) against the rotated Q
+    bf16x8_t kf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const uint2* src = (const uint2*)(Rl + eos_off(KSELF, 32 * s + 8 * q4, D));
       const uint2 lo = src[0], hi = src[1];
-      kraw[s] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-    }
-    bf16x8_t kf[NS];
-#pragma unroll
-    for (int s = 0; s < NP; ++s) {
-      float xl[8], xh[8], yl[8], yh[8];
-      unpack8(make_uint4(kraw[s].x, kraw[s].y, kraw[s].z, kraw[s].w), xl);
-      unpack8(make_uint4(kraw[s + NP].x, kraw[s + NP].y, kraw[s + NP].z, kraw[s + NP].w), xh);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 c = cst[32 * s + 8 * q4 + e];
-        yl[e] = __builtin_fmaf(xl[e], c.x, -(xh[e] * c.y));
-        yh[e] = __builtin_fmaf(xh[e], c.x, xl[e] * c.y);
-      }
-      kf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
-      kf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
+      kf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
     }
     f32x4_t acc;
 #pragma unroll
@@ -834,26 +835,42 @@ gist_fwd_eos(const FwdArgs a) {
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
 
   // ---- P = exp2((s - max) * scale*log2 e); O = P·V and row sums on the
-  // matrix cores; V fragment (d-tile dt, key tile kt) by transpose read: the lane supplying
-  // a piece reads key (lane >> 2) of the tile, channels
+  // matrix cores; V fragment (d-tile dt, key tile kt) by transpose read: the
+  // lane supplying a piece reads key (lane >> 2) of the tile, channels
   // 32*(dt >> 1) + 4*(dt & 1) + 8*(lane & 3) .. +3, so MFMA row r of the tile
   // is channel vt_row(dt, r) and key k of the tile is MFMA column k
+  // The weights are normalized before the P·V product: the row sums come
+  // first (on the matrix cores, against a ones tile), then each lane scales
+  // its four weights by 1/l of its column, so the products land normalized.
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   const float sl2 = a.scale_log2, nmx = -mx * sl2;
-  f32x4_t o[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float w[NT][4];
   f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kt = 0; kt < NT; ++kt) {
-    if (kt < ngt || kt == NGT) {
-      const uint2 pk = make_uint2(
-          pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][0], sl2, nmx)),
-                     __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][1], sl2, nmx))),
-          pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][2], sl2, nmx)),
-                     __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][3], sl2, nmx))));
-      const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
+    if (kt == 0 || kt < ngt || kt == NGT) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        w[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], sl2, nmx));
+      const bf16x4v pf = __builtin_bit_cast(
+          bf16x4v, make_uint2(pack2_bf16(w[kt][0], w[kt][1]), pack2_bf16(w[kt][2], w[kt][3])));
       lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
+    }
+  }
+  const float inv = __builtin_amdgcn_rcpf(lacc[0]);
+  const float invi = FP8 ? inv * svi : inv, invq = FP8 ? inv * svq : inv;
+  f32x4_t o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kt = 0; kt < NT; ++kt) {
+    if (kt == 0 || kt < ngt || kt == NGT) {
+      float wn[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        wn[r] = w[kt][r] * (kt == NGT ? inv : (16 * kt + 4 * q4 + r < a.k ? invi : invq));
+      const bf16x4v pv =
+          __builtin_bit_cast(bf16x4v, make_uint2(pack2_bf16(wn[0], wn[1]), pack2_bf16(wn[2], wn[3])));
       // the self tile has one key: every lane reads the V_new row
       const int R = kt == NGT ? VSELF : 16 * kt + (lane >> 2);
 #pragma unroll
@@ -861,21 +878,20 @@ gist_fwd_eos(const FwdArgs a) {
         const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(Rl + eos_off(R, ch, D)));
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pf, o[dt],
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pv, o[dt],
                                                           0, 0, 0);
       }
     }
   }
   if (n < G) {
-    const float inv = __builtin_amdgcn_rcpf(lacc[0]);
     bf16_t* orow = out + orow0 + (int64_t)n * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       float v[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        v[r] = o[2 * s][r] * inv;
-        v[4 + r] = o[2 * s + 1][r] * inv;
+        v[r] = o[2 * s][r];
+        v[4 + r] = o[2 * s + 1][r];
       }
       *(uint4*)(orow + 32 * s) = pack8_bf16(v);
     }
@@ -1234,10 +1250,14 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
   }
   if ((pool->dtype == GIST_BF16 || fp8) && ell == 1 && a.G <= 16 && kg <= 32) {
     const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
+    // Q staging units per lane: G heads x d/16 chunk pairs over 64 lanes
+    const bool qu2 = a.G * (d / 16) > 64;
     auto go = [&](auto d_c, auto ngt_c) {
       constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
-      if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false>), grid, dim3(256), 0, s, a);
+      if (fp8 && qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
+      else if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
+      else if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
     };
     using I64 = std::integral_constant<int, 64>;
     using I128 = std::integral_constant<int, 128>;

@@ -144,7 +144,9 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  * GIST_FP8_E4M3 pools: q, k_new, v_new and out are bf16, qpool must be fp8
  * too, and only the EOS kernel's shapes (ell == 1, Hq / H <= 16,
  * k + k' <= 32) are implemented; other shapes return GIST_ERR_UNSUPPORTED.
- * The gist rows are decoded, scaled and rounded to bf16 as they are loaded.
+ * Every E4M3 value is a bf16 value, so the codes enter the matrix products
+ * exactly; a key's K scale multiplies its fp32 logit and its V scale its
+ * softmax weight.
  */
 gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                               int ell, int Hq, const void* q, const void* k_new,
