@@ -45,10 +45,6 @@ struct FwdArgs {
   int64_t qpool_layer_off;
   int64_t qN;
   int kq;  // 0 when there is no query gist
-  // fp8 pools: this layer's scales [N][2][H] (and [qN][2][H]); pool offsets
-  // are then in bytes
-  const float* pool_scales;
-  const float* qpool_scales;
   const int32_t* item_ids;
   const int32_t* q_ids;
   const void* q;
@@ -62,6 +58,10 @@ struct FwdArgs {
   // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
   // set bits b of i, for kernels that form a lane's frequency from scalars
   double rev_step[6];
+  // fp8 pools: this layer's scales [N][2][H] (and [qN][2][H]); pool offsets
+  // are then in bytes
+  const float* pool_scales;
+  const float* qpool_scales;
 };
 
 // ---------------------------------------------------------------------------
