@@ -230,6 +230,73 @@ def pool_write(pool: np.ndarray, layer: int, ids, k_src: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Offline gist extraction, one layer ([GIST] "论文做了什么": the item is run
+# with its k gist tokens appended and the gist positions' K/V are kept;
+# "在线的一次 attention": they are stored for the query to meet at distance k)
+# ---------------------------------------------------------------------------
+
+
+def causal_mask(n: int) -> np.ndarray:
+    """Token t sees tokens 0..t."""
+    return np.arange(n)[None, :] <= np.arange(n)[:, None]
+
+
+def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, base: float,
+                      scale: float, round_rotated: bool = False) -> np.ndarray:
+    """Causal self-attention of B packed sequences [item tokens ; gist tokens].
+
+    q [T][Hq][d]; k, v [T][H][d], not rotated.  Sequence b is tokens
+    seq_start[b] .. seq_start[b+1]-1, at positions 1..len.  Query head h reads
+    KV head h // (Hq/H).  Over [item ; gist] alone the gist mask of training
+    is the causal mask: it only removes item keys from tokens after the gist,
+    and none are present.  With round_rotated the rotated Q and K are rounded
+    to bf16 first.  Returns out [T][Hq][d].
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    hq, h_kv = q.shape[1], k.shape[1]
+    group = hq // h_kv
+    out = np.zeros_like(q)
+    starts = np.asarray(seq_start, np.int64)
+    for b in range(len(starts) - 1):
+        s0, s1 = int(starts[b]), int(starts[b + 1])
+        n = s1 - s0
+        if n == 0:
+            continue
+        pos = 1 + np.arange(n)
+        mask = causal_mask(n)
+        for hh in range(hq):
+            g = hh // group
+            qr = rope(q[s0:s1, hh], pos, base)
+            kr = rope(k[s0:s1, g], pos, base)
+            if round_rotated:
+                qr, kr = round_bf16(qr), round_bf16(kr)
+            out[s0:s1, hh] = attention(qr, kr, v[s0:s1, g], mask, scale)
+    return out
+
+
+def gist_rows_from_prefill(k: np.ndarray, v: np.ndarray, seq_start, n_gist: int,
+                           base: float):
+    """The last n_gist tokens of each packed sequence are its gist: their K,
+    rotated at the canonical positions 1..n_gist (the K the prefill rotates at
+    j+1..j+n_gist, turned back by j), and their V.  Returns (gk, gv), each
+    [B][n_gist][H][d], in the row order gist_pool_write takes."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    starts = np.asarray(seq_start, np.int64)
+    B = len(starts) - 1
+    gk = np.zeros((B, n_gist) + k.shape[1:])
+    gv = np.zeros_like(gk)
+    for b in range(B):
+        e = int(starts[b + 1])
+        rows = slice(e - n_gist, e)
+        gk[b] = rope(k[rows].transpose(1, 0, 2), 1 + np.arange(n_gist), base).transpose(1, 0, 2)
+        gv[b] = v[rows]
+    return gk, gv
+
+
+# ---------------------------------------------------------------------------
 # Paged decode ([KVC] "Reusable-state"; [SFX] section 6 problem 4)
 # ---------------------------------------------------------------------------
 

@@ -661,3 +661,129 @@ def test_dequantize_gist_scales_each_k_v_head_block():
             for g in range(3):
                 np.testing.assert_array_equal(
                     d[i, kv, g], O.decode_e4m3(codes[i, kv, g]) * float(scales[i, kv, g]))
+
+
+# ---------------------------------------------------------------------------
+# Offline gist extraction: causal prefill over [item ; gist] and the gist rows
+# ---------------------------------------------------------------------------
+
+
+def _packed(r, lens, hq, h, d):
+    T = sum(lens)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return (r.standard_normal((T, hq, d)), r.standard_normal((T, h, d)),
+            r.standard_normal((T, h, d)), starts)
+
+
+def test_prefill_matches_sdpa_causal_per_sequence():
+    r = rng(40)
+    hq, h, d = 6, 2, 16
+    lens = [9, 1, 17, 4]
+    q, k, v, st = _packed(r, lens, hq, h, d)
+    out = O.prefill_attention(q, k, v, st, 1e4, 0.3)
+    for b, n in enumerate(lens):
+        s = slice(st[b], st[b + 1])
+        pos = 1 + np.arange(n)
+        qr = O.rope(q[s].transpose(1, 0, 2), pos, 1e4)
+        kr = O.rope(k[s].transpose(1, 0, 2), pos, 1e4)
+        ref = F.scaled_dot_product_attention(
+            torch.from_numpy(qr)[None], torch.from_numpy(kr)[None],
+            torch.from_numpy(v[s].transpose(1, 0, 2).copy())[None], is_causal=True, scale=0.3,
+            enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        assert np.allclose(out[s], ref, atol=1e-12)
+
+
+def test_prefill_sequences_are_independent_and_causal():
+    r = rng(41)
+    hq, h, d = 4, 1, 8
+    lens = [7, 12]
+    q, k, v, st = _packed(r, lens, hq, h, d)
+    out = O.prefill_attention(q, k, v, st, 1e4, 0.5)
+    # each sequence alone, numbered from 1
+    for b in range(2):
+        s = slice(st[b], st[b + 1])
+        alone = O.prefill_attention(q[s], k[s], v[s], [0, lens[b]], 1e4, 0.5)
+        assert np.array_equal(out[s], alone)
+    # changing tokens after t leaves rows <= t of the same sequence unchanged
+    t = 4
+    k2, v2, q2 = k.copy(), v.copy(), q.copy()
+    k2[t + 1:7] += 3.0
+    v2[t + 1:7] -= 2.0
+    q2[t + 1:7] *= -1.0
+    out2 = O.prefill_attention(q2, k2, v2, st, 1e4, 0.5)
+    assert np.array_equal(out2[:t + 1], out[:t + 1]) and not np.allclose(out2[t + 1:7], out[t + 1:7])
+    assert np.array_equal(out2[7:], out[7:])
+
+
+def test_gist_rows_equal_the_pool_write_of_the_prefill_keys():
+    r = rng(42)
+    h, d, n_gist = 2, 16, 4
+    lens = [11, 6]
+    _, k, v, st = _packed(r, lens, 2, h, d)
+    gk, gv = O.gist_rows_from_prefill(k, v, st, n_gist, 1e4)
+    for b, n in enumerate(lens):
+        j = n - n_gist
+        rows = slice(st[b] + j, st[b + 1])
+        # the keys as the prefill rotates them: at j+1 .. j+n_gist
+        k_at = O.rope(k[rows].transpose(1, 0, 2), j + 1 + np.arange(n_gist), 1e4).transpose(1, 0, 2)
+        pool = O.pool_write(np.zeros((1, 1, 2, h, n_gist, d)), 0, [0], k_at[None], v[rows][None],
+                            j + 1, 1e4)
+        assert np.allclose(gk[b].transpose(1, 0, 2), pool[0, 0, 0], atol=1e-12)
+        assert np.array_equal(gv[b].transpose(1, 0, 2), pool[0, 0, 1])
+
+
+def test_toy_model_offline_extraction_by_prefill_then_online():
+    """Two random-weight layers: the offline pass runs the prefill over [item ;
+    gist] only and keeps its gist rows; the online pass over the query tokens
+    then reproduces the query rows of the training layout [item ; gist ;
+    query] under the gist mask (computed with torch's SDPA)."""
+    r = rng(43)
+    j, k, ell, dm, hq, h, d = 13, 4, 6, 32, 4, 2, 8
+    n = j + k + ell
+    layers = [dict(wq=r.standard_normal((dm, hq * d)) / math.sqrt(dm),
+                   wk=r.standard_normal((dm, h * d)) / math.sqrt(dm),
+                   wv=r.standard_normal((dm, h * d)) / math.sqrt(dm),
+                   wo=r.standard_normal((hq * d, dm)) / math.sqrt(hq * d)) for _ in range(2)]
+    x0 = r.standard_normal((n, dm))
+    scale = 1 / math.sqrt(d)
+    mlp = lambda x: np.tanh(x)  # noqa: E731
+
+    x = x0.copy()
+    pos = 1 + np.arange(n)
+    mask = torch.from_numpy(training_mask(j, k, ell))
+    for L in layers:
+        qh = (x @ L["wq"]).reshape(n, hq, d).transpose(1, 0, 2)
+        kh = (x @ L["wk"]).reshape(n, h, d).transpose(1, 0, 2)
+        vh = (x @ L["wv"]).reshape(n, h, d).transpose(1, 0, 2)
+        a = F.scaled_dot_product_attention(
+            torch.from_numpy(O.rope(qh, pos, 1e4))[None], torch.from_numpy(O.rope(kh, pos, 1e4))[None],
+            torch.from_numpy(vh)[None], attn_mask=mask[None], scale=scale, enable_gqa=True)[0].numpy()
+        x = x + a.transpose(1, 0, 2).reshape(n, hq * d) @ L["wo"]
+        x = x + mlp(x)
+    train_rows = x[j + k:]
+
+    # offline: prefill over [item ; gist] only, gist rows kept per layer
+    pool = np.zeros((2, 1, 2, h, k, d))
+    xo = x0[:j + k].copy()
+    st = [0, j + k]
+    for li, L in enumerate(layers):
+        qn = (xo @ L["wq"]).reshape(j + k, hq, d)
+        kn = (xo @ L["wk"]).reshape(j + k, h, d)
+        vn = (xo @ L["wv"]).reshape(j + k, h, d)
+        gk, gv = O.gist_rows_from_prefill(kn, vn, st, k, 1e4)
+        pool[li, 0, 0], pool[li, 0, 1] = gk[0].transpose(1, 0, 2), gv[0].transpose(1, 0, 2)
+        a = O.prefill_attention(qn, kn, vn, st, 1e4, scale)
+        xo = xo + a.reshape(j + k, hq * d) @ L["wo"]
+        xo = xo + mlp(xo)
+    assert np.allclose(xo, x[:j + k], atol=1e-10)  # item and gist rows: the prefill is exact
+
+    # online: only the query tokens, the gist injected as KV, pos0 = k+1
+    x = x0[j + k:].copy()
+    for li, L in enumerate(layers):
+        qn = (x @ L["wq"]).reshape(1, ell, hq, d)
+        kn = (x @ L["wk"]).reshape(1, ell, h, d)
+        vn = (x @ L["wv"]).reshape(1, ell, h, d)
+        a = O.gist_attn_forward(pool, li, [0], qn, kn, vn, k + 1, 1e4, scale)[0]
+        x = x + a.reshape(ell, hq * d) @ L["wo"]
+        x = x + mlp(x)
+    assert np.allclose(x, train_rows, atol=1e-10)
