@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
                     choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos",
-                             "wide_eos_fp8", "paged", "paged_fp8", "copy"])
+                             "wide_eos_fp8", "paged", "paged_fp8", "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
@@ -239,6 +239,102 @@ def paged_bench(args, fp8: bool = False):
                      "avg_launch_us": avg_s * 1e6}}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def prefill_flops(lens, hq: int, d: int) -> int:
+    """Algorithmic FLOPs of causal attention over sequences of these lengths:
+    token t of a sequence takes t+1 keys, 2*d FLOPs per key for q·k and 2*d
+    for the weighted V sum, for every query head."""
+    return sum(2 * n * (n + 1) * d for n in lens) * hq
+
+
+def prefill_bench(args):
+    """Offline gist extraction: one step is every layer's causal prefill over
+    a batch of items [item ; gist], with the gist rows stored into that
+    layer's pool."""
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import gist_compressed_kv_amd as G
+    from gist_compressed_kv_amd import synth
+
+    wl = synth.PREFILL
+    dev = "cuda"
+    print(f"[bench] generating inputs: {wl.name}", file=sys.stderr, flush=True)
+    lens = synth.prefill_lengths(wl, "cpu")
+    T = int(lens.sum())
+    st = torch.zeros(wl.items + 1, dtype=torch.int32)
+    st[1:] = torch.cumsum(lens, 0)
+    st = st.to(dev)
+    max_len = int(lens.max())
+    pool_t = torch.zeros((wl.layers, wl.items, 2, wl.h, wl.k, wl.d), dtype=torch.bfloat16, device=dev)
+    pool = G.GistPool(pool_t)
+    ids = torch.arange(wl.items, dtype=torch.int32, device=dev)
+    # two activation sets, used by alternate layers (one set is 0.6 GB)
+    sets = []
+    for si in range(2):
+        sets.append((synth.randn((T, wl.hq, wl.d), synth.tensor_seed(wl.seed, 21, si), torch.bfloat16, dev),
+                     synth.randn((T, wl.h, wl.d), synth.tensor_seed(wl.seed, 22, si), torch.bfloat16, dev),
+                     synth.randn((T, wl.h, wl.d), synth.tensor_seed(wl.seed, 23, si), torch.bfloat16, dev)))
+    out = torch.empty_like(sets[0][0])
+    ws = torch.empty(G.gist_prefill_workspace_bytes(T, wl.h, wl.d), dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(wl.d)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step():
+        for li in range(wl.layers):
+            q, k, v = sets[li % 2]
+            G.gist_prefill_attn(q, k, v, st, max_len, 10000.0, scale, out=out, workspace=ws,
+                                pool=pool, layer=li, item_ids=ids, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # one call = the K rotation / gist store kernel, then the attention kernel
+    avg_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
+    flops = prefill_flops(lens.tolist(), wl.hq, wl.d)
+    achieved = flops / avg_s / 1e12
+    res = {
+        "metric": "offline gist extraction tokens/s (causal prefill over items + gist, 24 layers)",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic N(0,1) Q/K/V; seeded item lengths",
+        "config": {"workload": wl.name, "items": wl.items, "tokens": T, "max_len": max_len},
+        "items_per_s": wl.items / (ms / 1e3),
+        "roofline": {"bound": "mfma", "kernel": "prefill_prep + prefill_attn (per call)",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_us": avg_s * 1e6},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import gist_oracle as O
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        b = 0
+        s0, s1 = int(st[b]), int(st[b + 1])
+        q, k, v = (t[s0:s1].to("cpu", torch.float64).numpy() for t in sets[0])
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            for _ in range(wl.layers):
+                O.prefill_attention(q, k, v, [0, s1 - s0], 10000.0, scale)
+            dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": (s1 - s0) / dt, "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"item 0 ({s1 - s0} tokens), all {wl.layers} layers; fp64 "
+                                         f"numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -253,6 +349,9 @@ def main():
         return
     if args.workload in ("paged", "paged_fp8"):
         paged_bench(args, fp8=args.workload == "paged_fp8")
+        return
+    if args.workload == "prefill":
+        prefill_bench(args)
         return
 
     import gist_compressed_kv_amd as G

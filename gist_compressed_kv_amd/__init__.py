@@ -18,7 +18,8 @@ from ._lib import GIST_BF16, GIST_F32, GIST_FP8_E4M3, GistError  # noqa: F401
 __all__ = [
     "GistPool", "GistError", "gist_pool_bytes", "gist_pool_fp8_storage", "gist_pool_create",
     "gist_pool_write",
-    "gist_attn_forward", "paged_decode_workspace_bytes", "paged_decode_attn",
+    "gist_attn_forward", "gist_prefill_workspace_bytes", "gist_prefill_attn",
+    "paged_decode_workspace_bytes", "paged_decode_attn",
 ]
 
 _DTYPES = {torch.bfloat16: GIST_BF16, torch.float32: GIST_F32}
@@ -159,6 +160,50 @@ def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: tor
     _lib.check(_lib.lib().gist_attn_forward(pool.handle, layer, ptrs[0], P, ell, Hq, ptrs[1],
                                             ptrs[2], ptrs[3], pos0, rope_base, scale, qh, qi,
                                             ptrs[4], _stream_ptr(stream)), "gist_attn_forward")
+    return out
+
+
+def gist_prefill_workspace_bytes(n_tokens: int, H: int, d: int) -> int:
+    return _lib.lib().gist_prefill_workspace_bytes(n_tokens, H, d)
+
+
+def gist_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_start: torch.Tensor,
+                      max_len: int | None = None, rope_base: float = 10000.0,
+                      scale: float | None = None, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, pool: GistPool | None = None,
+                      layer: int = 0, item_ids: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Causal attention over packed bf16 sequences [item ; gist] (one layer of
+    the offline gist extraction): q [T, Hq, d], k, v [T, H, d], seq_start int32
+    [B+1].  With a pool, each sequence's last pool.k tokens are stored as the
+    gist of item item_ids[b].  Returns out [T, Hq, d]."""
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [T, Hq, d] and k, v [T, H, d]")
+    T, Hq, d = q.shape
+    H = k.shape[1]
+    B = seq_start.numel() - 1
+    if max_len is None:
+        lens = (seq_start[1:] - seq_start[:-1]) if B > 0 else seq_start[:0]
+        max_len = max(1, int(lens.max().item())) if B > 0 else 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(max(gist_prefill_workspace_bytes(T, H, d), 16), dtype=torch.uint8,
+                                device=q.device)
+    bf = torch.bfloat16
+    ptrs = (_dev(q, "q", bf), _dev(k, "k", bf, (T, H, d)), _dev(v, "v", bf, (T, H, d)),
+            _dev(seq_start, "seq_start", torch.int32), _dev(out, "out", bf, q.shape),
+            _dev(workspace, "workspace"))
+    ph, ids = None, None
+    if pool is not None:
+        ph = pool.handle
+        ids = _dev(item_ids, "item_ids", torch.int32, (B,))
+    _lib.check(_lib.lib().gist_prefill_attn(
+        ptrs[0], ptrs[1], ptrs[2], ptrs[3], B, T, max_len, Hq, H, d, rope_base, scale, ptrs[4],
+        ptrs[5], workspace.numel() * workspace.element_size(), ph, layer, ids,
+        _stream_ptr(stream)), "gist_prefill_attn")
     return out
 
 

@@ -15,7 +15,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libgist_attn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["pool.hip", "gist_forward.hip", "paged_decode.hip"]
+SOURCES = ["pool.hip", "gist_forward.hip", "paged_decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -123,6 +123,30 @@ __device__ __forceinline__ void rope_cos_sin(double pos, double rev, float& c, f
 }
 
 // ---------------------------------------------------------------------------
+// LDS layout of row-major key rows (one row per key, D channels) whose V is
+// read back as MFMA A fragments with the LDS transpose read
+// (ds_read_b64_tr_b16).  One such read covers rows R0..R0+3 (R0 a multiple
+// of 4) and the same 8-byte half of four 16-byte chunks per pass.  With a row
+// stride of D + 4 elements (8 bytes of padding) and the chunks of row R
+// rotated by 3*((R >> 1) & 1), those 16 pieces land on 32 distinct banks, as
+// do the 16-byte row writes of the staging.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ constexpr int vrow_off(int R, int ch, int D) {
+  return R * (D + 4) + ((((ch >> 3) + 3 * ((R >> 1) & 1)) & (D / 8 - 1)) << 3) + (ch & 7);
+}
+
+// Row of the Vᵀ tile that MFMA row r of d-tile dt stands for (16x16 tiles,
+// sixteen channels per d-tile).  The mapping is chosen so that after the P·V
+// product each lane holds, for every 32-channel step s, the eight consecutive
+// channels 32s + 8*(lane/16) .. +8 of its token: the same layout the Q loads
+// use, so output stores are 16-byte vectors.  A transpose read from
+// vrow_off rows yields this mapping when the lane supplying a piece reads
+// channels 32*(dt >> 1) + 4*(dt & 1) + 8*(lane & 3) .. +3.
+__device__ __forceinline__ constexpr int vt_row(int dt, int r) {
+  return 32 * (dt >> 1) + 8 * (r >> 2) + 4 * (dt & 1) + (r & 3);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side pool handle
 // ---------------------------------------------------------------------------
 }  // namespace gist

@@ -110,13 +110,6 @@ __device__ __forceinline__ void for_each_const(F&& f) {
   for_each_const_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Row of the Vᵀ tile that MFMA row r of d-tile dt stands for.  The mapping is
-// chosen so that after the P·V product each lane holds, for every 32-channel
-// step s, the eight consecutive channels 32s + 8*(lane/16) .. +8 of its token:
-// the same layout the Q loads use, so output stores are 16-byte vectors.
-__device__ __forceinline__ constexpr int vt_row(int dt, int r) {
-  return 32 * (dt >> 1) + 8 * (r >> 2) + 4 * (dt & 1) + (r & 3);
-}
 
 // Source row of key j (K or V part selected by `v`) of pair p, KV head g.
 __device__ __forceinline__ const bf16_t* key_row(const FwdArgs& a, const bf16_t* gK,
@@ -560,17 +553,6 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 // query heads are the MFMA columns
 // ---------------------------------------------------------------------------
 
-// Row-major K/V rows in LDS (one row per key, D channels) for the EOS
-// kernel.  V rows are read back as MFMA A fragments with the LDS transpose
-// read (ds_read_b64_tr_b16), which covers rows R0..R0+3 (R0 a multiple of 4)
-// and the same 8-byte half of four 16-byte chunks per pass.  With a row
-// stride of D + 4 elements (8 bytes of padding) and the chunks of row R
-// rotated by 3*((R >> 1) & 1), those 16 pieces land on 32 distinct banks, as
-// do the 16-byte row writes of the staging.
-__device__ __forceinline__ constexpr int eos_off(int R, int ch, int D) {
-  return R * (D + 4) + ((((ch >> 3) + 3 * ((R >> 1) & 1)) & (D / 8 - 1)) << 3) + (ch & 7);
-}
-
 // One wave per (pair, KV head); four per workgroup, each with its own LDS
 // slice, so no workgroup barrier is involved.
 //   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
@@ -788,7 +770,7 @@ gist_fwd_eos(const FwdArgs a) {
   // ---- rows to LDS: the gist V rows, then V_new and K_new -------------------
   auto put = [&](int r, int c, const u32x4_t& w) {
     // rows are 8-byte aligned: two 8-byte stores
-    uint2* dst = (uint2*)(Rl + eos_off(r, 8 * c, D));
+    uint2* dst = (uint2*)(Rl + vrow_off(r, 8 * c, D));
     dst[0] = make_uint2(w.x, w.y);
     dst[1] = make_uint2(w.z, w.w);
   };
@@ -801,8 +783,8 @@ gist_fwd_eos(const FwdArgs a) {
   // K_new rotated at pos0 in place: lane i < D/2 turns channel pair
   // (i, i + D/2) with its own cos/sin and rounds the pair to bf16
   if (lane < D / 2) {
-    bf16_t* kl = Rl + eos_off(KSELF, lane, D);
-    bf16_t* kh = Rl + eos_off(KSELF, lane + D / 2, D);
+    bf16_t* kl = Rl + vrow_off(KSELF, lane, D);
+    bf16_t* kh = Rl + vrow_off(KSELF, lane + D / 2, D);
     const float xl = bf16_bits_to_f32(*kl), xh = bf16_bits_to_f32(*kh);
     const uint32_t pk = pack2_bf16(__builtin_fmaf(xl, csc, -(xh * css)),
                                    __builtin_fmaf(xh, csc, xl * css));
@@ -816,7 +798,7 @@ gist_fwd_eos(const FwdArgs a) {
     bf16x8_t kf[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint2* src = (const uint2*)(Rl + eos_off(KSELF, 32 * s + 8 * q4, D));
+      const uint2* src = (const uint2*)(Rl + vrow_off(KSELF, 32 * s + 8 * q4, D));
       const uint2 lo = src[0], hi = src[1];
       kf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
     }
@@ -877,7 +859,7 @@ gist_fwd_eos(const FwdArgs a) {
       for (int dt = 0; dt < NDT; ++dt) {
         const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
         const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(Rl + eos_off(R, ch, D)));
+            (__attribute__((address_space(3))) s16x4*)(Rl + vrow_off(R, ch, D)));
         o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4_t, v), pv, o[dt],
                                                           0, 0, 0);
       }

@@ -148,6 +148,27 @@ class DecodeWorkload:
         return -(-self.context // self.block_size)
 
 
+@dataclass(frozen=True)
+class PrefillWorkload:
+    name: str
+    layers: int
+    items: int
+    min_item: int  # item tokens, drawn uniformly in [min_item, max_item]
+    max_item: int
+    k: int         # gist tokens appended to every item
+    hq: int
+    h: int
+    d: int
+    seed: int
+
+
+def prefill_lengths(wl: PrefillWorkload, device) -> torch.Tensor:
+    """Sequence lengths (item tokens + k gist tokens) of a prefill workload."""
+    g = generator(wl.seed, "cpu")
+    items = torch.randint(wl.min_item, wl.max_item + 1, (wl.items,), generator=g)
+    return (items + wl.k).to(torch.int32).to(device)
+
+
 TINY = GistWorkload("tiny: 1 layer, 4 pairs over 2 items, k=8, ell=16, Hq=4, H=1, d=64, fp32",
                     1, 2, 8, 16, 4, 1, 64, 4, 2, torch.float32, 1)
 SINGLE_LAYER = GistWorkload("1 layer, Hq=14, H=2, d=64, k=8, ell=64, 500 pairs, 100k-item pool, bf16",
@@ -173,3 +194,7 @@ WIDE_EOS_FP8 = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query
 PAGED_FP8 = DecodeWorkload("paged decode, fp8 E4M3 cache with per-(block, head) scales: 32 requests "
                            "x 4096 cached tokens in 256-token blocks, Hq=H=32, d=128, 32 layers, "
                            "bf16 activations", 32, 32, 4096, 256, 32, 32, 128, torch.bfloat16, 6)
+
+PREFILL = PrefillWorkload("offline gist extraction: 256 items of 900-1100 tokens + 8 gist tokens, "
+                          "causal prefill, Hq=14, H=2, d=64, 24 layers, bf16", 24, 256, 900, 1100, 8,
+                          14, 2, 64, 8)

@@ -155,6 +155,48 @@ gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* i
                               void* stream);
 
 /*
+ * gist_prefill_workspace_bytes — bytes of the workspace gist_prefill_attn
+ * needs for n_tokens packed tokens, H KV heads and head size d (every K row
+ * rotated, bf16).  Returns 0 for invalid shapes.
+ */
+size_t gist_prefill_workspace_bytes(int64_t n_tokens, int H, int d);
+
+/*
+ * gist_prefill_attn — offline gist extraction, one layer ([GIST] 论文做了什么:
+ * the item runs with its k gist tokens appended, and every layer's K/V at the
+ * gist positions are what is kept; 在线的一次 attention: they are stored at
+ * the canonical positions 1..k).  Causal self-attention of B packed bf16
+ * sequences [item tokens ; gist tokens] (over these alone the gist mask of
+ * training is the causal mask) and, when pool != NULL, the store of each
+ * sequence's last pool->k tokens as its gist.
+ *   q          device [n_tokens][Hq][d]; k, v device [n_tokens][H][d]; Q and
+ *              K not yet rotated
+ *   seq_start  device int32 [B+1]: non-decreasing, seq_start[0] = 0,
+ *              seq_start[B] = n_tokens, every length <= max_len.  Sequence b
+ *              is tokens seq_start[b] .. seq_start[b+1]-1 at positions
+ *              1..len.  A sequence whose bounds break these rules is skipped
+ *              on the device (its output rows are not written).
+ *   out        device [n_tokens][Hq][d]: token t of a sequence gets
+ *              softmax(scale * q_t·K^T) V over its keys 0..t
+ *   workspace  device buffer of >= gist_prefill_workspace_bytes(n_tokens, H,
+ *              d) bytes, 16-byte aligned; receives every K row rotated at
+ *              its position (the K the attention reads)
+ *   pool, layer, item_ids  optional bf16 gist pool with the call's H and d:
+ *              the K of the last pool->k tokens of sequence b, rotated at
+ *              1..k, and their V are stored at item item_ids[b] (device int32
+ *              [B]).  Out-of-range ids and sequences shorter than k are
+ *              skipped.  NULL pool: nothing is stored.
+ * bf16 only; d in {64, 128}; Hq a multiple of H; B <= 65535.  B == 0 or
+ * n_tokens == 0 is a no-op.  Two kernels run on the stream, K rotation (and
+ * the gist store) first.
+ */
+gist_status gist_prefill_attn(const void* q, const void* k, const void* v, const int32_t* seq_start,
+                              int B, int64_t n_tokens, int max_len, int Hq, int H, int d,
+                              float rope_base, float scale, void* out, void* workspace,
+                              size_t workspace_bytes, const gist_pool* pool, int layer,
+                              const int32_t* item_ids, void* stream);
+
+/*
  * paged_decode_workspace_bytes — fp32 workspace that paged_decode_attn needs
  * for R requests, Hq query heads, block tables of max_blocks entries of
  * block_size tokens and head size d.  Returns 0 for invalid shapes.

@@ -162,3 +162,42 @@ class DecodeCase:
         return O.paged_decode(kc, vc, t2, lens, f64(self.q[idx]), f64(self.kn[idx]),
                               f64(self.vn[idx]), self.positions.cpu().numpy()[reqs], ROPE_BASE,
                               self.scale)
+
+
+class PrefillCase:
+    """Packed bf16 sequences [item ; gist] for the offline gist extraction."""
+
+    def __init__(self, lens, hq, h, d, seed, device="cuda"):
+        self.lens = list(lens)
+        self.hq, self.h, self.d = hq, h, d
+        T = sum(self.lens)
+        self.T = T
+        st = np.concatenate([[0], np.cumsum(self.lens)]).astype(np.int32)
+        self.seq_start = torch.as_tensor(st, device=device)
+        self.q = synth.randn((T, hq, d), synth.tensor_seed(seed, 21), torch.bfloat16, device)
+        self.k = synth.randn((T, h, d), synth.tensor_seed(seed, 22), torch.bfloat16, device)
+        self.v = synth.randn((T, h, d), synth.tensor_seed(seed, 23), torch.bfloat16, device)
+        self.scale = 1.0 / math.sqrt(d)
+
+    def run(self, out=None, pool=None, layer=0, item_ids=None):
+        return G.gist_prefill_attn(self.q, self.k, self.v, self.seq_start, max(self.lens), ROPE_BASE,
+                                   self.scale, out=out, pool=pool, layer=layer, item_ids=item_ids)
+
+    def oracle(self, seqs=None, rounded=False):
+        """Oracle rows of the listed sequences, as (rows index, values)."""
+        seqs = range(len(self.lens)) if seqs is None else seqs
+        st = self.seq_start.cpu().numpy()
+        idx, vals = [], []
+        for b in seqs:
+            s = slice(int(st[b]), int(st[b + 1]))
+            ref = O.prefill_attention(f64(self.q[s]), f64(self.k[s]), f64(self.v[s]),
+                                      [0, self.lens[b]], ROPE_BASE, self.scale, round_rotated=rounded)
+            idx.append(np.arange(s.start, s.stop))
+            vals.append(ref)
+        return np.concatenate(idx), np.concatenate(vals)
+
+    def max_err(self, out, seqs=None, rounded=False):
+        idx, ref = self.oracle(seqs, rounded)
+        got = f64(out[torch.as_tensor(idx, device=out.device)])
+        assert np.isfinite(got).all(), "non-finite output"
+        return float(np.abs(got - ref).max())

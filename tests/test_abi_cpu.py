@@ -220,3 +220,40 @@ def test_fp8_pool_forward_limits(L):
     finally:
         for h in (pool, qp8, qbf, big):
             L.gist_pool_destroy(h)
+
+
+def _pf(L, B=2, T=100, max_len=64, Hq=4, H=2, d=64, ptr=FAKE, ws=None, pool=None, layer=0,
+        ids=FAKE, scale=0.125, base=1e4):
+    if ws is None:
+        ws = L.gist_prefill_workspace_bytes(T, H, d)
+    return L.gist_prefill_attn(ptr, ptr, ptr, ptr, B, T, max_len, Hq, H, d, base, scale, ptr, ptr,
+                               ws, pool, layer, ids, None)
+
+
+def test_prefill_validation(L):
+    assert L.gist_prefill_workspace_bytes(1000, 2, 64) == 1000 * 2 * 64 * 2
+    assert L.gist_prefill_workspace_bytes(-1, 2, 64) == 0
+    assert _pf(L, B=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, max_len=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, Hq=5) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pf(L, scale=0.0) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, base=float("inf")) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, ptr=ctypes.c_void_p((1 << 20) + 8)) == _lib.GIST_ERR_INVALID_ARG
+    assert _pf(L, ws=100) == _lib.GIST_ERR_INVALID_ARG
+    assert "workspace too small" in L.gist_last_error().decode()
+    assert _pf(L, B=0, ptr=None) == _lib.GIST_OK
+    assert _pf(L, B=70000) == _lib.GIST_ERR_UNSUPPORTED
+    bf = _pool(L, H=2, d=64)
+    f32 = _pool(L, H=2, d=64, dt=F32)
+    other = _pool(L, H=1, d=64)
+    try:
+        assert _pf(L, pool=f32) == _lib.GIST_ERR_UNSUPPORTED
+        assert _pf(L, pool=other) == _lib.GIST_ERR_INVALID_ARG
+        assert _pf(L, pool=bf, layer=2) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert _pf(L, pool=bf, ids=None) == _lib.GIST_ERR_INVALID_ARG
+        assert _pf(L, pool=bf, B=0, ptr=None, ids=None) == _lib.GIST_OK
+    finally:
+        for hd in (bf, f32, other):
+            L.gist_pool_destroy(hd)

@@ -496,3 +496,94 @@ def test_pool_write_fp8_matches_oracle(src_pos0):
                       np.abs(f64(vn)).max(axis=(1, 3)))                # [n][h]
     vmax = np.repeat(np.maximum(vmax, 1.0), 4 // h, axis=1)[:, None, :, None]  # per query head
     assert (np.abs(f64(out) - ref) / vmax).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Offline gist extraction: causal prefill over packed [item ; gist] sequences
+# ---------------------------------------------------------------------------
+
+from gpu_cases import ROPE_BASE, PrefillCase  # noqa: E402
+
+PREFILL_SHAPES = [
+    # lengths, hq, h, d
+    ([1, 2, 16, 31, 32, 33], 4, 2, 64),
+    ([127, 128, 129], 14, 2, 64),
+    ([300, 5, 257], 8, 1, 128),
+    ([200, 64], 16, 2, 128),
+    ([97], 7, 7, 64),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=lambda s: "L%s_hq%d_h%d_d%d" % (
+    "-".join(map(str, s[0])), s[1], s[2], s[3]))
+def test_prefill_shapes(shape):
+    lens, hq, h, d = shape
+    case = PrefillCase(lens, hq, h, d, 700 + sum(lens))
+    out = case.run()
+    torch.cuda.synchronize()
+    err = case.max_err(out)
+    say(f"prefill {shape}: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_prefill_item_length_workload_sampled():
+    wl = synth.PREFILL
+    lens = synth.prefill_lengths(wl, "cpu").tolist()
+    case = PrefillCase(lens, wl.hq, wl.h, wl.d, wl.seed)
+    out = case.run()
+    torch.cuda.synchronize()
+    seqs = [0, len(lens) // 2, len(lens) - 1]
+    err = case.max_err(out, seqs)
+    say(f"prefill workload ({len(lens)} items, {case.T} tokens), sequences {seqs}: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_prefill_peaky_softmax_moves_the_running_maximum():
+    # Q x 8: logits of tens, so the running maximum moves many times; held to
+    # the oracle with the rotated Q and K rounded to bf16, as the kernel does
+    case = PrefillCase([400, 77], 8, 2, 64, 711)
+    case.q.mul_(8.0)
+    out = case.run()
+    torch.cuda.synchronize()
+    err, exact = case.max_err(out, rounded=True), case.max_err(out)
+    say(f"prefill peaky: max-abs err {err:.3g} (vs exact oracle {exact:.3g})")
+    assert err <= 2e-2
+
+
+def test_prefill_writes_the_gist_rows_to_the_pool():
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    lens, kk, h, d = [40, 9, 3, 25], 8, 2, 64
+    case = PrefillCase(lens, 4, h, d, 712)
+    L, N = 2, 6
+    pool_t = torch.zeros((L, N, 2, h, kk, d), dtype=torch.bfloat16, device="cuda")
+    pool = G.GistPool(pool_t)
+    ids = torch.tensor([4, 0, 2, 9], dtype=torch.int32, device="cuda")  # 9: out of range
+    out = case.run(pool=pool, layer=1, item_ids=ids)
+    torch.cuda.synchronize()
+    assert case.max_err(out) <= 2e-2
+    st = case.seq_start.cpu().numpy()
+    gk, gv = O.gist_rows_from_prefill(f64(case.k), f64(case.v), st, kk, ROPE_BASE)
+    got = f64(pool_t)
+    for b, item in [(0, 4), (1, 0)]:
+        ref_k = gk[b].transpose(1, 0, 2)
+        # K rotated in fp32 and rounded to bf16 once: half an ulp, <= 2^-9 relative
+        assert np.abs(got[1, item, 0] - ref_k).max() <= 2.0 ** -8 * np.abs(ref_k).max()
+        assert np.array_equal(got[1, item, 1], gv[b].transpose(1, 0, 2))
+    # sequence 2 is shorter than k and sequence 3 has an out-of-range id:
+    # nothing else was written, and layer 0 is untouched
+    assert not got[1, [1, 2, 3, 5]].any() and not got[0].any()
+
+
+def test_prefill_skips_a_sequence_with_bad_bounds():
+    case = PrefillCase([20, 30, 10], 4, 1, 64, 713)
+    st = case.seq_start.clone()
+    st[2] = st[1] - 1  # sequence 1 ends before it starts; sequence 2 starts early
+    out = torch.full_like(case.q, 7.0)
+    G_ = __import__("gist_compressed_kv_amd")
+    G_.gist_prefill_attn(case.q, case.k, case.v, st, 30, 1e4, case.scale, out=out)
+    torch.cuda.synchronize()
+    o = f64(out)
+    assert (o[20:60] == 7.0).all()  # sequences 1 and 2 (longer than max_len now) skipped
+    idx, ref = case.oracle([0])
+    assert np.abs(o[idx] - ref).max() <= 2e-2
