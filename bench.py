@@ -38,6 +38,7 @@ COUNTER_FILES = {
     "wide_eos_fp8": ("gist_fwd_eos_fp8_d128_wide_eos_counters.json", "gist_forward.hip"),
     "paged": ("paged_decode_32x4096_counters.json", "paged_decode.hip"),
     "paged_fp8": ("paged_decode_fp8_32x4096_counters.json", "paged_decode.hip"),
+    "prefill": ("prefill_attn_d64_256items_counters.json", "prefill.hip"),
 }
 
 
@@ -314,24 +315,24 @@ def prefill_bench(args):
         "items_per_s": wl.items / (ms / 1e3),
         "roofline": {"bound": "mfma", "kernel": "prefill_prep + prefill_attn (per call)",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic("prefill"),
                      "flops_per_launch": flops, "avg_launch_us": avg_s * 1e6},
     }
     if not args.no_cpu_baseline:
         from oracle import gist_oracle as O
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        b = 0
-        s0, s1 = int(st[b]), int(st[b + 1])
-        q, k, v = (t[s0:s1].to("cpu", torch.float64).numpy() for t in sets[0])
+        nb = 4  # the first items, every layer
+        s1 = int(st[nb])
+        q, k, v = (t[:s1].to("cpu", torch.float64).numpy() for t in sets[0])
+        st_cpu = st[:nb + 1].cpu().numpy()
         with threadpool_limits(1):
             t0 = time.perf_counter()
             for _ in range(wl.layers):
-                O.prefill_attention(q, k, v, [0, s1 - s0], 10000.0, scale)
+                O.prefill_attention(q, k, v, st_cpu, 10000.0, scale)
             dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": (s1 - s0) / dt, "unit": "tokens/s",
-                               "cores": 1, "kind": "oracle",
-                               "sample": f"item 0 ({s1 - s0} tokens), all {wl.layers} layers; fp64 "
-                                         f"numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+        res["cpu_baseline"] = {"value": s1 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"items 0-{nb - 1} ({s1} tokens), all {wl.layers} layers; "
+                                         f"fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
     print(json.dumps(res), flush=True)
 
 

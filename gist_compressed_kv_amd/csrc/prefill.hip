@@ -97,16 +97,36 @@ __global__ void __launch_bounds__(256) prefill_prep(const PrefillArgs a) {
   }
 }
 
+// max of x and of x in the lane 32 (resp. 16) apart, with the gfx950 lane
+// swaps: each of the two results of a swap holds the partner's value in one
+// half of the wave and the lane's own value in the other
+__device__ __forceinline__ float xmax32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, __uint_as_float(r[0])),
+                                       __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xmax16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, __uint_as_float(r[0])),
+                                       __uint_as_float(r[1]));
+}
+
 // Causal attention, flash style.  Workgroup = 128 query tokens of one
 // sequence and one query head; wave w holds tokens q0 + 32w .. +31 as two
 // 16-token MFMA column tiles.  Key blocks of 32 tokens are staged in LDS (K
 // rotated, from the workspace; V) with the next block's loads in flight
 // while the current one is computed.  Per key block and column tile:
-//   Sᵀ = K·Qᵀ       v_mfma_f32_16x16x32_bf16 (keys are MFMA rows, so a
-//                   lane's four logits belong to its own query and the
-//                   softmax weights are the B operand of the P·V product)
-//   l += Pᵀ·1, Oᵀ += Vᵀ·Pᵀ   v_mfma_f32_16x16x16_bf16 (Vᵀ fragments by LDS
-//                   transpose reads)
+//   Sᵀ = K·Qᵀ       two 16-key tiles, v_mfma_f32_16x16x32_bf16 (keys are
+//                   MFMA rows, so a lane's logits belong to its own query and
+//                   the softmax weights are the B operand of the P·V product)
+//   l += Pᵀ·1, Oᵀ += Vᵀ·Pᵀ   v_mfma_f32_16x16x32_bf16 over all 32 keys: K-index
+//                   8*q4 + e stands for key 4*q4 + e (e < 4) of the first tile
+//                   and 4*q4 + e - 4 of the second, which is what a lane's
+//                   weights of the two tiles are and what two LDS transpose
+//                   reads (one per tile) give the Vᵀ operand
+// A diagonal block (keys up to the wave's own tokens) is the only one that
+// needs the causal mask; the branch to it is marked unlikely so that the
+// other blocks carry no mask selects.
 // The running maximum is only moved (and O, l rescaled) when a block's
 // maximum exceeds it by more than 8 in log2 units, so most blocks skip the
 // rescale; the weights exp2(s - m) then stay below 2^8.
@@ -199,7 +219,9 @@ prefill_attn(const PrefillArgs a) {
     }
   };
 
-  const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
   const float sl2 = a.scale_log2;
   f32x4_t o[2][NDT], lacc[2];
   float mrun[2];  // running maximum of the raw logits per column tile
@@ -210,7 +232,6 @@ prefill_attn(const PrefillArgs a) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
 
   load_block(0);
   for (int kb = 0; kb < nkb; ++kb) {
@@ -238,7 +259,7 @@ prefill_attn(const PrefillArgs a) {
         sacc[ct][kt] = acc;
       }
     }
-    if (diag) {
+    if (diag) [[unlikely]] {
       // key 32kb + 16kt + 4q4 + r against token qw + 16ct + n
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
@@ -255,8 +276,7 @@ prefill_attn(const PrefillArgs a) {
     for (int ct = 0; ct < 2; ++ct) {
       float m = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
       m = fmaxf(m, fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3])));
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(m))));
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(m))));
+      m = xmax16(xmax32(m));
       mb[ct] = m;
     }
     const bool move0 = (mb[0] - mrun[0]) * sl2 > 8.f, move1 = (mb[1] - mrun[1]) * sl2 > 8.f;
@@ -276,34 +296,32 @@ prefill_attn(const PrefillArgs a) {
           for (int r = 0; r < 4; ++r) o[ct][dt][r] *= alpha;
       }
     }
-    bf16x4v pf[2][2];
+    bf16x8_t pf[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       const float nm = -mrun[ct] * sl2;
+      float p[8];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float p[4];
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ct][kt][r], sl2, nm));
-        pf[ct][kt] = __builtin_bit_cast(bf16x4v, make_uint2(pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3])));
-        lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf[ct][kt], lacc[ct], 0, 0, 0);
-      }
+          p[4 * kt + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ct][kt][r], sl2, nm));
+      pf[ct] = __builtin_bit_cast(bf16x8_t, pack8_bf16(p));
+      lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[ct], lacc[ct], 0, 0, 0);
     }
-    // Oᵀ += Vᵀ·Pᵀ: the lane supplying a piece of the transpose read reads
-    // key (lane >> 2) of the tile, channels 32(dt>>1) + 4(dt&1) + 8(lane&3)..
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
+      s16x4 vv[2];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
-        const s16x4 vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      for (int kt = 0; kt < 2; ++kt)
+        vv[kt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(Vs + vrow_off(16 * kt + (lane >> 2), ch, D)));
-        const bf16x4_t vf = __builtin_bit_cast(bf16x4_t, vv);
+      const bf16x8_t vf = __builtin_bit_cast(
+          bf16x8_t, __builtin_shufflevector(vv[0], vv[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf[ct][kt], o[ct][dt], 0, 0, 0);
-      }
+      for (int ct = 0; ct < 2; ++ct)
+        o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ct], o[ct][dt], 0, 0, 0);
     }
   }
 
