@@ -42,11 +42,11 @@ COUNTER_FILES = {
 }
 
 
-def gist_bytes_per_pair_layer(wl) -> int:
+def gist_bytes_per_pair_layer(wl, last_only: bool = False) -> int:
     """Algorithmic HBM bytes one (pair, layer) must move: the item's gist K/V
     (and query gist, if any), Q in, K_new/V_new in, O out, the 4-byte id.
     An fp8 gist record is one byte per element plus a 4-byte scale per (K or
-    V, head)."""
+    V, head).  last_only: Q and O of the last token only."""
     b = wl.dtype.itemsize
 
     def record(rows):
@@ -57,9 +57,10 @@ def gist_bytes_per_pair_layer(wl) -> int:
     gist = record(wl.k)
     # a query's gist rows are shared by its candidates: counted once per query
     qgist = record(wl.kq) * wl.queries / wl.pairs if wl.kq else 0
-    q = wl.ell * wl.hq * wl.d * b
+    rows = 1 if last_only else wl.ell
+    q = rows * wl.hq * wl.d * b
     kv_new = 2 * wl.ell * wl.h * wl.d * b
-    o = wl.ell * wl.hq * wl.d * b
+    o = rows * wl.hq * wl.d * b
     ids = 4 * (2 if wl.kq else 1)
     return int(round(gist + qgist + q + kv_new + o + ids))
 
@@ -70,7 +71,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b2000", "1L_b500", "wide_ell64", "wide_eos",
+                    choices=["24L_b500", "24L_b500_last", "24L_b2000", "1L_b500", "wide_ell64",
+                             "wide_eos",
                              "wide_eos_fp8", "paged", "paged_fp8", "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
@@ -358,7 +360,10 @@ def main():
     import gist_compressed_kv_amd as G
     from gist_compressed_kv_amd import synth
 
-    wl = {"24L_b500": synth.L24_B500, "24L_b2000": synth.L24_B2000,
+    # 24L_b500_last: the same pass with the final layer producing only the last
+    # token's rows (what the score head reads)
+    last_layer_eos = args.workload == "24L_b500_last"
+    wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500, "24L_b2000": synth.L24_B2000,
           "1L_b500": synth.SINGLE_LAYER, "wide_ell64": synth.WIDE_ELL64,
           "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
     dev = "cuda"
@@ -397,6 +402,8 @@ def main():
         kns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 4, li), wl.dtype, dev))
         vns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 5, li), wl.dtype, dev))
         outs.append(torch.empty_like(qs[-1]))
+    q_lasts = [q[:, -1].contiguous() for q in qs] if last_layer_eos else None
+    out_last = torch.empty_like(q_lasts[0]) if last_layer_eos else None
     torch.cuda.synchronize()
     scale = 1.0 / math.sqrt(wl.d)
     stream = torch.cuda.current_stream()
@@ -407,8 +414,13 @@ def main():
         base = passes[0] * wl.layers
         for li in range(wl.layers):
             si = (base + li) % n_sets
-            G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
-                                qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
+            if last_layer_eos and li == wl.layers - 1:
+                G.gist_attn_forward_last(pool, li, ids, q_lasts[si], kns[si], vns[si], wl.pos0,
+                                         10000.0, scale, qpool=qpool, q_ids=q_ids, out=out_last,
+                                         stream=stream)
+            else:
+                G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
+                                    qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
         passes[0] += 1
 
     for _ in range(args.warmup):
@@ -433,12 +445,19 @@ def main():
 
     bytes_unit = gist_bytes_per_pair_layer(wl)
     bytes_launch = bytes_unit * wl.pairs
+    if last_layer_eos:
+        # the pass moves L-1 full layers and one last-token layer; price the
+        # pass's bytes over the pass's launches
+        last_bytes = gist_bytes_per_pair_layer(wl, last_only=True) * wl.pairs
+        bytes_launch = (bytes_launch * (wl.layers - 1) + last_bytes) / wl.layers
     achieved_gbps = bytes_launch / avg_launch_s / 1e9
     pairs_per_s = wl.pairs / (ms_per_step / 1e3)
     traffic = measured_traffic(args.workload)
 
     res = {
         "metric": METRIC if args.workload == "24L_b500" else
+                  "pairs/s + % of HBM peak, gist-KV attention (24L, GQA 14:2, k=8, ℓ=64; final "
+                  "layer for the last token only)" if last_layer_eos else
                   f"pairs/s + % of HBM peak, gist-KV attention ({args.workload})",
         "value": pairs_per_s,
         "unit": "pairs/s",
@@ -459,7 +478,9 @@ def main():
         "pass_hbm_gbps_algorithmic": bytes_launch * wl.layers / (ms_per_step / 1e3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
+            "kernel": "gist_fwd_mfma<64> (23 full layers + 1 last-token layer; pass bytes / "
+                      "launches)" if last_layer_eos else
+                      "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
                       ("gist_fwd_mfma<128>" if wl.ell > 1 else
                        ("gist_fwd_eos<128, fp8 gist>" if wl.fp8 else "gist_fwd_eos<128>")),
             "achieved": achieved_gbps,
@@ -474,7 +495,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         case = {"pool": pool_t, "ids": ids, "q": qs, "kn": kns, "vn": vns}
-        if wl.kq or n_sets != wl.layers:
+        if wl.kq or n_sets != wl.layers or last_layer_eos:
             res["cpu_baseline"] = None
         else:
             print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

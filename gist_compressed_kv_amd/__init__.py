@@ -18,7 +18,8 @@ from ._lib import GIST_BF16, GIST_F32, GIST_FP8_E4M3, GistError  # noqa: F401
 __all__ = [
     "GistPool", "GistError", "gist_pool_bytes", "gist_pool_fp8_storage", "gist_pool_create",
     "gist_pool_write",
-    "gist_attn_forward", "gist_prefill_workspace_bytes", "gist_prefill_attn",
+    "gist_attn_forward", "gist_attn_forward_last", "gist_prefill_workspace_bytes",
+    "gist_prefill_attn",
     "paged_decode_workspace_bytes", "paged_decode_attn",
 ]
 
@@ -160,6 +161,38 @@ def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: tor
     _lib.check(_lib.lib().gist_attn_forward(pool.handle, layer, ptrs[0], P, ell, Hq, ptrs[1],
                                             ptrs[2], ptrs[3], pos0, rope_base, scale, qh, qi,
                                             ptrs[4], _stream_ptr(stream)), "gist_attn_forward")
+    return out
+
+
+def gist_attn_forward_last(pool: GistPool, layer: int, item_ids: torch.Tensor, q_last: torch.Tensor,
+                           k_new: torch.Tensor, v_new: torch.Tensor, pos0: int | None = None,
+                           rope_base: float = 10000.0, scale: float | None = None,
+                           qpool: GistPool | None = None, q_ids: torch.Tensor | None = None,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The last token only: q_last [P, Hq, d] (token ell-1); k_new, v_new
+    [P, ell, H, d]; returns out [P, Hq, d], row ell-1 of gist_attn_forward."""
+    if q_last.dim() != 3 or k_new.dim() != 4:
+        raise ValueError("q_last must be [P, Hq, d] and k_new, v_new [P, ell, H, d]")
+    P, Hq, d = q_last.shape
+    ell = k_new.shape[1]
+    if pos0 is None:
+        pos0 = pool.k + (qpool.k if qpool is not None else 0) + 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q_last)
+    kv_shape = (P, ell, pool.H, pool.d)
+    dt = pool.act_dtype
+    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q_last, "q_last", dt),
+            _dev(k_new, "k_new", dt, kv_shape), _dev(v_new, "v_new", dt, kv_shape),
+            _dev(out, "out", dt, q_last.shape))
+    qh, qi = None, None
+    if qpool is not None:
+        qh = qpool.handle
+        qi = _dev(q_ids, "q_ids", torch.int32, (P,))
+    _lib.check(_lib.lib().gist_attn_forward_last(
+        pool.handle, layer, ptrs[0], P, ell, Hq, ptrs[1], ptrs[2], ptrs[3], pos0, rope_base, scale,
+        qh, qi, ptrs[4], _stream_ptr(stream)), "gist_attn_forward_last")
     return out
 
 

@@ -62,6 +62,8 @@ struct FwdArgs {
   // are then in bytes
   const float* pool_scales;
   const float* qpool_scales;
+  // the VALU kernel produces only the last token's rows (q, out: one row per pair)
+  int last_only;
 };
 
 // ---------------------------------------------------------------------------
@@ -169,7 +171,10 @@ struct MfmaLds {
 // visible key), so tile j sits at a compile-time offset from one per-wave
 // base address, and only tiles j = 0 and j = 1 can hold keys that some token
 // of the wave may not see.
-template <int D, int NKT, int QPF, int GT>
+// LAST: only the last token's rows are produced (q and out hold one token
+// per pair).  The keys are staged as for every token; only the wave whose
+// token block holds the last token computes, and it stores that token alone.
+template <int D, int NKT, int QPF, int GT, bool LAST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
@@ -206,7 +211,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const int n = lane & 15, q4 = lane >> 4;
   const int t0 = 16 * wv;
   const int t = t0 + n;
-  const bool wave_active = t0 < ell;
+  const bool wave_active = LAST ? (t0 <= ell - 1 && ell - 1 < t0 + 16) : t0 < ell;
   const bool tvalid = t < ell;
   // rows past ell read the last valid token (finite values, never stored)
   const int tl = tvalid ? t : ell - 1;
@@ -221,7 +226,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   constexpr int CPR = D / 8;   // 16-byte chunks per (token, head) row
   constexpr int RPI = 64 / CPR; // token rows per instruction
   const int cl = lane % CPR, rl = lane / CPR;
-  const int64_t pair_off = (int64_t)p * ell * Hq * D;
+  const int64_t pair_off = (int64_t)p * (LAST ? 1 : ell) * Hq * D;
   const char* qpair = (const char*)((const bf16_t*)a.q + pair_off);
   char* opair = (char*)(out + pair_off);
   uint32_t qlane[NS], olane[NS];
@@ -229,9 +234,12 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int tc = t0 + rl + RPI * s;
-    ovalid[s] = tc < ell;
-    qlane[s] = (uint32_t)((((tc < ell ? tc : ell - 1) * Hq + g * G) * D + 8 * cl) * 2);
-    olane[s] = (uint32_t)(((tc * Hq + g * G) * D + 8 * cl) * 2);
+    // LAST: every token row reads the one Q row given, and only the last
+    // token is stored, at the pair's one output row
+    const int tq = LAST ? 0 : (tc < ell ? tc : ell - 1);
+    ovalid[s] = LAST ? tc == ell - 1 : tc < ell;
+    qlane[s] = (uint32_t)(((tq * Hq + g * G) * D + 8 * cl) * 2);
+    olane[s] = (uint32_t)((((LAST ? 0 : tc) * Hq + g * G) * D + 8 * cl) * 2);
   }
   // Q ring held in native vectors (not the HIP uint4 struct) so it always
   // stays in registers
@@ -262,10 +270,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     bad = bad || qid < 0 || qid >= a.qN;
   }
   if (bad) {
-    const int per_t = G * D;
-    for (int u = tid; u < ell * per_t; u += 256) {
+    const int per_t = G * D, nt = LAST ? 1 : ell;
+    for (int u = tid; u < nt * per_t; u += 256) {
       const int t = u / per_t, r = u - t * per_t;
-      out[((int64_t)p * ell + t) * Hq * D + (int64_t)g * G * D + r] = nan_value<bf16_t>();
+      out[((int64_t)p * nt + t) * Hq * D + (int64_t)g * G * D + r] = nan_value<bf16_t>();
     }
     return;
   }
@@ -926,8 +934,12 @@ __global__ void __launch_bounds__(64)
 gist_fwd_valu(const FwdArgs a) {
   constexpr int E2 = D / 32;  // channels per lane in each half
   const int ell = a.ell, H = a.H, G = a.G, Hq = a.Hq;
-  const int t = blockIdx.x % ell;
-  const int pg = blockIdx.x / ell;
+  // last_only: one block per (pair, KV head), for the last token, whose q and
+  // out rows are the pair's only rows
+  const int t = a.last_only ? ell - 1 : blockIdx.x % ell;
+  const int pg = a.last_only ? blockIdx.x : blockIdx.x / ell;
+  const int trow = a.last_only ? 0 : t;  // row of q and out within the pair
+  const int nrow = a.last_only ? 1 : ell;
   const int g = pg % H;
   const int p = pg / H;
   const int lane = threadIdx.x;
@@ -948,7 +960,7 @@ gist_fwd_valu(const FwdArgs a) {
     qid = a.q_ids[p];
     bad = bad || qid < 0 || qid >= a.qN;
   }
-  const int64_t orow0 = (((int64_t)p * ell + t) * Hq + (int64_t)g * G) * D;
+  const int64_t orow0 = (((int64_t)p * nrow + trow) * Hq + (int64_t)g * G) * D;
   if (bad) {
     for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<T>();
     return;
@@ -980,7 +992,7 @@ gist_fwd_valu(const FwdArgs a) {
     for (int e = 0; e < 2 * E2; ++e) o[mh][e] = 0.f, qv[mh][e] = 0.f;
     const int hh = hs + ngh * mh;
     if (mh < hpg && hh < G) {
-      const T* qr = (const T*)a.q + (((int64_t)p * ell + t) * Hq + (int64_t)g * G + hh) * D;
+      const T* qr = (const T*)a.q + (((int64_t)p * nrow + trow) * Hq + (int64_t)g * G + hh) * D;
       float xl[E2], xh[E2];
       load_n<T, E2>(qr + lo, xl);
       load_n<T, E2>(qr + hi, xh);
@@ -1092,7 +1104,7 @@ namespace {
 
 template <typename T, int D>
 void launch_valu(const FwdArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.P * a.H * a.ell));
+  const dim3 grid((unsigned)((int64_t)a.P * a.H * (a.last_only ? 1 : a.ell)));
   const int ngh = a.G < 4 ? a.G : 4;
   const int hpg = (a.G + ngh - 1) / ngh;
   if (hpg <= 1)
@@ -1120,13 +1132,12 @@ int device_cu_count() {
   return cached[dev];
 }
 
-}  // namespace
-
-extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids,
-                                         int P, int ell, int Hq, const void* q, const void* k_new,
-                                         const void* v_new, int pos0, float rope_base, float scale,
-                                         const gist_pool* qpool, const int32_t* q_ids, void* out,
-                                         void* stream) {
+// gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
+// last token of each pair)
+gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P, int ell,
+                         int Hq, const void* q, const void* k_new, const void* v_new, int pos0,
+                         float rope_base, float scale, const gist_pool* qpool,
+                         const int32_t* q_ids, void* out, void* stream, bool last) {
   clear_error();
   if (!pool) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward: pool is NULL");
   if (layer < 0 || layer >= pool->L)
@@ -1184,6 +1195,7 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
   a.G = Hq / H;
   a.pos0 = pos0;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.last_only = last ? 1 : 0;
   make_rope_freqs(a.freqs, d, rope_base);
   {
     double q = std::pow((double)rope_base, -2.0 / (double)d);
@@ -1195,6 +1207,8 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
   if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 104 KiB per workgroup
     const dim3 grid((unsigned)((int64_t)P * H));
+    auto go = [&](auto last_c) {
+    constexpr bool L = decltype(last_c)::value;
     const int nkt = nk_pad / 16;
     const int G = a.G;
     if (d == 64) {
@@ -1206,28 +1220,31 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
         // several generations of workgroups, two heads ahead.
         const bool one_generation = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
         if (G == 7 && one_generation)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 7)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8 && one_generation)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L>), grid, dim3(256), lds, s, a, nk_pad);
         else
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L>), grid, dim3(256),
                            (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     } else {
       if (nkt <= 5) {
         const size_t lds = MfmaLds<128, 5>::bytes(nk_pad, ell);
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0>), grid, dim3(256), lds, s, a, nk_pad);
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L>), grid, dim3(256),
                            (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     }
+    };
+    if (last) go(std::true_type{});
+    else go(std::false_type{});
     return check_launch("gist_attn_forward(mfma)");
   }
   if ((pool->dtype == GIST_BF16 || fp8) && ell == 1 && a.G <= 16 && kg <= 32) {
@@ -1262,4 +1279,25 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
     else launch_valu<float, 128>(a, s);
   }
   return check_launch("gist_attn_forward(valu)");
+}
+
+}  // namespace
+
+extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids,
+                                         int P, int ell, int Hq, const void* q, const void* k_new,
+                                         const void* v_new, int pos0, float rope_base, float scale,
+                                         const gist_pool* qpool, const int32_t* q_ids, void* out,
+                                         void* stream) {
+  return attn_forward(pool, layer, item_ids, P, ell, Hq, q, k_new, v_new, pos0, rope_base, scale,
+                      qpool, q_ids, out, stream, false);
+}
+
+extern "C" gist_status gist_attn_forward_last(const gist_pool* pool, int layer,
+                                              const int32_t* item_ids, int P, int ell, int Hq,
+                                              const void* q_last, const void* k_new,
+                                              const void* v_new, int pos0, float rope_base,
+                                              float scale, const gist_pool* qpool,
+                                              const int32_t* q_ids, void* out, void* stream) {
+  return attn_forward(pool, layer, item_ids, P, ell, Hq, q_last, k_new, v_new, pos0, rope_base,
+                      scale, qpool, q_ids, out, stream, true);
 }

@@ -155,6 +155,25 @@ gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* i
                               void* stream);
 
 /*
+ * gist_attn_forward_last — gist_attn_forward for the last query token of
+ * each pair only.  At the final layer the relevance score reads only the
+ * last position ([GIST] 在线的一次 attention: the score head is applied to
+ * the EOS token's hidden state), so that layer needs one output row per pair.
+ *   q_last   device [P][Hq][d]: Q of token ell-1 only (position pos0+ell-1)
+ *   k_new, v_new  device [P][ell][H][d], every new token (all are keys of
+ *            the last token)
+ *   out      device [P][Hq][d]
+ * Every other argument, limit and error behaviour is that of
+ * gist_attn_forward; the result equals row ell-1 of gist_attn_forward's
+ * output (bit for bit: the same kernels compute it).
+ */
+gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
+                                   int ell, int Hq, const void* q_last, const void* k_new,
+                                   const void* v_new, int pos0, float rope_base, float scale,
+                                   const gist_pool* qpool, const int32_t* q_ids, void* out,
+                                   void* stream);
+
+/*
  * gist_prefill_workspace_bytes — bytes of the workspace gist_prefill_attn
  * needs for n_tokens packed tokens, H KV heads and head size d (every K row
  * rotated, bf16).  Returns 0 for invalid shapes.

@@ -72,6 +72,12 @@ class GistCase:
                                    self.vn[layer], self.pos0, ROPE_BASE, self.scale,
                                    qpool=self.qpool, q_ids=self.q_ids, out=out)
 
+    def run_last(self, layer, out=None):
+        """gist_attn_forward_last with the last token's Q of this case."""
+        return G.gist_attn_forward_last(self.pool, layer, self.ids, self.q[layer][:, -1].contiguous(),
+                                        self.kn[layer], self.vn[layer], self.pos0, ROPE_BASE,
+                                        self.scale, qpool=self.qpool, q_ids=self.q_ids, out=out)
+
     def oracle(self, layer, sample, rounded=False):
         """Oracle rows for the sampled pairs; only the referenced pool rows are
         copied back.  rounded: round the rotated Q and new K to bf16 first."""

@@ -587,3 +587,45 @@ def test_prefill_skips_a_sequence_with_bad_bounds():
     assert (o[20:60] == 7.0).all()  # sequences 1 and 2 (longer than max_len now) skipped
     idx, ref = case.oracle([0])
     assert np.abs(o[idx] - ref).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Last token only (the final layer of a scoring pass)
+# ---------------------------------------------------------------------------
+
+LAST_SHAPES = [
+    # layers, items, k, ell, kq, hq, h, d, pairs, dtype
+    (1, 50, 8, 64, 0, 14, 2, 64, 40, torch.bfloat16),    # ell=64 MFMA kernel (b500 shape)
+    (1, 9, 8, 17, 8, 16, 2, 128, 9, torch.bfloat16),     # MFMA, query gist, d=128
+    (1, 9, 3, 2, 0, 8, 1, 64, 5, torch.bfloat16),        # MFMA, ell=2
+    (1, 9, 8, 33, 0, 16, 4, 64, 1200, torch.bfloat16),   # MFMA, several workgroup generations
+    (1, 9, 8, 1, 8, 64, 8, 128, 7, torch.bfloat16),      # ell=1: the EOS kernel
+    (1, 9, 8, 100, 0, 14, 2, 64, 3, torch.bfloat16),     # VALU kernel (ell > 64)
+    (1, 9, 8, 7, 8, 16, 2, 128, 3, torch.float32),       # VALU kernel, fp32
+]
+
+
+@pytest.mark.parametrize("shape", LAST_SHAPES, ids=lambda s: "ell%d_k%d_kq%d_hq%d_h%d_d%d_p%d_%s" % (
+    s[3], s[2], s[4], s[5], s[6], s[7], s[8], str(s[9])[6:]))
+def test_last_token_only_equals_last_row(shape):
+    layers, items, k, ell, kq, hq, h, d, P, dtype = shape
+    qids = (torch.arange(P) * 7) % 3 if kq else None
+    case = GistCase(layers, items, k, ell, hq, h, d, P, dtype, 800 + ell + hq, kq=kq, n_qrows=3,
+                    q_ids=qids)
+    full = case.run(0).clone()
+    last = case.run_last(0)
+    torch.cuda.synchronize()
+    # the same kernels compute the last row either way
+    assert torch.equal(last, full[:, -1])
+    sample = np.arange(P) if P <= 64 else np.unique(np.r_[0, P - 1, np.arange(0, P, 97)])
+    ref = case.oracle(0, sample)[:, -1]
+    err = float(np.abs(f64(last[torch.as_tensor(sample, device="cuda")]) - ref).max())
+    say(f"last token {shape}: max-abs err {err:.3g}")
+    assert err <= TOL[dtype]
+
+
+def test_last_token_only_bad_ids_give_nan_rows():
+    case = GistCase(1, 6, 8, 64, 14, 2, 64, 4, torch.bfloat16, 820, ids=torch.tensor([0, 6, 3, -1]))
+    o = f64(case.run_last(0))
+    torch.cuda.synchronize()
+    assert np.isnan(o[[1, 3]]).all() and np.isfinite(o[[0, 2]]).all()
