@@ -18,7 +18,8 @@ from ._lib import GIST_BF16, GIST_F32, GIST_FP8_E4M3, GistError  # noqa: F401
 __all__ = [
     "GistPool", "GistError", "gist_pool_bytes", "gist_pool_fp8_storage", "gist_pool_create",
     "gist_pool_write",
-    "gist_attn_forward", "gist_attn_forward_last", "gist_prefill_workspace_bytes",
+    "gist_attn_forward", "gist_attn_forward_last", "gist_attn_forward_paged",
+    "gist_prefill_workspace_bytes",
     "gist_prefill_attn",
     "paged_decode_workspace_bytes", "paged_decode_attn",
 ]
@@ -193,6 +194,37 @@ def gist_attn_forward_last(pool: GistPool, layer: int, item_ids: torch.Tensor, q
     _lib.check(_lib.lib().gist_attn_forward_last(
         pool.handle, layer, ptrs[0], P, ell, Hq, ptrs[1], ptrs[2], ptrs[3], pos0, rope_base, scale,
         qh, qi, ptrs[4], _stream_ptr(stream)), "gist_attn_forward_last")
+    return out
+
+
+def gist_attn_forward_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, item_blocks: torch.Tensor,
+                            k: int, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                            query_blocks: torch.Tensor | None = None, kq: int = 0, q_row0: int = 0,
+                            pos0: int | None = None, rope_base: float = 10000.0,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """EOS step over gists held in a paged cache: k_cache, v_cache bf16
+    [n_blocks, H, block_size, d]; item gist = rows 0..k-1 of item_blocks[p],
+    query gist = rows q_row0..q_row0+kq-1 of query_blocks[p]; q [P, Hq, d],
+    k_new, v_new [P, H, d]; returns out [P, Hq, d]."""
+    n_blocks, H, bs, d = k_cache.shape
+    P, Hq, _ = q.shape
+    if pos0 is None:
+        pos0 = k + kq + 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    bf = torch.bfloat16
+    ptrs = (_dev(k_cache, "k_cache", bf), _dev(v_cache, "v_cache", bf, k_cache.shape),
+            _dev(item_blocks, "item_blocks", torch.int32, (P,)),
+            _dev(query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
+            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (P, H, d)), _dev(v_new, "v_new", bf, (P, H, d)),
+            _dev(out, "out", bf, q.shape))
+    _lib.check(_lib.lib().gist_attn_forward_paged(
+        ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], k, ptrs[3], kq, q_row0, P, Hq, H, d, ptrs[4],
+        ptrs[5], ptrs[6], pos0, rope_base, scale, ptrs[7], _stream_ptr(stream)),
+        "gist_attn_forward_paged")
     return out
 
 

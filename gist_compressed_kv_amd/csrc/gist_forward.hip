@@ -64,6 +64,14 @@ struct FwdArgs {
   const float* qpool_scales;
   // the VALU kernel produces only the last token's rows (q, out: one row per pair)
   int last_only;
+  // paged gist (EOS kernel): item_ids and q_ids are block indices of a paged
+  // cache [N][H][block_size][d] (N blocks; qN = N); the item gist is rows
+  // 0..k-1 of its block, the query gist rows q_row0..q_row0+k'-1 of its block
+  int paged;
+  const void* paged_k;
+  const void* paged_v;
+  int block_size;
+  int q_row0;
 };
 
 // ---------------------------------------------------------------------------
@@ -643,16 +651,30 @@ gist_fwd_eos(const FwdArgs a) {
     for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<bf16_t>();
     return;
   }
-  const C* gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-                (int64_t)g * a.k * D;
-  const C* qK = gK;
-  if (a.kq)
-    qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
-         (int64_t)g * a.kq * D;
-  // gist key j (< kg): K row, and its V row at +H*k*D (item) or +H*k'*D (query)
+  // first K and V rows of the item gist and of the query gist
+  const C *gK, *gV, *qK, *qV;
+  if (a.paged) {
+    const int64_t ib = ((int64_t)item * a.H + g) * a.block_size * D;
+    const int64_t qb = (((int64_t)qid * a.H + g) * a.block_size + a.q_row0) * D;
+    gK = (const C*)a.paged_k + ib;
+    gV = (const C*)a.paged_v + ib;
+    qK = (const C*)a.paged_k + qb;
+    qV = (const C*)a.paged_v + qb;
+  } else {
+    // pool record: K of every head, then V of every head
+    gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+         (int64_t)g * a.k * D;
+    gV = gK + (int64_t)a.H * a.k * D;
+    qK = gK;
+    if (a.kq)
+      qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+           (int64_t)g * a.kq * D;
+    qV = qK + (int64_t)a.H * a.kq * D;
+  }
+  // gist key j (< kg): its K row, or V row
   auto gist_row = [&](int j, bool v) -> const C* {
-    if (j < a.k) return gK + (int64_t)((v ? a.H * a.k : 0) + j) * D;
-    return qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+    if (j < a.k) return (v ? gV : gK) + (int64_t)j * D;
+    return (v ? qV : qK) + (int64_t)(j - a.k) * D;
   };
 
   // ---- gist loads, all unconditional (clamped rows) ------------------------
@@ -1196,6 +1218,10 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
   a.pos0 = pos0;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.last_only = last ? 1 : 0;
+  a.paged = 0;
+  a.paged_k = a.paged_v = nullptr;
+  a.block_size = 0;
+  a.q_row0 = 0;
   make_rope_freqs(a.freqs, d, rope_base);
   {
     double q = std::pow((double)rope_base, -2.0 / (double)d);
@@ -1290,6 +1316,93 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
                                          void* stream) {
   return attn_forward(pool, layer, item_ids, P, ell, Hq, q, k_new, v_new, pos0, rope_base, scale,
                       qpool, q_ids, out, stream, false);
+}
+
+extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache,
+                                               int64_t n_blocks, int block_size,
+                                               const int32_t* item_blocks, int k,
+                                               const int32_t* query_blocks, int kq, int q_row0,
+                                               int P, int Hq, int H, int d, const void* q,
+                                               const void* k_new, const void* v_new, int pos0,
+                                               float rope_base, float scale, void* out,
+                                               void* stream) {
+  clear_error();
+  if (P < 0) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: P < 0");
+  if (n_blocks < 1 || n_blocks > INT32_MAX || block_size < 1)
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: bad n_blocks or block_size");
+  if (d != 64 && d != 128)
+    return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: d must be 64 or 128");
+  if (H < 1 || Hq < H || Hq % H != 0)
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: Hq must be a positive multiple of H");
+  if (Hq / H > 16) return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: Hq/H must be <= 16");
+  if (k < 1 || kq < 0 || q_row0 < 0 || k > block_size || q_row0 + kq > block_size)
+    return fail(GIST_ERR_INVALID_ARG,
+                "gist_attn_forward_paged: gist rows must lie within one block (k >= 1)");
+  if (k + kq > 32) return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: k + k' must be <= 32");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: scale must be positive and finite");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: rope_base must be positive");
+  if (kq > 0 && !query_blocks)
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: query_blocks is NULL");
+  if (P == 0) return GIST_OK;
+  if (!k_cache || !v_cache || !item_blocks || !q || !k_new || !v_new || !out)
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: NULL tensor argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
+      !aligned16(v_new) || !aligned16(out))
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: tensors must be 16-byte aligned");
+  if ((int64_t)P * H > INT32_MAX)
+    return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: P*H too large for one launch");
+
+  FwdArgs a = {};
+  a.N = n_blocks;
+  a.k = k;
+  a.qN = n_blocks;
+  a.kq = kq;
+  a.item_ids = item_blocks;
+  a.q_ids = kq ? query_blocks : nullptr;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.out = out;
+  a.P = P;
+  a.ell = 1;
+  a.Hq = Hq;
+  a.H = H;
+  a.G = Hq / H;
+  a.pos0 = pos0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  make_rope_freqs(a.freqs, d, rope_base);
+  {
+    double qq = std::pow((double)rope_base, -2.0 / (double)d);
+    for (int b = 0; b < 6; ++b, qq *= qq) a.rev_step[b] = qq;
+  }
+  a.paged = 1;
+  a.paged_k = k_cache;
+  a.paged_v = v_cache;
+  a.block_size = block_size;
+  a.q_row0 = q_row0;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
+  const int kg = k + kq;
+  const bool qu2 = a.G * (d / 16) > 64;
+  auto go = [&](auto d_c, auto ngt_c) {
+    constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
+    if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (d == 64) {
+    if (kg <= 16) go(I64{}, I1{});
+    else go(I64{}, I2{});
+  } else {
+    if (kg <= 16) go(I128{}, I1{});
+    else go(I128{}, I2{});
+  }
+  return check_launch("gist_attn_forward_paged");
 }
 
 extern "C" gist_status gist_attn_forward_last(const gist_pool* pool, int layer,

@@ -155,6 +155,34 @@ gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* i
                               void* stream);
 
 /*
+ * gist_attn_forward_paged — the query-gist EOS step (ell = 1, [GIST]
+ * 能不能再进一步: one token over the item gist, the query gist and itself)
+ * with both gists read from a paged KV cache in the layout paged decode uses,
+ * so gist rows and decode sequences can live in one block pool.  With
+ * 16-token blocks, k + k' = 8 + 8 fills one block exactly (the alignment the
+ * same section recommends): pass query_blocks = item_blocks and q_row0 = k.
+ *   k_cache, v_cache  device bf16 [n_blocks][H][block_size][d]; gist K rows
+ *                     already rotated at their canonical positions (item
+ *                     gist 1..k, query gist k+1..k+k')
+ *   item_blocks       device int32 [P]: the item gist of pair p is rows
+ *                     0..k-1 of block item_blocks[p]
+ *   query_blocks      device int32 [P] (NULL when k' = 0): the query gist is
+ *                     rows q_row0 .. q_row0+k'-1 of block query_blocks[p]
+ *   q, k_new, v_new, out  as gist_attn_forward with ell = 1: q, out
+ *                     [P][Hq][d]; k_new, v_new [P][H][d]
+ *   pos0              position of the token: k + k' + 1
+ * Limits: d in {64, 128}; Hq % H == 0, Hq/H <= 16; 1 <= k; k + k' <= 32;
+ * both gists within a block.  Block indices are bounds-checked on the
+ * device (out-of-range: the pair's rows are NaN).  P == 0 is a no-op.
+ */
+gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache, int64_t n_blocks,
+                                    int block_size, const int32_t* item_blocks, int k,
+                                    const int32_t* query_blocks, int kq, int q_row0, int P, int Hq,
+                                    int H, int d, const void* q, const void* k_new,
+                                    const void* v_new, int pos0, float rope_base, float scale,
+                                    void* out, void* stream);
+
+/*
  * gist_attn_forward_last — gist_attn_forward for the last query token of
  * each pair only.  At the final layer the relevance score reads only the
  * last position ([GIST] 在线的一次 attention: the score head is applied to

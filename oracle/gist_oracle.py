@@ -229,6 +229,24 @@ def pool_write(pool: np.ndarray, layer: int, ids, k_src: np.ndarray,
     return out
 
 
+def paged_gist_pools(k_cache, v_cache, item_blocks, k: int, query_blocks, kq: int, q_row0: int):
+    """Gists held in a paged cache [n_blocks][H][bs][d] as one-layer pools:
+    pair p's item gist is rows 0..k-1 of block item_blocks[p] and its query
+    gist rows q_row0..q_row0+kq-1 of block query_blocks[p].  Returns (pool,
+    qpool), each [1][P][2][H][rows][d] (qpool None when kq = 0), to be read
+    with item id p and query id p."""
+    kc = np.asarray(k_cache, np.float64)
+    vc = np.asarray(v_cache, np.float64)
+    ib = np.asarray(item_blocks, np.int64)
+    pool = np.stack([kc[ib, :, :k], vc[ib, :, :k]], axis=1)[None]
+    qpool = None
+    if kq:
+        qb = np.asarray(query_blocks, np.int64)
+        rows = slice(q_row0, q_row0 + kq)
+        qpool = np.stack([kc[qb, :, rows], vc[qb, :, rows]], axis=1)[None]
+    return pool, qpool
+
+
 # ---------------------------------------------------------------------------
 # Offline gist extraction, one layer ([GIST] "论文做了什么": the item is run
 # with its k gist tokens appended and the gist positions' K/V are kept;

@@ -257,3 +257,26 @@ def test_prefill_validation(L):
     finally:
         for hd in (bf, f32, other):
             L.gist_pool_destroy(hd)
+
+
+def _pg(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE, scale=0.125):
+    return L.gist_attn_forward_paged(ptr, ptr, nblk, bs, ptr, k, qb, kq, q_row0, P, Hq, H, d, ptr,
+                                     ptr, ptr, k + kq + 1, 1e4, scale, ptr, None)
+
+
+def test_paged_gist_validation(L):
+    assert _pg(L, P=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, nblk=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, bs=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg(L, Hq=3) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, Hq=34) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg(L, k=0) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, k=17) == _lib.GIST_ERR_INVALID_ARG        # item gist past the block
+    assert _pg(L, q_row0=9) == _lib.GIST_ERR_INVALID_ARG    # query gist past the block
+    assert _pg(L, bs=64, k=20, kq=20, q_row0=20) == _lib.GIST_ERR_UNSUPPORTED  # k + k' > 32
+    assert _pg(L, qb=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, ptr=ctypes.c_void_p((1 << 20) + 4)) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg(L, P=0, ptr=None) == _lib.GIST_OK
+    assert _pg(L, kq=0, qb=None, P=0, ptr=None) == _lib.GIST_OK

@@ -629,3 +629,77 @@ def test_last_token_only_bad_ids_give_nan_rows():
     o = f64(case.run_last(0))
     torch.cuda.synchronize()
     assert np.isnan(o[[1, 3]]).all() and np.isfinite(o[[0, 2]]).all()
+
+
+# ---------------------------------------------------------------------------
+# Gists read from a paged cache (the decode cache layout)
+# ---------------------------------------------------------------------------
+
+
+def _paged_from_case(case, bs, same_block):
+    """The case's layer-0 gists in a paged cache: item gist of pair p in rows
+    0..k-1 of block 2p (or p), query gist in rows k.. of the same block or
+    rows 0.. of block 2p+1."""
+    P, h, d, k, kq = case.pairs, case.h, case.d, case.k, case.kq
+    nb = P if same_block else 2 * P
+    kc = torch.zeros((nb, h, bs, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    ib = torch.arange(P, device="cuda") * (1 if same_block else 2)
+    qb = ib if same_block else ib + 1
+    q_row0 = k if same_block else 0
+    rec = case.pool_t[0][case.ids.long()]  # [P][2][H][k][d]
+    kc[ib, :, :k], vc[ib, :, :k] = rec[:, 0], rec[:, 1]
+    if kq:
+        qrec = case.qpool_t[0][case.q_ids.long()]
+        kc[qb, :, q_row0:q_row0 + kq], vc[qb, :, q_row0:q_row0 + kq] = qrec[:, 0], qrec[:, 1]
+    return kc, vc, ib.to(torch.int32), qb.to(torch.int32), q_row0
+
+
+PAGED_GIST_SHAPES = [
+    # k, kq, hq, h, d, pairs, block size, same block
+    (8, 8, 64, 8, 128, 40, 16, True),     # 8 + 8 gist rows fill one 16-token block
+    (8, 8, 64, 8, 128, 40, 16, False),    # item and query gist in separate blocks
+    (8, 0, 14, 2, 64, 30, 16, False),
+    (12, 12, 16, 2, 128, 9, 32, True),
+    (5, 3, 8, 1, 64, 7, 16, False),
+]
+
+
+@pytest.mark.parametrize("shape", PAGED_GIST_SHAPES, ids=lambda s: "k%d_kq%d_hq%d_h%d_d%d_p%d_bs%d_%s" % (
+    s[0], s[1], s[2], s[3], s[4], s[5], s[6], "one" if s[7] else "two"))
+def test_paged_gist_eos_equals_pooled(shape):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    k, kq, hq, h, d, P, bs, same = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 11, k, 1, hq, h, d, P, torch.bfloat16, 900 + k + kq + hq, kq=kq, n_qrows=3,
+                    q_ids=qids)
+    pooled = case.run(0)
+    kc, vc, ib, qb, q_row0 = _paged_from_case(case, bs, same)
+    paged = G.gist_attn_forward_paged(kc, vc, ib, k, case.q[0][:, 0].contiguous(), case.kn[0][:, 0],
+                                      case.vn[0][:, 0], query_blocks=qb if kq else None, kq=kq,
+                                      q_row0=q_row0, pos0=case.pos0, scale=case.scale)
+    torch.cuda.synchronize()
+    # the same kernel reads the same rows through another address
+    assert torch.equal(paged, pooled[:, 0])
+    pool, qpool = O.paged_gist_pools(f64(kc), f64(vc), ib.cpu().numpy(), k,
+                                     qb.cpu().numpy() if kq else None, kq, q_row0)
+    ref = O.gist_attn_forward(pool, 0, np.arange(P), f64(case.q[0]), f64(case.kn[0]), f64(case.vn[0]),
+                              case.pos0, ROPE_BASE, case.scale, qpool=qpool,
+                              q_ids=np.arange(P) if kq else None)[:, 0]
+    err = float(np.abs(f64(paged) - ref).max())
+    say(f"paged gist {shape}: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_paged_gist_bad_block_gives_nan_rows():
+    import gist_compressed_kv_amd as G
+    case = GistCase(1, 11, 8, 1, 16, 2, 64, 4, torch.bfloat16, 930, kq=8, n_qrows=3,
+                    q_ids=torch.tensor([0, 1, 2, 0]))
+    kc, vc, ib, qb, q_row0 = _paged_from_case(case, 16, True)
+    ib[1] = 99
+    qb[2] = -1
+    o = f64(G.gist_attn_forward_paged(kc, vc, ib, 8, case.q[0][:, 0].contiguous(), case.kn[0][:, 0],
+                                      case.vn[0][:, 0], query_blocks=qb, kq=8, q_row0=8))
+    torch.cuda.synchronize()
+    assert np.isnan(o[[1, 2]]).all() and np.isfinite(o[[0, 3]]).all()

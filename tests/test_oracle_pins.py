@@ -787,3 +787,31 @@ def test_toy_model_offline_extraction_by_prefill_then_online():
         x = x + a.reshape(ell, hq * d) @ L["wo"]
         x = x + mlp(x)
     assert np.allclose(x, train_rows, atol=1e-10)
+
+
+def test_paged_gist_pools_round_trip_and_attention():
+    r = rng(50)
+    P, H, d, k, kq, bs, nb = 5, 2, 16, 4, 3, 8, 12
+    pool = r.standard_normal((1, P, 2, H, k, d))
+    qpool = r.standard_normal((1, P, 2, H, kq, d))
+    kc = np.zeros((nb, H, bs, d))
+    vc = np.zeros_like(kc)
+    ib = np.array([3, 0, 7, 11, 5])
+    qb = np.array([1, 2, 4, 6, 8])
+    q_row0 = 2
+    for p in range(P):
+        for g in range(H):
+            kc[ib[p], g, :k], vc[ib[p], g, :k] = pool[0, p, 0, g], pool[0, p, 1, g]
+            kc[qb[p], g, q_row0:q_row0 + kq] = qpool[0, p, 0, g]
+            vc[qb[p], g, q_row0:q_row0 + kq] = qpool[0, p, 1, g]
+    gp, gq = O.paged_gist_pools(kc, vc, ib, k, qb, kq, q_row0)
+    assert np.array_equal(gp, pool) and np.array_equal(gq, qpool)
+    # both gists in one block (item rows 0..k-1, query rows k..k+kq-1)
+    kc1 = np.zeros((P, H, bs, d))
+    vc1 = np.zeros_like(kc1)
+    kc1[:, :, :k], vc1[:, :, :k] = pool[0, :, 0], pool[0, :, 1]
+    kc1[:, :, k:k + kq], vc1[:, :, k:k + kq] = qpool[0, :, 0], qpool[0, :, 1]
+    gp1, gq1 = O.paged_gist_pools(kc1, vc1, np.arange(P), k, np.arange(P), kq, k)
+    assert np.array_equal(gp1, pool) and np.array_equal(gq1, qpool)
+    gp0, gq0 = O.paged_gist_pools(kc, vc, ib, k, None, 0, 0)
+    assert gq0 is None and np.array_equal(gp0, pool)
