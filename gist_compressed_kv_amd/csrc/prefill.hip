@@ -270,21 +270,40 @@ prefill_attn(const PrefillArgs a) {
             if (16 * kt + 4 * q4 + r > 16 * ct + n) sacc[ct][kt][r] = -INFINITY;
     }
 
-    // online softmax with a lazily moved maximum
-    float mb[2];
+    // online softmax with a lazily moved maximum.  The weights are formed
+    // with the running maximum as it stands, alongside the lane-local maxima;
+    // if no lane has a logit above its running maximum + 8 (log2 units), no
+    // column maximum does, nothing moves, and the cross-lane reduction is
+    // skipped.  Otherwise (always on the first block) the maxima that moved
+    // rescale O and l and the weights are formed again.
+    float w[2][8];
+    auto weigh = [&](int ct) {
+      const float nm = -mrun[ct] * sl2;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          w[ct][4 * kt + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ct][kt][r], sl2, nm));
+    };
+    weigh(0);
+    weigh(1);
+    auto mx3 = [](float x, float y, float z) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
+    float ml[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      float m = fmaxf(fmaxf(sacc[ct][0][0], sacc[ct][0][1]), fmaxf(sacc[ct][0][2], sacc[ct][0][3]));
-      m = fmaxf(m, fmaxf(fmaxf(sacc[ct][1][0], sacc[ct][1][1]), fmaxf(sacc[ct][1][2], sacc[ct][1][3])));
-      m = xmax16(xmax32(m));
-      mb[ct] = m;
+      float m = mx3(sacc[ct][0][0], sacc[ct][0][1], sacc[ct][0][2]);
+      m = mx3(m, sacc[ct][0][3], sacc[ct][1][0]);
+      m = mx3(m, sacc[ct][1][1], sacc[ct][1][2]);
+      ml[ct] = __builtin_elementwise_maximum(m, sacc[ct][1][3]);
     }
-    const bool move0 = (mb[0] - mrun[0]) * sl2 > 8.f, move1 = (mb[1] - mrun[1]) * sl2 > 8.f;
-    if (__builtin_amdgcn_ballot_w64(move0 || move1)) {
+    if (__builtin_amdgcn_ballot_w64((ml[0] - mrun[0]) * sl2 > 8.f || (ml[1] - mrun[1]) * sl2 > 8.f)) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const bool mv = ct == 0 ? move0 : move1;
-        const float mnew = mv ? mb[ct] : mrun[ct];
+        const float mb = xmax16(xmax32(ml[ct]));  // the column maximum
+        const bool mv = (mb - mrun[ct]) * sl2 > 8.f;
+        const float mnew = mv ? mb : mrun[ct];
         // the first block: mrun = -inf, the products are 0 * 0
         const float alpha = mv ? __builtin_amdgcn_exp2f((mrun[ct] - mnew) * sl2) : 1.f;
         mrun[ct] = mnew;
@@ -294,19 +313,13 @@ prefill_attn(const PrefillArgs a) {
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[ct][dt][r] *= alpha;
+        weigh(ct);
       }
     }
     bf16x8_t pf[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      const float nm = -mrun[ct] * sl2;
-      float p[8];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          p[4 * kt + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ct][kt][r], sl2, nm));
-      pf[ct] = __builtin_bit_cast(bf16x8_t, pack8_bf16(p));
+      pf[ct] = __builtin_bit_cast(bf16x8_t, pack8_bf16(w[ct]));
       lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[ct], lacc[ct], 0, 0, 0);
     }
 #pragma unroll
