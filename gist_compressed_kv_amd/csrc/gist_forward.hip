@@ -180,8 +180,9 @@ struct MfmaLds {
 // base address, and only tiles j = 0 and j = 1 can hold keys that some token
 // of the wave may not see.
 // LAST: only the last token's rows are produced (q and out hold one token
-// per pair).  The keys are staged as for every token; only the wave whose
-// token block holds the last token computes, and it stores that token alone.
+// per pair).  The keys are staged as for every token; every wave takes the
+// 16-token block that holds the last token and the group's heads are spread
+// over the four waves (head h on wave h mod 4), each storing that token alone.
 template <int D, int NKT, int QPF, int GT, bool LAST>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 gist_fwd_mfma(const FwdArgs a, int nk_pad) {
@@ -217,9 +218,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const int wv = __builtin_amdgcn_readfirstlane(((tid >> 6) + blockIdx.x) & 3);
   const int lane = tid & 63;
   const int n = lane & 15, q4 = lane >> 4;
-  const int t0 = 16 * wv;
+  const int t0 = LAST ? 16 * ((ell - 1) >> 4) : 16 * wv;
   const int t = t0 + n;
-  const bool wave_active = LAST ? (t0 <= ell - 1 && ell - 1 < t0 + 16) : t0 < ell;
+  const bool wave_active = LAST ? wv < G : t0 < ell;
   const bool tvalid = t < ell;
   // rows past ell read the last valid token (finite values, never stored)
   const int tl = tvalid ? t : ell - 1;
@@ -261,7 +262,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   };
 #pragma unroll
   for (int i = 0; i < QPF; ++i) {
-    const int hq = i < G ? i : G - 1;
+    // LAST: slot 0 holds this wave's first head
+    const int hq = LAST ? (wv < G ? wv : G - 1) : (i < G ? i : G - 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       raw[i][s] = __builtin_nontemporal_load((const u32x4_t*)(qpair + qlane[s] + (uint32_t)(hq * D) * 2));
@@ -541,7 +543,14 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         }
         };
 
-  if constexpr (GT > 0) {
+  if constexpr (LAST) {
+    // heads wv, wv + 4, ...: the first from the prefetch, the next loaded here
+    using S0 = std::integral_constant<int, 0>;
+    for (int hh = wv; hh < G; hh += 4) {
+      if (hh != wv) load_q(S0{}, hh);
+      head(S0{}, hh, [] {});
+    }
+  } else if constexpr (GT > 0) {
     // compile-time group size: the whole head sequence unrolls, so the ring
     // slot of every head and every wait count is known to the compiler
     for_each_const<GT>([&](auto hc) {
