@@ -136,13 +136,19 @@ prefill_attn(const PrefillArgs a) {
   constexpr int NS = D / 32;  // 32-channel steps of the Q·Kᵀ product
   constexpr int NP = NS / 2;  // RoPE: step s pairs with step s + NP
   constexpr int NDT = D / 16;
-  constexpr int KS = D + 8;   // K row stride (elements): 16*odd bytes
+  // K and V rows are D + 16 elements apart (160 B at d = 64, 288 B at 128):
+  // with that stride the 16-row b128 reads of K and the transposed b64 reads
+  // of V run at the LDS's full rate; a stride of D + 8 costs 1.9x and 1.5x.
+  constexpr int KS = D + 16;
   constexpr int BN = 32;      // keys per block
   constexpr int CPR = D / 8;  // 16-byte chunks per row
   constexpr int SU = BN * CPR / 256;  // staging chunks per thread per tensor
   static_assert(SU >= 1 && BN * CPR % 256 == 0, "staging layout");
   __shared__ __align__(16) bf16_t Ks[BN * KS];
-  __shared__ __align__(16) bf16_t Vs[BN * (D + 4)];
+  // V row r holds channel ch at vpos(ch): the four channels that a lane of
+  // the transposed read takes for output tile dt sit at 16 dt + 4 (lane & 3),
+  // so the four lanes of a row read 32 contiguous bytes
+  __shared__ __align__(16) bf16_t Vs[BN * KS];
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
@@ -165,7 +171,9 @@ prefill_attn(const PrefillArgs a) {
   const int kb_diag = qw / BN;                 // this wave's diagonal block
   const bool wave_active = qw < len;
 
-  // ---- Q of the wave's two column tiles, rotated at t+1, MFMA B layout -----
+  // ---- Q of the wave's two column tiles, rotated at t+1 and multiplied by
+  // scale * log2(e) (the logits then come out in log2 units), MFMA B layout --
+  const float sl2 = a.scale_log2;
   bf16x8_t qf[2][NS];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
@@ -183,8 +191,8 @@ prefill_attn(const PrefillArgs a) {
       for (int e = 0; e < 8; ++e) {
         float cs, sn;
         rope_cos_sin((double)(t + 1), a.freqs.rev[32 * s + 8 * q4 + e], cs, sn);
-        yl[e] = __builtin_fmaf(xl[e], cs, -(xh[e] * sn));
-        yh[e] = __builtin_fmaf(xh[e], cs, xl[e] * sn);
+        yl[e] = __builtin_fmaf(xl[e], cs, -(xh[e] * sn)) * sl2;
+        yh[e] = __builtin_fmaf(xh[e], cs, xl[e] * sn) * sl2;
       }
       qf[ct][s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
       qf[ct][s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
@@ -196,15 +204,18 @@ prefill_attn(const PrefillArgs a) {
   // query of the workgroup) -------------------------------------------------
   const bf16_t* kseq = a.k_rot + (s0 * a.H + g) * D;
   const bf16_t* vseq = a.v + (s0 * a.H + g) * D;
-  const int64_t rstride = (int64_t)a.H * D;
+  // element offsets inside the sequence fit 32 bits (len * H * d < 2^31 is
+  // checked on the host) and rows times the row stride fit a 24-bit product
+  const unsigned rstride = (unsigned)(a.H * D);
   u32x4_t kst[SU], vst[SU];
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
       const int u = tid + 256 * i;
-      const int r = min(BN * kb + u / CPR, len - 1), c = u % CPR;
-      kst[i] = *(const u32x4_t*)(kseq + r * rstride + 8 * c);
-      vst[i] = *(const u32x4_t*)(vseq + r * rstride + 8 * c);
+      const unsigned r = (unsigned)min(BN * kb + u / CPR, len - 1), c = u % CPR;
+      const unsigned e = __umul24(r, rstride) + 8 * c;
+      kst[i] = *(const u32x4_t*)(kseq + e);
+      vst[i] = *(const u32x4_t*)(vseq + e);
     }
   };
   auto store_block = [&]() {
@@ -213,21 +224,26 @@ prefill_attn(const PrefillArgs a) {
       const int u = tid + 256 * i;
       const int r = u / CPR, c = u % CPR;
       *(u32x4_t*)(Ks + r * KS + 8 * c) = kst[i];
-      uint2* dst = (uint2*)(Vs + vrow_off(r, 8 * c, D));
-      dst[0] = make_uint2(vst[i].x, vst[i].y);
-      dst[1] = make_uint2(vst[i].z, vst[i].w);
+      // channels 8c..8c+3 go to vpos(8c) = 32 (c >> 2) + 4 (c & 3), and
+      // 8c+4..8c+7 sixteen elements further
+      bf16_t* vrow = Vs + r * KS + 32 * (c >> 2) + 4 * (c & 3);
+      *(uint2*)vrow = make_uint2(vst[i].x, vst[i].y);
+      *(uint2*)(vrow + 16) = make_uint2(vst[i].z, vst[i].w);
     }
   };
 
   bf16x8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
-  const float sl2 = a.scale_log2;
   f32x4_t o[2][NDT], lacc[2];
-  float mrun[2];  // running maximum of the raw logits per column tile
+  // minus the running maximum of the logits (log2 units) per column tile, in
+  // all four entries: the logit accumulators start from it, so they hold the
+  // logit minus the maximum.  0 before the first block, where the maximum is
+  // always taken.
+  f32x4_t negm[2];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
-    mrun[ct] = -INFINITY;
+    negm[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     lacc[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[ct][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -252,12 +268,25 @@ prefill_attn(const PrefillArgs a) {
         kf[s] = *(const bf16x8_t*)(Ks + (16 * kt + n) * KS + 32 * s + 8 * q4);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc = negm[ct];
 #pragma unroll
         for (int s = 0; s < NS; ++s)
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[ct][s], acc, 0, 0, 0);
         sacc[ct][kt] = acc;
       }
+    }
+    // V operands of the weighted sum, read now so that the LDS latency is
+    // covered by the softmax: channels 32 (dt >> 1) + 4 (dt & 1) + 8 (lane & 3)
+    // .. +3 of key rows 16 kt + (lane >> 2)
+    bf16x8_t vf[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      s16x4 vv[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        vv[kt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+            Vs + (16 * kt + (lane >> 2)) * KS + 16 * dt + 4 * (lane & 3)));
+      vf[dt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vv[0], vv[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
     if (diag) [[unlikely]] {
       // key 32kb + 16kt + 4q4 + r against token qw + 16ct + n
@@ -270,23 +299,20 @@ prefill_attn(const PrefillArgs a) {
             if (16 * kt + 4 * q4 + r > 16 * ct + n) sacc[ct][kt][r] = -INFINITY;
     }
 
-    // online softmax with a lazily moved maximum.  The weights are formed
-    // with the running maximum as it stands, alongside the lane-local maxima;
-    // if no lane has a logit above its running maximum + 8 (log2 units), no
-    // column maximum does, nothing moves, and the cross-lane reduction is
-    // skipped.  Otherwise (always on the first block) the maxima that moved
-    // rescale O and l and the weights are formed again.
+    // online softmax with a lazily moved maximum.  The accumulators hold the
+    // logits minus the running maximum, so the weights are their exponentials
+    // as they stand, formed alongside the lane-local maxima.  If no lane holds
+    // a value above 8 (log2 units), no column maximum exceeds the running one
+    // by more than 8, nothing moves, and the cross-lane reduction is skipped.
+    // Otherwise, and always on the first block, the columns whose maximum
+    // moved rescale O and l and form their weights again.
     float w[2][8];
-    auto weigh = [&](int ct) {
-      const float nm = -mrun[ct] * sl2;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          w[ct][4 * kt + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[ct][kt][r], sl2, nm));
-    };
-    weigh(0);
-    weigh(1);
+        for (int r = 0; r < 4; ++r) w[ct][4 * kt + r] = __builtin_amdgcn_exp2f(sacc[ct][kt][r]);
     auto mx3 = [](float x, float y, float z) {
       return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
     };
@@ -298,22 +324,29 @@ prefill_attn(const PrefillArgs a) {
       m = mx3(m, sacc[ct][1][1], sacc[ct][1][2]);
       ml[ct] = __builtin_elementwise_maximum(m, sacc[ct][1][3]);
     }
-    if (__builtin_amdgcn_ballot_w64((ml[0] - mrun[0]) * sl2 > 8.f || (ml[1] - mrun[1]) * sl2 > 8.f)) {
+    const bool first = kb == 0;
+    if (first || __builtin_amdgcn_ballot_w64(ml[0] > 8.f || ml[1] > 8.f)) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float mb = xmax16(xmax32(ml[ct]));  // the column maximum
-        const bool mv = (mb - mrun[ct]) * sl2 > 8.f;
-        const float mnew = mv ? mb : mrun[ct];
-        // the first block: mrun = -inf, the products are 0 * 0
-        const float alpha = mv ? __builtin_amdgcn_exp2f((mrun[ct] - mnew) * sl2) : 1.f;
-        mrun[ct] = mnew;
+        // the column maximum relative to the running one; on the first block
+        // O and l are still zero and the maximum is taken as it is
+        const float mb = xmax16(xmax32(ml[ct]));
+        const float dm = (first || mb > 8.f) ? mb : 0.f;
+        const float nm = negm[ct][0] - dm;
+        negm[ct] = f32x4_t{nm, nm, nm, nm};
+        if (!first) {
+          const float alpha = __builtin_amdgcn_exp2f(-dm);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lacc[ct][r] *= alpha;
+          for (int r = 0; r < 4; ++r) lacc[ct][r] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o[ct][dt][r] *= alpha;
-        weigh(ct);
+            for (int r = 0; r < 4; ++r) o[ct][dt][r] *= alpha;
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w[ct][4 * kt + r] = __builtin_amdgcn_exp2f(sacc[ct][kt][r] - dm);
       }
     }
     bf16x8_t pf[2];
@@ -323,19 +356,10 @@ prefill_attn(const PrefillArgs a) {
       lacc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[ct], lacc[ct], 0, 0, 0);
     }
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
-      s16x4 vv[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        vv[kt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(Vs + vrow_off(16 * kt + (lane >> 2), ch, D)));
-      const bf16x8_t vf = __builtin_bit_cast(
-          bf16x8_t, __builtin_shufflevector(vv[0], vv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
-        o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ct], o[ct][dt], 0, 0, 0);
-    }
+        o[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf[ct], o[ct][dt], 0, 0, 0);
   }
 
   // ---- normalize and store: lane holds channels 32s + 8q4 .. +7 ----------
@@ -406,7 +430,7 @@ extern "C" gist_status gist_prefill_attn(const void* q, const void* k, const voi
     return fail(GIST_ERR_INVALID_ARG, "gist_prefill_attn: workspace too small");
   const int64_t prep_blocks = ((int64_t)max_len * H * (d / 16) + 255) / 256;
   const int64_t qblocks = (max_len + 127) / 128;
-  if (prep_blocks > INT32_MAX || B > 65535 || Hq > 65535)
+  if (prep_blocks > INT32_MAX || B > 65535 || Hq > 65535 || (int64_t)max_len * H * d >= (1LL << 31))
     return fail(GIST_ERR_UNSUPPORTED, "gist_prefill_attn: shape too large for one launch");
 
   PrefillArgs a;

@@ -233,7 +233,8 @@ size_t gist_prefill_workspace_bytes(int64_t n_tokens, int H, int d);
  *              1..k, and their V are stored at item item_ids[b] (device int32
  *              [B]).  Out-of-range ids and sequences shorter than k are
  *              skipped.  NULL pool: nothing is stored.
- * bf16 only; d in {64, 128}; Hq a multiple of H; B <= 65535.  B == 0 or
+ * bf16 only; d in {64, 128}; Hq a multiple of H; B <= 65535;
+ * max_len * H * d < 2^31 (else GIST_ERR_UNSUPPORTED).  B == 0 or
  * n_tokens == 0 is a no-op.  Two kernels run on the stream, K rotation (and
  * the gist store) first.
  */

@@ -38,7 +38,8 @@ library makes identically):
 * bf16 rounding points (used only when asked for, by ``round_rotated``): the
   rotated Q and the rotated new K are rounded to bf16, as an unfused
   RoPE-then-attention pipeline stores them; the stored gist K and every V
-  are bf16 inputs already.
+  are bf16 inputs already.  For the prefill the rounded Q may carry a factor
+  (``q_factor``: the softmax scale folded into Q before its rounding).
 * fp8 storage (the pages name KV quantization as a lever but fix no scheme):
   OCP FP8 E4M3 codes with one fp32 scale per block (a paged-cache (block,
   head); a gist pool's (item, K or V, head)), scale = amax / 448, codes the
@@ -260,7 +261,8 @@ def causal_mask(n: int) -> np.ndarray:
 
 
 def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, base: float,
-                      scale: float, round_rotated: bool = False) -> np.ndarray:
+                      scale: float, round_rotated: bool = False,
+                      q_factor: float = 1.0) -> np.ndarray:
     """Causal self-attention of B packed sequences [item tokens ; gist tokens].
 
     q [T][Hq][d]; k, v [T][H][d], not rotated.  Sequence b is tokens
@@ -268,7 +270,10 @@ def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, ba
     KV head h // (Hq/H).  Over [item ; gist] alone the gist mask of training
     is the causal mask: it only removes item keys from tokens after the gist,
     and none are present.  With round_rotated the rotated Q and K are rounded
-    to bf16 first.  Returns out [T][Hq][d].
+    to bf16 first; the Q rounded is the rotated Q times q_factor, divided by it
+    again after rounding (a pipeline that folds the softmax scale into Q rounds
+    that product).  Without rounding q_factor changes nothing.
+    Returns out [T][Hq][d].
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -289,7 +294,7 @@ def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, ba
             qr = rope(q[s0:s1, hh], pos, base)
             kr = rope(k[s0:s1, g], pos, base)
             if round_rotated:
-                qr, kr = round_bf16(qr), round_bf16(kr)
+                qr, kr = round_bf16(qr * q_factor) / q_factor, round_bf16(kr)
             out[s0:s1, hh] = attention(qr, kr, v[s0:s1, g], mask, scale)
     return out
 

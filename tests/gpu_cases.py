@@ -184,6 +184,9 @@ class PrefillCase:
         self.k = synth.randn((T, h, d), synth.tensor_seed(seed, 22), torch.bfloat16, device)
         self.v = synth.randn((T, h, d), synth.tensor_seed(seed, 23), torch.bfloat16, device)
         self.scale = 1.0 / math.sqrt(d)
+        # the kernel rounds the rotated Q times scale * log2(e) (an fp32
+        # product) to bf16; the rounded oracle rounds the same product
+        self.q_factor = float(np.float32(self.scale) * np.float32(1.4426950408889634))
 
     def run(self, out=None, pool=None, layer=0, item_ids=None):
         return G.gist_prefill_attn(self.q, self.k, self.v, self.seq_start, max(self.lens), ROPE_BASE,
@@ -197,7 +200,8 @@ class PrefillCase:
         for b in seqs:
             s = slice(int(st[b]), int(st[b + 1]))
             ref = O.prefill_attention(f64(self.q[s]), f64(self.k[s]), f64(self.v[s]),
-                                      [0, self.lens[b]], ROPE_BASE, self.scale, round_rotated=rounded)
+                                      [0, self.lens[b]], ROPE_BASE, self.scale, round_rotated=rounded,
+                                      q_factor=self.q_factor)
             idx.append(np.arange(s.start, s.stop))
             vals.append(ref)
         return np.concatenate(idx), np.concatenate(vals)

@@ -715,6 +715,24 @@ def test_prefill_sequences_are_independent_and_causal():
     assert np.array_equal(out2[7:], out[7:])
 
 
+def test_prefill_q_factor_moves_only_the_rounding_point():
+    # q_factor acts only inside the bf16 rounding of the rotated Q: the exact
+    # result ignores it, a power of two commutes with the rounding (the same
+    # result bit for bit), and another factor rounds a different product,
+    # which moves the output only by what rounding Q can move it
+    r = rng(43)
+    lens = [11, 6]
+    q, k, v, st = _packed(r, lens, 4, 2, 16)
+    exact = O.prefill_attention(q, k, v, st, 1e4, 0.25)
+    assert np.array_equal(O.prefill_attention(q, k, v, st, 1e4, 0.25, q_factor=0.18), exact)
+    rounded = O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True)
+    assert np.array_equal(
+        O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True, q_factor=0.125), rounded)
+    other = O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True, q_factor=0.18)
+    assert not np.array_equal(other, rounded)
+    assert np.abs(other - exact).max() < 2e-2
+
+
 def test_gist_rows_equal_the_pool_write_of_the_prefill_keys():
     r = rng(42)
     h, d, n_gist = 2, 16, 4
