@@ -28,6 +28,7 @@
 //    including both members of its RoPE pairs, dot products reduce across the
 //    16-lane row with DPP.  This is the ell = 1 path (EOS over item gist +
 //    query gist + itself) and the fp32 path.
+#include <atomic>
 #include <cfloat>
 #include <type_traits>
 #include <utility>
@@ -1149,18 +1150,19 @@ void launch_valu(const FwdArgs& a, hipStream_t s) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Compute units of the current device, queried once per device (a lookup
-// that fails counts as 256, the MI355X figure).
+// that fails counts as 256, the MI355X figure).  Calls from several host
+// threads may fill an entry at the same time; they store the same value.
 int device_cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
