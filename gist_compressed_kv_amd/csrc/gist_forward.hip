@@ -10,24 +10,27 @@
 // sees every gist key and new keys 0..t, and gets softmax(scale·q·Kᵀ)·V
 // (mcfzz.com "为什么自回归推理缓存 KV，而不缓存历史 Q？", Reusable-state).
 //
-// Two kernels:
-//  * gist_fwd_mfma<D>  bf16, 2 <= ell <= 64, k+k'+ell <= 128.  One workgroup
-//    (4 wave64s) per (pair, KV head).  All keys of the pair are staged once
-//    in LDS (K row-major with RoPE applied on load, V transposed), and each
-//    wave owns 16 query tokens and loops over the G query heads of the GQA
-//    group, so every K/V tile in LDS serves all G heads.  Logits are
-//    computed transposed, Sᵀ = K·Qᵀ, with v_mfma_f32_16x16x32_bf16, so each
-//    lane ends up holding four keys of one token; that is exactly the B
-//    operand layout of the P·V product (v_mfma_f32_16x16x16_bf16, Oᵀ = Vᵀ·Pᵀ)
-//    and the softmax never leaves registers.  Softmax is online over 16-key
-//    tiles (running max and sum in fp32, exp2 with log2(e) folded into the
-//    scale); causally invisible tiles are skipped.
-//  * gist_fwd_valu<T, D, MAXH>  any ell, any gist length, bf16 or fp32.  One
-//    wave64 per (pair, KV head, token); four 16-lane rows split the heads of
-//    the group (or, for G < 4, the keys), each lane holds d/16 channels
-//    including both members of its RoPE pairs, dot products reduce across the
-//    16-lane row with DPP.  This is the ell = 1 path (EOS over item gist +
-//    query gist + itself) and the fp32 path.
+// Three kernels:
+//  * gist_fwd_mfma  bf16 activations, 2 <= ell <= 64, k+k'+ell <= 128, bf16
+//    or fp8 gist pools.  One workgroup (4 wave64s) per (pair, KV head).  All
+//    keys of the pair are staged once in LDS (K row-major with RoPE applied on
+//    load, V transposed), and each wave owns 16 query tokens and loops over
+//    the G query heads of the GQA group, so every K/V tile in LDS serves all
+//    G heads.  Logits are computed transposed, Sᵀ = K·Qᵀ, with
+//    v_mfma_f32_16x16x32_bf16, so each lane ends up holding four keys of one
+//    token: exactly the B operand layout of the P·V product
+//    (v_mfma_f32_16x16x16_bf16, Oᵀ = Vᵀ·Pᵀ), and the softmax never leaves
+//    registers.  All keys of a token are in registers at once, so the row
+//    maximum is exact before the exponentials; causally invisible tiles are
+//    skipped.
+//  * gist_fwd_eos  ell = 1 (the EOS token over item gist + query gist +
+//    itself), bf16 activations, bf16 or fp8 gist pools, G <= 16, k+k' <= 32.
+//    One wave per (pair, KV head); the G query heads are the MFMA columns.
+//  * gist_fwd_valu<T, D, MAXH>  every other shape (bf16 with ell > 64 or
+//    long gists, and fp32).  One wave64 per (pair, KV head, token); four
+//    16-lane rows split the heads of the group (or, for G < 4, the keys), each
+//    lane holds d/16 channels including both members of its RoPE pairs, dot
+//    products reduce across the 16-lane row with DPP.
 #include <atomic>
 #include <cfloat>
 #include <type_traits>
@@ -184,8 +187,12 @@ struct MfmaLds {
 // per pair).  The keys are staged as for every token; every wave takes the
 // 16-token block that holds the last token and the group's heads are spread
 // over the four waves (head h on wave h mod 4), each storing that token alone.
-template <int D, int NKT, int QPF, int GT, bool LAST>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
+// FP8: the gist pools hold E4M3 codes.  They are decoded exactly into the bf16
+// rows of LDS; the K scale of a gist key multiplies its fp32 logit, and the V
+// scale its softmax weight in the P·V product (the row sum takes the unscaled
+// weight).
+template <int D, int NKT, int QPF, int GT, bool LAST, bool FP8>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !FP8 ? 4 : 2)))
 gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
   constexpr int KS = MfmaLds<D, NKT>::KS;
@@ -288,30 +295,63 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     }
     return;
   }
-  const bf16_t* gK = (const bf16_t*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-                     (int64_t)g * a.k * D;
-  const bf16_t* qK = nullptr;
+  typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
+  const C* gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+                (int64_t)g * a.k * D;
+  const C* qK = nullptr;
   if (a.kq)
-    qK = (const bf16_t*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+    qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
          (int64_t)g * a.kq * D;
+  // eight channels from channel ch of key row j as bf16 (E4M3 codes decode
+  // exactly); the new rows are bf16 activations
+  auto load8 = [&](int j, bool v, int ch) -> uint4 {
+    if constexpr (FP8) {
+      if (j < kg) {
+        const C* row = j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
+                               : qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+        const uint2 w = *(const uint2*)(row + ch);
+        float f[8];
+        decode4_e4m3(w.x, f);
+        decode4_e4m3(w.y, f + 4);
+        return pack8_bf16(f);
+      }
+      const bf16_t* base = (const bf16_t*)(v ? a.v_new : a.k_new);
+      return *(const uint4*)(base + (((int64_t)p * a.ell + (j - kg)) * a.H + g) * D + ch);
+    } else {
+      return *(const uint4*)(key_row(a, gK, qK, p, g, j, kg, D, v) + ch);
+    }
+  };
+  // fp8: K and V scales of the item gist and of the query gist (scalars)
+  float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
+  if constexpr (FP8) {
+    const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+    ski = si[g];
+    svi = si[a.H + g];
+    if (a.kq) {
+      const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+      skq = sq[g];
+      svq = sq[a.H + g];
+    }
+  }
 
   // ---- issue every staging load of this thread ----------------------------
   // Every load below is unconditional (out-of-range units read row 0 and
   // are zeroed afterwards), so the compiler can count the loads in flight
-  // exactly and later waits never have to drain the Q prefetch.
+  // exactly and later waits never have to drain the Q prefetch (bf16 pools;
+  // fp8 gist rows take a load of their own).
   uint4 klo[IT], khi[IT], v0[IT], v1[IT];
   const int npairs = nk_pad >> 1;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int u = tid + 256 * it;
     const int j = u / CH, c = u - j * CH;
-    const bf16_t* src = key_row(a, gK, qK, p, g, j < nk ? j : 0, kg, D, false);
-    klo[it] = *(const uint4*)(src + 8 * c);
-    khi[it] = *(const uint4*)(src + D / 2 + 8 * c);
+    const int jc = j < nk ? j : 0;
+    klo[it] = load8(jc, false, 8 * c);
+    khi[it] = load8(jc, false, D / 2 + 8 * c);
     const int cv = u / npairs, jp = u - cv * npairs;
     const int cvc = cv < CV ? cv : 0;
-    v0[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp < nk ? 2 * jp : 0, kg, D, true) + 8 * cvc);
-    v1[it] = *(const uint4*)(key_row(a, gK, qK, p, g, 2 * jp + 1 < nk ? 2 * jp + 1 : 0, kg, D, true) + 8 * cvc);
+    v0[it] = load8(2 * jp < nk ? 2 * jp : 0, true, 8 * cvc);
+    v1[it] = load8(2 * jp + 1 < nk ? 2 * jp + 1 : 0, true, 8 * cvc);
   }
 
   // keep the staging loads together (the Q prefetch above was issued first
@@ -487,6 +527,16 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
               const bf16x8_t kf = *(const bf16x8_t*)(kbase + 16 * KS * j + 32 * s);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
             }
+            if constexpr (FP8) {
+              // slot r of lane group q4 is key 16*(nkt-1-j) + 15 - 4*q4 - r;
+              // every tile takes a factor per slot (1 past the gist), with
+              // selects rather than a branch around the MFMA results
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key = 16 * (nkt - 1 - j) + 15 - 4 * q4 - r;
+                acc[r] *= key < a.k ? ski : (key < kg ? skq : 1.f);
+              }
+            }
             sacc[j] = acc;
             mx = vmax3(mx, acc[0], acc[1]);
             mx = vmax3(mx, acc[2], acc[3]);
@@ -507,17 +557,27 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
         for (int j = 0; j < NKT; ++j) {
           if (j == 0 || j < nkt) {
-            const uint2 pk = make_uint2(
-                pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][0], sl2, nmx)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][1], sl2, nmx))),
-                pack2_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][2], sl2, nmx)),
-                           __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][3], sl2, nmx))));
+            float w[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r], sl2, nmx));
+            const uint2 pk = make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]));
             const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
             lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
+            // the weights of the product with V; fp8: a gist key's weight
+            // carries its V scale
+            bf16x4v pv = pf;
+            if constexpr (FP8) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int key = 16 * (nkt - 1 - j) + 15 - 4 * q4 - r;
+                w[r] *= key < a.k ? svi : (key < kg ? svq : 1.f);
+              }
+              pv = __builtin_bit_cast(bf16x4v, make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3])));
+            }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
               const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pv, o[dt], 0, 0, 0);
             }
           }
         }
@@ -1193,9 +1253,16 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     if (!q_ids) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward: q_ids is NULL");
   }
   const bool fp8 = pool->dtype == GIST_FP8_E4M3;
-  if (fp8 && !(ell == 1 && Hq / H <= 16 && pool->k + (qpool ? qpool->k : 0) <= 32))
-    return fail(GIST_ERR_UNSUPPORTED,
-                "gist_attn_forward: fp8 pools support ell == 1, Hq/H <= 16 and k + k' <= 32 only");
+  {
+    // fp8 pools run on the MFMA and EOS kernels only
+    const int kgv = pool->k + (qpool ? qpool->k : 0);
+    const bool mfma_shape = ell >= 2 && ell <= 64 && (kgv + ell + 15) / 16 * 16 <= 128;
+    const bool eos_shape = ell == 1 && Hq / H <= 16 && kgv <= 32;
+    if (fp8 && !mfma_shape && !eos_shape)
+      return fail(GIST_ERR_UNSUPPORTED,
+                  "gist_attn_forward: fp8 pools support 2 <= ell <= 64 with k + k' + ell <= 128, "
+                  "or ell == 1 with Hq/H <= 16 and k + k' <= 32");
+  }
   if (P == 0) return GIST_OK;
   if (!item_ids || !q || !k_new || !v_new || !out)
     return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward: NULL tensor argument");
@@ -1242,12 +1309,28 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
 
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  if (pool->dtype == GIST_BF16 && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 104 KiB per workgroup
+  if ((pool->dtype == GIST_BF16 || fp8) && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 104 KiB per workgroup
     const dim3 grid((unsigned)((int64_t)P * H));
     auto go = [&](auto last_c) {
     constexpr bool L = decltype(last_c)::value;
     const int nkt = nk_pad / 16;
     const int G = a.G;
+    if (fp8) {
+      // fp8 pools: the instances with the group size taken from the arguments
+      if (d == 64 && nkt <= 5)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 0, L, true>), grid, dim3(256),
+                           (MfmaLds<64, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
+      else if (d == 64)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, true>), grid, dim3(256),
+                           (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+      else if (nkt <= 5)
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, true>), grid, dim3(256),
+                           (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
+      else
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 1, 0, L, true>), grid, dim3(256),
+                           (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+      return;
+    }
     if (d == 64) {
       if (nkt <= 5) {
         const size_t lds = MfmaLds<64, 5>::bytes(nk_pad, ell);
@@ -1257,25 +1340,25 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
         // several generations of workgroups, two heads ahead.
         const bool one_generation = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
         if (G == 7 && one_generation)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 7)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8 && one_generation)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, false>), grid, dim3(256),
                            (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     } else {
       if (nkt <= 5) {
         const size_t lds = MfmaLds<128, 5>::bytes(nk_pad, ell);
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L>), grid, dim3(256), lds, s, a, nk_pad);
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, false>), grid, dim3(256),
                            (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       }
     }

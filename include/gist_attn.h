@@ -141,12 +141,13 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  * bf16 with 2 <= ell <= 64 and k + k' + ell <= 128 runs the MFMA kernel;
  * bf16 with ell == 1, Hq / H <= 16 and k + k' <= 32 the EOS kernel; every
  * other case runs the VALU kernel.
- * GIST_FP8_E4M3 pools: q, k_new, v_new and out are bf16, qpool must be fp8
- * too, and only the EOS kernel's shapes (ell == 1, Hq / H <= 16,
- * k + k' <= 32) are implemented; other shapes return GIST_ERR_UNSUPPORTED.
- * Every E4M3 value is a bf16 value, so the codes enter the matrix products
- * exactly; a key's K scale multiplies its fp32 logit and its V scale its
- * softmax weight.
+ * GIST_FP8_E4M3 pools: q, k_new, v_new and out are bf16 and qpool must be
+ * fp8 too.  The MFMA shapes (2 <= ell <= 64, k + k' + ell <= 128) and the
+ * EOS shapes (ell == 1, Hq / H <= 16, k + k' <= 32) are implemented; other
+ * shapes return GIST_ERR_UNSUPPORTED.  Every E4M3 value is a bf16 value, so
+ * the codes enter the matrix products exactly; a key's K scale multiplies
+ * its fp32 logit and its V scale its softmax weight in the product with V
+ * (the softmax denominator takes the unscaled weight).
  */
 gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                               int ell, int Hq, const void* q, const void* k_new,
@@ -193,7 +194,7 @@ gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache, in
  *   out      device [P][Hq][d]
  * Every other argument, limit and error behaviour is that of
  * gist_attn_forward; the result equals row ell-1 of gist_attn_forward's
- * output (bit for bit: the same kernels compute it).
+ * output (bit for bit: the same kernel code computes it).
  */
 gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                                    int ell, int Hq, const void* q_last, const void* k_new,

@@ -208,17 +208,24 @@ def test_fp8_pool_forward_limits(L):
     qp8 = _pool(L, k=8, dt=FP8)
     qbf = _pool(L, k=8, dt=BF16)
     big = _pool(L, k=30, dt=FP8)  # k + k' = 38 > 32
+    p64 = _pool(L, k=64, dt=FP8)
     try:
-        # only the ell = 1 (EOS) shapes are implemented for fp8 pools
-        assert _fwd(L, pool, ell=16) == _lib.GIST_ERR_UNSUPPORTED
+        # fp8 pools run on the MFMA kernel (2 <= ell <= 64, k + k' + ell <= 128)
+        # and the EOS kernel (ell = 1, Hq/H <= 16, k + k' <= 32) only
+        assert _fwd(L, pool, ell=65) == _lib.GIST_ERR_UNSUPPORTED
         assert "fp8" in L.gist_last_error().decode()
+        assert _fwd(L, p64, ell=2, qpool=p64, qids=FAKE) == _lib.GIST_ERR_UNSUPPORTED
         assert _fwd(L, pool, ell=1, Hq=34) == _lib.GIST_ERR_UNSUPPORTED
         assert _fwd(L, pool, ell=1, qpool=big, qids=FAKE) == _lib.GIST_ERR_UNSUPPORTED
+        # in range: validated, nothing launched for P = 0
+        assert _fwd(L, pool, ell=16, P=0, ptr=None, ids=None) == _lib.GIST_OK
+        assert _fwd(L, p64, ell=64, P=0, ptr=None, ids=None) == _lib.GIST_OK
         # the query-gist pool must be fp8 too
         assert _fwd(L, pool, ell=1, qpool=qbf, qids=FAKE) == _lib.GIST_ERR_INVALID_ARG
+        assert _fwd(L, pool, ell=16, qpool=qbf, qids=FAKE) == _lib.GIST_ERR_INVALID_ARG
         assert _fwd(L, pool, ell=1, P=0, qpool=qp8, qids=FAKE, ptr=None, ids=None) == _lib.GIST_OK
     finally:
-        for h in (pool, qp8, qbf, big):
+        for h in (pool, qp8, qbf, big, p64):
             L.gist_pool_destroy(h)
 
 

@@ -433,6 +433,86 @@ def test_wide_eos_fp8_workload_sampled():
     check_gist(case, sample=sample, label="wide EOS, fp8 item+query gist, 2000 pairs")
 
 
+# The ell >= 2 (MFMA) kernel over fp8 pools: codes decoded exactly into the
+# bf16 rows it stages, K scales on the gist logits, V scales on the gist
+# weights of the P·V product.
+MFMA_FP8_SHAPES = [
+    # k, kq, ell, hq, h, d, pairs
+    (8, 0, 64, 14, 2, 64, 40),    # the b500 shape
+    (8, 0, 64, 64, 8, 128, 6),    # the wide ell = 64 shape
+    (8, 8, 16, 64, 8, 128, 9),    # item + query gist, d = 128
+    (17, 0, 40, 12, 3, 64, 7),    # gist keys over two key tiles
+    (20, 12, 64, 16, 2, 64, 5),   # 96 keys: the 128-key instance, d = 64
+    (16, 16, 60, 8, 1, 128, 4),   # 92 keys: the 128-key instance, d = 128
+    (3, 0, 2, 8, 1, 64, 5),       # ell = 2
+]
+
+
+@pytest.mark.parametrize("shape", MFMA_FP8_SHAPES,
+                         ids=lambda s: "k%d_kq%d_ell%d_hq%d_h%d_d%d_p%d" % s)
+def test_mfma_fp8_pool_shapes(shape):
+    k, kq, ell, hq, h, d, P = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(2, 7, k, ell, hq, h, d, P, torch.bfloat16, 640 + k + kq + ell, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    check_gist(case, label=f"mfma fp8 {shape}")
+
+
+@pytest.mark.parametrize("shape", [MFMA_FP8_SHAPES[0], MFMA_FP8_SHAPES[2]],
+                         ids=lambda s: "k%d_kq%d_ell%d_hq%d_h%d_d%d_p%d" % s)
+def test_mfma_fp8_last_token_equals_last_row(shape):
+    k, kq, ell, hq, h, d, P = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 7, k, ell, hq, h, d, P, torch.bfloat16, 660 + ell, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    full = case.run(0).clone()
+    last = case.run_last(0)
+    torch.cuda.synchronize()
+    assert torch.equal(last, full[:, -1])
+    ref = case.oracle(0, np.arange(P))[:, -1]
+    assert float(np.abs(f64(last) - ref).max()) <= 2e-2
+
+
+@pytest.mark.parametrize("scales", ["k", "v", "kv"])
+@pytest.mark.parametrize("shape", [MFMA_FP8_SHAPES[0], MFMA_FP8_SHAPES[2], MFMA_FP8_SHAPES[4],
+                                   (8, 8, 1, 64, 8, 128, 9), (8, 0, 1, 14, 2, 64, 11)],
+                         ids=lambda s: "k%d_kq%d_ell%d_hq%d_h%d_d%d_p%d" % s)
+def test_fp8_pool_with_power_of_two_scales_equals_bf16_pool(shape, scales):
+    # with every scale a power of two, scaling the logits and weights commutes
+    # with every rounding, so an fp8 pool must give the bf16 pool of its
+    # decoded values bit for bit (the ell = 1 shapes run the EOS kernel)
+    import gist_compressed_kv_amd as G
+    from gpu_cases import ROPE_BASE
+    k, kq, ell, hq, h, d, P = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 7, k, ell, hq, h, d, P, torch.bfloat16, 680 + ell + hq, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    ks = 2.0 ** -7 if "k" in scales else 1.0
+    vs = 2.0 ** -6 if "v" in scales else 1.0
+    bf = []
+    for pl in [case.pool] + ([case.qpool] if case.qpool is not None else []):
+        pl.scales[:, :, 0].fill_(ks)
+        pl.scales[:, :, 1].fill_(vs)
+        vals = pl.codes.view(torch.float8_e4m3fn).float()
+        vals[:, :, 0] *= ks
+        vals[:, :, 1] *= vs
+        bf.append(G.GistPool(vals.to(torch.bfloat16).contiguous()))
+    o8 = case.run(0).clone()
+    ob = G.gist_attn_forward(bf[0], 0, case.ids, case.q[0], case.kn[0], case.vn[0], case.pos0,
+                             ROPE_BASE, case.scale, qpool=bf[1] if kq else None, q_ids=case.q_ids)
+    torch.cuda.synchronize()
+    assert torch.equal(o8, ob)
+
+
+def test_mfma_fp8_out_of_range_ids_give_nan_rows_only():
+    case = GistCase(1, 6, 8, 64, 14, 2, 64, 5, torch.bfloat16, 670, ids=torch.tensor([0, 6, 2, -1, 5]),
+                    fp8=True)
+    o = f64(case.run(0))
+    torch.cuda.synchronize()
+    assert np.isnan(o[[1, 3]]).all() and np.isfinite(o[[0, 2, 4]]).all()
+    assert case.max_err(0, case.run(0), [0, 2, 4]) <= 2e-2
+
+
 def test_eos_fp8_out_of_range_ids_give_nan_rows_only():
     case = GistCase(1, 6, 8, 1, 64, 8, 128, 5, torch.bfloat16, 610, kq=8, n_qrows=2,
                     ids=torch.tensor([0, 6, 2, 5, -3]), q_ids=torch.tensor([0, 1, 2, 1, 0]),
