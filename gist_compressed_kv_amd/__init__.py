@@ -19,9 +19,10 @@ __all__ = [
     "GistPool", "GistError", "gist_pool_bytes", "gist_pool_fp8_storage", "gist_pool_create",
     "gist_pool_write",
     "gist_attn_forward", "gist_attn_forward_last", "gist_attn_forward_paged",
+    "gist_attn_forward_paged_fp8",
     "gist_prefill_workspace_bytes",
     "gist_prefill_attn",
-    "paged_decode_workspace_bytes", "paged_decode_attn",
+    "paged_decode_workspace_bytes", "paged_decode_attn", "paged_decode_attn_fp8",
 ]
 
 _DTYPES = {torch.bfloat16: GIST_BF16, torch.float32: GIST_F32}
@@ -225,6 +226,40 @@ def gist_attn_forward_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, item_b
         ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], k, ptrs[3], kq, q_row0, P, Hq, H, d, ptrs[4],
         ptrs[5], ptrs[6], pos0, rope_base, scale, ptrs[7], _stream_ptr(stream)),
         "gist_attn_forward_paged")
+    return out
+
+
+def gist_attn_forward_paged_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                k_scale: torch.Tensor, v_scale: torch.Tensor,
+                                item_blocks: torch.Tensor, k: int, q: torch.Tensor,
+                                k_new: torch.Tensor, v_new: torch.Tensor,
+                                query_blocks: torch.Tensor | None = None, kq: int = 0,
+                                q_row0: int = 0, pos0: int | None = None,
+                                rope_base: float = 10000.0, scale: float | None = None,
+                                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """gist_attn_forward_paged over an fp8 cache: k_cache, v_cache uint8 E4M3
+    codes [n_blocks, H, block_size, d]; k_scale, v_scale fp32 [n_blocks, H];
+    q [P, Hq, d], k_new, v_new [P, H, d] bf16; returns out [P, Hq, d]."""
+    n_blocks, H, bs, d = k_cache.shape
+    P, Hq, _ = q.shape
+    if pos0 is None:
+        pos0 = k + kq + 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    bf = torch.bfloat16
+    ptrs = (_dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8, k_cache.shape),
+            _dev(k_scale, "k_scale", torch.float32, (n_blocks, H)),
+            _dev(v_scale, "v_scale", torch.float32, (n_blocks, H)),
+            _dev(item_blocks, "item_blocks", torch.int32, (P,)),
+            _dev(query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
+            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (P, H, d)), _dev(v_new, "v_new", bf, (P, H, d)),
+            _dev(out, "out", bf, q.shape))
+    _lib.check(_lib.lib().gist_attn_forward_paged_fp8(
+        ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], k, ptrs[5], kq, q_row0, P, Hq, H,
+        d, ptrs[6], ptrs[7], ptrs[8], pos0, rope_base, scale, ptrs[9], _stream_ptr(stream)),
+        "gist_attn_forward_paged_fp8")
     return out
 
 

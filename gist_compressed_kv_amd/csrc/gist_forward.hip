@@ -76,6 +76,9 @@ struct FwdArgs {
   const void* paged_v;
   int block_size;
   int q_row0;
+  // fp8 paged gist: one scale per (block, KV head) for K and one for V
+  const float* paged_kscales;
+  const float* paged_vscales;
 };
 
 // ---------------------------------------------------------------------------
@@ -771,13 +774,23 @@ gist_fwd_eos(const FwdArgs a) {
   // fp8: scales of the item and query gist (K, V); wave-uniform scalars
   float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
   if constexpr (FP8) {
-    const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
-    ski = si[g];
-    svi = si[a.H + g];
-    if (a.kq) {
-      const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
-      skq = sq[g];
-      svq = sq[a.H + g];
+    if (a.paged) {
+      // paged cache: the scales of the gists' blocks
+      ski = a.paged_kscales[(int64_t)item * a.H + g];
+      svi = a.paged_vscales[(int64_t)item * a.H + g];
+      if (a.kq) {
+        skq = a.paged_kscales[(int64_t)qid * a.H + g];
+        svq = a.paged_vscales[(int64_t)qid * a.H + g];
+      }
+    } else {
+      const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+      ski = si[g];
+      svi = si[a.H + g];
+      if (a.kq) {
+        const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+        skq = sq[g];
+        svq = sq[a.H + g];
+      }
     }
   }
   // eight gist elements -> eight bf16 (exact for E4M3 codes)
@@ -1412,14 +1425,15 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
                       qpool, q_ids, out, stream, false);
 }
 
-extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache,
-                                               int64_t n_blocks, int block_size,
-                                               const int32_t* item_blocks, int k,
-                                               const int32_t* query_blocks, int kq, int q_row0,
-                                               int P, int Hq, int H, int d, const void* q,
-                                               const void* k_new, const void* v_new, int pos0,
-                                               float rope_base, float scale, void* out,
-                                               void* stream) {
+namespace {
+// gist_attn_forward_paged (k_scale == v_scale == NULL: bf16 cache) and
+// gist_attn_forward_paged_fp8
+gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, bool fp8, int64_t n_blocks, int block_size,
+                               const int32_t* item_blocks, int k, const int32_t* query_blocks,
+                               int kq, int q_row0, int P, int Hq, int H, int d, const void* q,
+                               const void* k_new, const void* v_new, int pos0, float rope_base,
+                               float scale, void* out, void* stream) {
   clear_error();
   if (P < 0) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: P < 0");
   if (n_blocks < 1 || n_blocks > INT32_MAX || block_size < 1)
@@ -1440,8 +1454,11 @@ extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* 
   if (kq > 0 && !query_blocks)
     return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: query_blocks is NULL");
   if (P == 0) return GIST_OK;
-  if (!k_cache || !v_cache || !item_blocks || !q || !k_new || !v_new || !out)
+  if (!k_cache || !v_cache || !item_blocks || !q || !k_new || !v_new || !out ||
+      (fp8 && (!k_scale || !v_scale)))
     return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: NULL tensor argument");
+  if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3) != 0)
+    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: scales must be 4-byte aligned");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
       !aligned16(v_new) || !aligned16(out))
     return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: tensors must be 16-byte aligned");
@@ -1476,14 +1493,21 @@ extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* 
   a.paged_v = v_cache;
   a.block_size = block_size;
   a.q_row0 = q_row0;
+  a.paged_kscales = fp8 ? k_scale : nullptr;
+  a.paged_vscales = fp8 ? v_scale : nullptr;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
   const int kg = k + kq;
   const bool qu2 = a.G * (d / 16) > 64;
   auto go = [&](auto d_c, auto ngt_c) {
     constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
-    if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
+    if (fp8) {
+      if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
+    } else {
+      if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
+    }
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
@@ -1496,7 +1520,35 @@ extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* 
     if (kg <= 16) go(I128{}, I1{});
     else go(I128{}, I2{});
   }
-  return check_launch("gist_attn_forward_paged");
+  return check_launch(fp8 ? "gist_attn_forward_paged_fp8" : "gist_attn_forward_paged");
+}
+}  // namespace
+
+extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache,
+                                               int64_t n_blocks, int block_size,
+                                               const int32_t* item_blocks, int k,
+                                               const int32_t* query_blocks, int kq, int q_row0,
+                                               int P, int Hq, int H, int d, const void* q,
+                                               const void* k_new, const void* v_new, int pos0,
+                                               float rope_base, float scale, void* out,
+                                               void* stream) {
+  return attn_forward_paged(k_cache, v_cache, nullptr, nullptr, false, n_blocks, block_size,
+                            item_blocks, k, query_blocks, kq, q_row0, P, Hq, H, d, q, k_new,
+                            v_new, pos0, rope_base, scale, out, stream);
+}
+
+extern "C" gist_status gist_attn_forward_paged_fp8(const void* k_cache, const void* v_cache,
+                                                   const float* k_scale, const float* v_scale,
+                                                   int64_t n_blocks, int block_size,
+                                                   const int32_t* item_blocks, int k,
+                                                   const int32_t* query_blocks, int kq, int q_row0,
+                                                   int P, int Hq, int H, int d, const void* q,
+                                                   const void* k_new, const void* v_new, int pos0,
+                                                   float rope_base, float scale, void* out,
+                                                   void* stream) {
+  return attn_forward_paged(k_cache, v_cache, k_scale, v_scale, true, n_blocks, block_size,
+                            item_blocks, k, query_blocks, kq, q_row0, P, Hq, H, d, q, k_new,
+                            v_new, pos0, rope_base, scale, out, stream);
 }
 
 extern "C" gist_status gist_attn_forward_last(const gist_pool* pool, int layer,

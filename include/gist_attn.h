@@ -184,6 +184,29 @@ gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache, in
                                     void* out, void* stream);
 
 /*
+ * gist_attn_forward_paged_fp8 — gist_attn_forward_paged over a paged cache of
+ * fp8 codes (OCP FP8 E4M3, as paged_decode_attn_fp8) with one fp32 scale per
+ * (block, KV head) for K and one for V: the fp8 pool of [GIST] 收益有多大：存储
+ * in the block layout of [GIST] 能不能再进一步.  A block holding both gists
+ * gives them one scale per head.
+ *   k_cache, v_cache  device uint8 codes [n_blocks][H][block_size][d], 16-byte
+ *                     aligned; element = decode(code) * k_scale[block][head]
+ *                     (resp. v_scale)
+ *   k_scale, v_scale  device fp32 [n_blocks][H], 4-byte aligned
+ * q, k_new, v_new and out are bf16; every other argument, limit and error
+ * behaviour is that of gist_attn_forward_paged.  A key's K scale multiplies
+ * its fp32 logit and its V scale its softmax weight.
+ */
+gist_status gist_attn_forward_paged_fp8(const void* k_cache, const void* v_cache,
+                                        const float* k_scale, const float* v_scale,
+                                        int64_t n_blocks, int block_size,
+                                        const int32_t* item_blocks, int k,
+                                        const int32_t* query_blocks, int kq, int q_row0, int P,
+                                        int Hq, int H, int d, const void* q, const void* k_new,
+                                        const void* v_new, int pos0, float rope_base, float scale,
+                                        void* out, void* stream);
+
+/*
  * gist_attn_forward_last — gist_attn_forward for the last query token of
  * each pair only.  At the final layer the relevance score reads only the
  * last position ([GIST] 在线的一次 attention: the score head is applied to

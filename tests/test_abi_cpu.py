@@ -287,3 +287,23 @@ def test_paged_gist_validation(L):
     assert _pg(L, ptr=ctypes.c_void_p((1 << 20) + 4)) == _lib.GIST_ERR_INVALID_ARG
     assert _pg(L, P=0, ptr=None) == _lib.GIST_OK
     assert _pg(L, kq=0, qb=None, P=0, ptr=None) == _lib.GIST_OK
+
+
+def _pg8(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE,
+         ks=FAKE, vs=FAKE):
+    return L.gist_attn_forward_paged_fp8(ptr, ptr, ks, vs, nblk, bs, ptr, k, qb, kq, q_row0, P, Hq,
+                                         H, d, ptr, ptr, ptr, k + kq + 1, 1e4, 0.125, ptr, None)
+
+
+def test_paged_gist_fp8_validation(L):
+    # the checks of the bf16 entry point, plus the two scale arrays
+    assert _pg8(L, P=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg8(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg8(L, Hq=34) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg8(L, k=17) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg8(L, bs=64, k=20, kq=20, q_row0=20) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg8(L, ks=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg8(L, vs=None) == _lib.GIST_ERR_INVALID_ARG
+    assert _pg8(L, vs=ctypes.c_void_p((1 << 20) + 2)) == _lib.GIST_ERR_INVALID_ARG
+    assert "4-byte" in L.gist_last_error().decode()
+    assert _pg8(L, P=0, ptr=None, ks=None, vs=None) == _lib.GIST_OK

@@ -6,6 +6,8 @@ full-size workloads (100k-item pools, 24/28/32 layers) are checked on
 seeded samples of pairs/requests, every head and token of each.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -770,6 +772,85 @@ def test_paged_gist_eos_equals_pooled(shape):
     err = float(np.abs(f64(paged) - ref).max())
     say(f"paged gist {shape}: max-abs err {err:.3g}")
     assert err <= 2e-2
+
+
+def _paged_fp8_from_case(case, bs):
+    """The case's layer-0 fp8 gists in a paged fp8 cache: item gist of pair p
+    in rows 0..k-1 of block 2p, query gist in rows 0.. of block 2p+1, each
+    block with its gist's (K, V) scales per head."""
+    P, h, d, k, kq = case.pairs, case.h, case.d, case.k, case.kq
+    kc = torch.zeros((2 * P, h, bs, d), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.ones((2 * P, h), dtype=torch.float32, device="cuda")
+    vs = torch.ones_like(ks)
+    ib = torch.arange(P, device="cuda") * 2
+    qb = ib + 1
+    ids = case.ids.long()
+    kc[ib, :, :k], vc[ib, :, :k] = case.pool.codes[0, ids, 0], case.pool.codes[0, ids, 1]
+    ks[ib], vs[ib] = case.pool.scales[0, ids, 0], case.pool.scales[0, ids, 1]
+    if kq:
+        qids = case.q_ids.long()
+        kc[qb, :, :kq], vc[qb, :, :kq] = case.qpool.codes[0, qids, 0], case.qpool.codes[0, qids, 1]
+        ks[qb], vs[qb] = case.qpool.scales[0, qids, 0], case.qpool.scales[0, qids, 1]
+    return kc, vc, ks, vs, ib.to(torch.int32), qb.to(torch.int32)
+
+
+@pytest.mark.parametrize("shape", [s for s in PAGED_GIST_SHAPES if not s[7]],
+                         ids=lambda s: "k%d_kq%d_hq%d_h%d_d%d_p%d_bs%d" % s[:7])
+def test_paged_gist_fp8_equals_pooled_fp8(shape):
+    import gist_compressed_kv_amd as G
+    k, kq, hq, h, d, P, bs, _ = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 11, k, 1, hq, h, d, P, torch.bfloat16, 940 + k + kq + hq, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    pooled = case.run(0)
+    kc, vc, ks, vs, ib, qb = _paged_fp8_from_case(case, bs)
+    paged = G.gist_attn_forward_paged_fp8(kc, vc, ks, vs, ib, k, case.q[0][:, 0].contiguous(),
+                                          case.kn[0][:, 0], case.vn[0][:, 0],
+                                          query_blocks=qb if kq else None, kq=kq, pos0=case.pos0,
+                                          scale=case.scale)
+    torch.cuda.synchronize()
+    # the same kernel reads the same codes and scales through other addresses
+    assert torch.equal(paged, pooled[:, 0])
+
+
+def test_paged_gist_fp8_one_block_matches_oracle():
+    # item and query gist in one 16-row block share that block's scales
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    P, k, kq, hq, h, d, bs = 9, 8, 8, 32, 4, 128, 16
+    kc, ks = synth.randn_fp8_blocks((P + 3, h, bs, d), 951, "cuda")
+    vc, vs = synth.randn_fp8_blocks((P + 3, h, bs, d), 952, "cuda")
+    ib = torch.tensor([(5 * p + 2) % (P + 3) for p in range(P)], dtype=torch.int32, device="cuda")
+    q = synth.randn((P, hq, d), 953, torch.bfloat16, "cuda")
+    kn = synth.randn((P, h, d), 954, torch.bfloat16, "cuda")
+    vn = synth.randn((P, h, d), 955, torch.bfloat16, "cuda")
+    pos0, scale = k + kq + 1, 1.0 / math.sqrt(d)
+    out = G.gist_attn_forward_paged_fp8(kc, vc, ks, vs, ib, k, q, kn, vn, query_blocks=ib, kq=kq,
+                                        q_row0=k, pos0=pos0, scale=scale)
+    torch.cuda.synchronize()
+    kf = O.dequantize_blocks(kc.cpu().numpy(), ks.cpu().numpy())
+    vf = O.dequantize_blocks(vc.cpu().numpy(), vs.cpu().numpy())
+    pool, qpool = O.paged_gist_pools(kf, vf, ib.cpu().numpy(), k, ib.cpu().numpy(), kq, k)
+    ref = O.gist_attn_forward(pool, 0, np.arange(P), f64(q)[:, None], f64(kn)[:, None],
+                              f64(vn)[:, None], pos0, ROPE_BASE, scale, qpool=qpool,
+                              q_ids=np.arange(P))[:, 0]
+    err = float(np.abs(f64(out) - ref).max())
+    say(f"paged fp8 gist, one block: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+def test_paged_gist_fp8_bad_block_gives_nan_rows():
+    import gist_compressed_kv_amd as G
+    case = GistCase(1, 11, 8, 1, 16, 2, 64, 4, torch.bfloat16, 960, kq=8, n_qrows=3,
+                    q_ids=torch.tensor([0, 1, 2, 0]), fp8=True)
+    kc, vc, ks, vs, ib, qb = _paged_fp8_from_case(case, 16)
+    ib[1] = 99
+    qb[2] = -1
+    o = f64(G.gist_attn_forward_paged_fp8(kc, vc, ks, vs, ib, 8, case.q[0][:, 0].contiguous(),
+                                          case.kn[0][:, 0], case.vn[0][:, 0], query_blocks=qb, kq=8))
+    torch.cuda.synchronize()
+    assert np.isnan(o[[1, 2]]).all() and np.isfinite(o[[0, 3]]).all()
 
 
 def test_paged_gist_bad_block_gives_nan_rows():
