@@ -72,8 +72,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
                     choices=["24L_b500", "24L_b500_last", "24L_b2000", "1L_b500", "wide_ell64",
-                             "wide_eos",
-                             "wide_eos_fp8", "paged", "paged_fp8", "prefill", "copy"])
+                             "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
+                             "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
@@ -365,6 +365,7 @@ def main():
     last_layer_eos = args.workload == "24L_b500_last"
     wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500, "24L_b2000": synth.L24_B2000,
           "1L_b500": synth.SINGLE_LAYER, "wide_ell64": synth.WIDE_ELL64,
+          "wide_ell64_fp8": synth.WIDE_ELL64_FP8,
           "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
     dev = "cuda"
     torch.cuda.init()
@@ -481,7 +482,7 @@ def main():
             "kernel": "gist_fwd_mfma<64> (23 full layers + 1 last-token layer; pass bytes / "
                       "launches)" if last_layer_eos else
                       "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
-                      ("gist_fwd_mfma<128>" if wl.ell > 1 else
+                      (("gist_fwd_mfma<128, fp8 gist>" if wl.fp8 else "gist_fwd_mfma<128>") if wl.ell > 1 else
                        ("gist_fwd_eos<128, fp8 gist>" if wl.fp8 else "gist_fwd_eos<128>")),
             "achieved": achieved_gbps,
             "peak": HBM_PEAK_GBPS,

@@ -190,12 +190,11 @@ struct MfmaLds {
 // per pair).  The keys are staged as for every token; every wave takes the
 // 16-token block that holds the last token and the group's heads are spread
 // over the four waves (head h on wave h mod 4), each storing that token alone.
-// FP8: the gist pools hold E4M3 codes.  They are decoded exactly into the bf16
-// rows of LDS; the K scale of a gist key multiplies its fp32 logit, and the V
-// scale its softmax weight in the P·V product (the row sum takes the unscaled
-// weight).
+// FP8: the gist pools hold E4M3 codes.  Each staged gist element is the
+// decoded code times its block's scale, rounded to bf16 once; the rest of the
+// kernel is the bf16 one.
 template <int D, int NKT, int QPF, int GT, bool LAST, bool FP8>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && !FP8 ? 4 : 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
 gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
   constexpr int KS = MfmaLds<D, NKT>::KS;
@@ -305,25 +304,6 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   if (a.kq)
     qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
          (int64_t)g * a.kq * D;
-  // eight channels from channel ch of key row j as bf16 (E4M3 codes decode
-  // exactly); the new rows are bf16 activations
-  auto load8 = [&](int j, bool v, int ch) -> uint4 {
-    if constexpr (FP8) {
-      if (j < kg) {
-        const C* row = j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
-                               : qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
-        const uint2 w = *(const uint2*)(row + ch);
-        float f[8];
-        decode4_e4m3(w.x, f);
-        decode4_e4m3(w.y, f + 4);
-        return pack8_bf16(f);
-      }
-      const bf16_t* base = (const bf16_t*)(v ? a.v_new : a.k_new);
-      return *(const uint4*)(base + (((int64_t)p * a.ell + (j - kg)) * a.H + g) * D + ch);
-    } else {
-      return *(const uint4*)(key_row(a, gK, qK, p, g, j, kg, D, v) + ch);
-    }
-  };
   // fp8: K and V scales of the item gist and of the query gist (scalars)
   float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
   if constexpr (FP8) {
@@ -336,7 +316,35 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       svq = sq[a.H + g];
     }
   }
-
+  // eight channels from channel ch of key row j as bf16.  fp8 gist rows are
+  // decoded, multiplied by their block's scale in fp32 and rounded to bf16
+  // once, so past the staging the kernel runs as over a bf16 pool; the new
+  // rows are bf16 activations.  With fp8 pools every lane still issues one
+  // 16-byte load, from its gist row or its new row (the address is the only
+  // per-lane choice), so the staging loads stay unconditional: a gist lane
+  // reads the aligned 16 codes that hold its 8 and decodes its half.
+  auto load8 = [&](int j, bool v, int ch) -> uint4 {
+    if constexpr (FP8) {
+      typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+      const bool gist = j < kg;
+      const C* grow = j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
+                      : (a.kq && gist) ? qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D
+                                       : gK;
+      const bf16_t* nrow = (const bf16_t*)(v ? a.v_new : a.k_new) +
+                           (((int64_t)p * a.ell + (gist ? 0 : j - kg)) * a.H + g) * D;
+      const u4_t raw = *(const u4_t*)(gist ? (const void*)(grow + (ch & ~15)) : (const void*)(nrow + ch));
+      const float sc = j < a.k ? (v ? svi : ski) : (v ? svq : skq);
+      float f[8];
+      decode4_e4m3((ch & 8) ? raw.z : raw.x, f);
+      decode4_e4m3((ch & 8) ? raw.w : raw.y, f + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] *= sc;
+      const uint4 dec = pack8_bf16(f);
+      return gist ? dec : make_uint4(raw.x, raw.y, raw.z, raw.w);
+    } else {
+      return *(const uint4*)(key_row(a, gK, qK, p, g, j, kg, D, v) + ch);
+    }
+  };
   // ---- issue every staging load of this thread ----------------------------
   // Every load below is unconditional (out-of-range units read row 0 and
   // are zeroed afterwards), so the compiler can count the loads in flight
@@ -530,16 +538,6 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
               const bf16x8_t kf = *(const bf16x8_t*)(kbase + 16 * KS * j + 32 * s);
               acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
             }
-            if constexpr (FP8) {
-              // slot r of lane group q4 is key 16*(nkt-1-j) + 15 - 4*q4 - r;
-              // every tile takes a factor per slot (1 past the gist), with
-              // selects rather than a branch around the MFMA results
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int key = 16 * (nkt - 1 - j) + 15 - 4 * q4 - r;
-                acc[r] *= key < a.k ? ski : (key < kg ? skq : 1.f);
-              }
-            }
             sacc[j] = acc;
             mx = vmax3(mx, acc[0], acc[1]);
             mx = vmax3(mx, acc[2], acc[3]);
@@ -566,21 +564,10 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
             const uint2 pk = make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]));
             const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
             lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
-            // the weights of the product with V; fp8: a gist key's weight
-            // carries its V scale
-            bf16x4v pv = pf;
-            if constexpr (FP8) {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int key = 16 * (nkt - 1 - j) + 15 - 4 * q4 - r;
-                w[r] *= key < a.k ? svi : (key < kg ? svq : 1.f);
-              }
-              pv = __builtin_bit_cast(bf16x4v, make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3])));
-            }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
               const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pv, o[dt], 0, 0, 0);
+              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
             }
           }
         }
@@ -1331,7 +1318,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     if (fp8) {
       // fp8 pools: the instances with the group size taken from the arguments
       if (d == 64 && nkt <= 5)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 0, L, true>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, true>), grid, dim3(256),
                            (MfmaLds<64, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
       else if (d == 64)
         hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, true>), grid, dim3(256),
@@ -1340,7 +1327,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
         hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, true>), grid, dim3(256),
                            (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
       else
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 1, 0, L, true>), grid, dim3(256),
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, true>), grid, dim3(256),
                            (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
       return;
     }

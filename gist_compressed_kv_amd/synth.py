@@ -191,6 +191,10 @@ WIDE_EOS_FP8 = GistWorkload("28 layers, Hq=64, H=8, d=128, item gist k=8 + query
                             "scales, bf16 activations", 28, 100_000, 8, 1, 64, 8, 128, 2000, 40,
                             torch.bfloat16, 7, kq=8, fp8=True)
 
+WIDE_ELL64_FP8 = GistWorkload("28 layers, Hq=64, H=8, d=128, k=8, ell=64, 2000 pairs, 100k-item "
+                              "pool as fp8 E4M3 with per-(item, K/V, head) scales, bf16 activations",
+                              28, 100_000, 8, 64, 64, 8, 128, 2000, 40, torch.bfloat16, 9, fp8=True)
+
 PAGED_FP8 = DecodeWorkload("paged decode, fp8 E4M3 cache with per-(block, head) scales: 32 requests "
                            "x 4096 cached tokens in 256-token blocks, Hq=H=32, d=128, 32 layers, "
                            "bf16 activations", 32, 32, 4096, 256, 32, 32, 128, torch.bfloat16, 6)

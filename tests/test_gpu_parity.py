@@ -157,6 +157,14 @@ def test_wide_ell64_workload_sampled():
     check_gist(case, sample=sample, label="wide ell=64, 2000 pairs (sampled)")
 
 
+def test_wide_ell64_fp8_workload_sampled():
+    wl = synth.WIDE_ELL64_FP8
+    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
+                    ids=_ids(wl), fp8=True)
+    sample = np.array([0, 1, 777, wl.pairs - 1])
+    check_gist(case, sample=sample, label="wide ell=64 over fp8 pools, 2000 pairs (sampled)")
+
+
 def test_wide_eos_query_gist_workload():
     wl = synth.WIDE_EOS
     qids = torch.arange(wl.pairs) // (wl.pairs // wl.queries)
