@@ -144,10 +144,12 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  * GIST_FP8_E4M3 pools: q, k_new, v_new and out are bf16 and qpool must be
  * fp8 too.  The MFMA shapes (2 <= ell <= 64, k + k' + ell <= 128) and the
  * EOS shapes (ell == 1, Hq / H <= 16, k + k' <= 32) are implemented; other
- * shapes return GIST_ERR_UNSUPPORTED.  Every E4M3 value is a bf16 value, so
- * the codes enter the matrix products exactly; a key's K scale multiplies
- * its fp32 logit and its V scale its softmax weight in the product with V
- * (the softmax denominator takes the unscaled weight).
+ * shapes return GIST_ERR_UNSUPPORTED.  Every E4M3 value is a bf16 value.
+ * With ell == 1 the codes enter the matrix products exactly, a key's K scale
+ * multiplies its fp32 logit and its V scale its softmax weight in the product
+ * with V (the softmax denominator takes the unscaled weight).  With ell >= 2
+ * each gist element, decode(code) * scale in fp32, is rounded to bf16 once
+ * as it is staged.
  */
 gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                               int ell, int Hq, const void* q, const void* k_new,
