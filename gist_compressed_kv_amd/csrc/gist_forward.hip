@@ -348,8 +348,8 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // ---- issue every staging load of this thread ----------------------------
   // Every load below is unconditional (out-of-range units read row 0 and
   // are zeroed afterwards), so the compiler can count the loads in flight
-  // exactly and later waits never have to drain the Q prefetch (bf16 pools;
-  // fp8 gist rows take a load of their own).
+  // exactly and later waits never have to drain the Q prefetch (with fp8
+  // pools too: load8 issues one load per unit whichever row it reads).
   uint4 klo[IT], khi[IT], v0[IT], v1[IT];
   const int npairs = nk_pad >> 1;
 #pragma unroll
