@@ -68,6 +68,8 @@ MFMA_SHAPES = [
     (63, 5, 0, 7, 1, 64, 2),
     (64, 24, 0, 32, 1, 128, 2),
     (48, 8, 0, 16, 2, 64, 5),
+    # k + k' + ell exactly 128 with a query gist
+    (64, 32, 32, 8, 2, 64, 2),
 ]
 
 
@@ -96,12 +98,18 @@ VALU_SHAPES = [
     (1, 8, 8, 64, 8, 128, 4, torch.bfloat16),
     (1, 8, 8, 8, 4, 64, 4, torch.bfloat16),
     (1, 3, 0, 3, 1, 128, 3, torch.bfloat16),
+    # the EOS kernel at both of its limits: k + k' = 32 and G = 16
+    (1, 16, 16, 16, 1, 64, 3, torch.bfloat16),
     (100, 8, 0, 14, 2, 64, 2, torch.bfloat16),
     (70, 64, 0, 4, 2, 128, 2, torch.bfloat16),
     (1, 8, 0, 14, 2, 64, 3, torch.float32),
     (7, 8, 8, 16, 2, 128, 3, torch.float32),
     (64, 8, 0, 14, 2, 64, 2, torch.float32),
     (5, 2, 0, 32, 1, 64, 2, torch.float32),
+    # one past the MFMA kernel's ell limit, and the largest ell accepted
+    (65, 8, 0, 14, 2, 64, 2, torch.bfloat16),
+    (1024, 8, 0, 4, 1, 64, 1, torch.bfloat16),
+    (1024, 64, 0, 2, 1, 128, 1, torch.float32),
 ]
 
 
