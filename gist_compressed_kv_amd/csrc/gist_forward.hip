@@ -376,7 +376,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     const int wraw = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tpos = tid & 63;
     if (tpos < ell) {
-      const double pos = (double)(a.pos0 + tpos);
+      const double pos = (double)a.pos0 + tpos;  // no int32 overflow near INT_MAX
 #pragma unroll
       for (int k = 0; k < D / 8; ++k) {
         const int i = wraw * (D / 8) + k;
@@ -1072,7 +1072,7 @@ gist_fwd_valu(const FwdArgs a) {
   // query rotation at pos0 + t for this lane's channel pairs
   float qcs[E2], qsn[E2];
 #pragma unroll
-  for (int e = 0; e < E2; ++e) rope_cos_sin((double)(a.pos0 + t), a.freqs.rev[lo + e], qcs[e], qsn[e]);
+  for (int e = 0; e < E2; ++e) rope_cos_sin((double)a.pos0 + t, a.freqs.rev[lo + e], qcs[e], qsn[e]);
 
   float qv[MAXH][2 * E2];
   float m[MAXH], l[MAXH], o[MAXH][2 * E2];
@@ -1123,7 +1123,7 @@ gist_fwd_valu(const FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < E2; ++e) {
           float cs = qcs[e], sn = qsn[e];
-          if (tj != t) rope_cos_sin((double)(a.pos0 + tj), a.freqs.rev[lo + e], cs, sn);
+          if (tj != t) rope_cos_sin((double)a.pos0 + tj, a.freqs.rev[lo + e], cs, sn);
           const float xl = kv[e], xh = kv[E2 + e];
           kv[e] = __builtin_fmaf(xl, cs, -(xh * sn));
           kv[E2 + e] = __builtin_fmaf(xh, cs, xl * sn);

@@ -53,7 +53,7 @@ pool_write_kernel(T* __restrict__ pool, int64_t layer_off, int64_t N, int k, int
   const int64_t kdst = ((int64_t)g * k + j) * d;
   const int64_t vdst = ((int64_t)(H + g) * k + j) * d;
   const int half = d / 2;
-  const double shift = (double)(1 - src_pos0);
+  const double shift = 1.0 - (double)src_pos0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int lo = 4 * c + e, hi = half + 4 * c + e;
@@ -129,7 +129,7 @@ pool_write_fp8_kernel(uint8_t* __restrict__ codes, float* __restrict__ scales, i
   const bool rotate = kv == 0 && src_pos0 != 1;
   const int chunks = d / 8, half = d / 2;
   const int units = k * chunks;
-  const double shift = (double)(1 - src_pos0);
+  const double shift = 1.0 - (double)src_pos0;
 
   auto values = [&](int u, float* yl, float* yh) {
     const int j = u / chunks, c = u - (u / chunks) * chunks;

@@ -102,7 +102,8 @@ gist_status gist_pool_destroy(gist_pool* pool);
  *            ids are skipped on the device)
  *   k_src    device [n][k][H][d], pool dtype; row i rotated at position
  *            src_pos0 + i.  It is re-rotated to the canonical position 1 + i
- *            (a rotation by 1 - src_pos0; a plain copy when src_pos0 == 1).
+ *            (a rotation by 1 - src_pos0, formed in double, so any int
+ *            src_pos0 is valid; a plain copy when src_pos0 == 1).
  *   v_src    device [n][k][H][d], pool dtype, copied unchanged.
  *   rope_base RoPE base used for the re-rotation.
  * Duplicate ids in one call race (one of the writes wins).  n == 0 is a no-op.
@@ -132,7 +133,9 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  *   k_new     device [P][ell][H][d]   (not yet rotated)
  *   v_new     device [P][ell][H][d]
  *   pos0      position of the first new token: k + 1 (k + k' + 1 with a
- *             query gist), so the query-to-gist distance matches training
+ *             query gist), so the query-to-gist distance matches training.
+ *             Any int: positions pos0 + t are formed in double, so they may
+ *             run past 2^31 - 1.
  *   scale     softmax scale, normally 1/sqrt(d)
  *   qpool     optional query-gist pool (same L, H, d, dtype); NULL for none
  *   q_ids     device int32 [P] rows of qpool (ignored when qpool is NULL)

@@ -301,6 +301,57 @@ def test_pool_write_matches_oracle(dtype, src_pos0):
 
 
 # ---------------------------------------------------------------------------
+# Positions at the int32 limit: the kernels form pos0 + t (and the pool
+# writer 1 - src_pos0) in double, so positions past 2^31 - 1 are rotated by
+# their true angle, as the oracle does with int64 positions.
+# ---------------------------------------------------------------------------
+
+INT32_MAX = 2 ** 31 - 1
+
+
+@pytest.mark.parametrize("ell,last", [(16, False), (16, True), (100, False), (100, True), (1, False)],
+                         ids=["mfma", "mfma_last", "valu", "valu_last", "eos"])
+def test_positions_past_int32_limit(ell, last):
+    case = GistCase(1, 5, 8, ell, 14, 2, 64, 3, torch.bfloat16, 900 + ell)
+    case.pos0 = INT32_MAX - ell // 2  # the last positions lie past 2^31 - 1
+    if not last:
+        check_gist(case, label=f"pos0 {case.pos0}, ell {ell}")
+        return
+    out = case.run_last(0)
+    torch.cuda.synchronize()
+    ref = case.oracle(0, np.arange(case.pairs))[:, -1]
+    err = float(np.abs(f64(out) - ref).max())
+    say(f"pos0 {case.pos0}, ell {ell}, last token: max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_pool_write_at_int32_min_position(dtype):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    L, N, k, h, d, n = 1, 4, 8, 2, 64, 3
+    src_pos0 = -2 ** 31  # re-rotation by 1 - src_pos0 = 2^31 + 1
+    pool_t = torch.zeros((L, N, 2, h, k, d), dtype=dtype, device="cuda")
+    pool = G.GistPool(pool_t)
+    ids = torch.tensor([2, 0, 3], dtype=torch.int32, device="cuda")
+    ks = synth.randn((n, k, h, d), 510, dtype, "cuda")
+    vs = synth.randn((n, k, h, d), 511, dtype, "cuda")
+    G.gist_pool_write(pool, 0, ids, ks, vs, src_pos0=src_pos0, rope_base=10000.0)
+    torch.cuda.synchronize()
+    ref = O.pool_write(np.zeros((L, N, 2, h, k, d)), 0, ids.cpu().numpy(), f64(ks), f64(vs),
+                       src_pos0, 10000.0)
+    got = f64(pool_t)
+    if dtype == torch.float32:
+        # the angle (2^31 + 1) * theta carries up to 2^-52 of itself in fp64
+        # on either side: 2^-51 * 2^31 rad per unit of |x|, on top of the 1e-6
+        # of the fp32 rotation at small angles
+        tol = 1e-6 + 2.0 ** -51 * (2.0 ** 31 + 1) * np.abs(f64(ks)).max()
+    else:
+        tol = 2.0 ** -8 * np.abs(ref).max()
+    assert np.abs(got - ref).max() <= tol
+
+
+# ---------------------------------------------------------------------------
 # Robustness: peaky softmax (Q scaled by 8) and outlier K channels (x10).
 # The oracle reads the same scaled device tensors back.  With logits this
 # large, rounding the rotated Q and new K to bf16 (what the MFMA operands
