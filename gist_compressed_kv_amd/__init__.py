@@ -41,17 +41,35 @@ def _stream_ptr(stream) -> int:
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    # dtype and shape first: the library reads every tensor at the extents
+    # its sizes imply, so a mismatch must never reach it
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must live on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
     return t.data_ptr()
+
+
+def _ptrs(*specs):
+    """Device pointers of a call's tensors, each spec (tensor, name, dtype,
+    shape) or None (passed on as None).  Types, dtypes, shapes and contiguity
+    of all of them are checked before any is required to be on the GPU."""
+    for sp in specs:
+        if sp is not None:
+            t, name, dtype, shape = (tuple(sp) + (None, None))[:4]
+            if not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name} must be a torch.Tensor")
+            if dtype is not None and t.dtype != dtype:
+                raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+            if shape is not None and tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return tuple(None if sp is None else _dev(*sp) for sp in specs)
 
 
 def gist_pool_bytes(L: int, N: int, k: int, H: int, d: int, dtype) -> int:
@@ -129,8 +147,8 @@ def gist_pool_write(pool: GistPool, layer: int, ids: torch.Tensor, k_src: torch.
                     stream=None) -> None:
     n = ids.numel()
     shape = (n, pool.k, pool.H, pool.d)
-    args = (_dev(ids, "ids", torch.int32), _dev(k_src, "k_src", pool.act_dtype, shape),
-            _dev(v_src, "v_src", pool.act_dtype, shape))
+    args = _ptrs((ids, "ids", torch.int32), (k_src, "k_src", pool.act_dtype, shape),
+                 (v_src, "v_src", pool.act_dtype, shape))
     _lib.check(_lib.lib().gist_pool_write(pool.handle, layer, args[0], n, args[1], args[2],
                                           src_pos0, rope_base, _stream_ptr(stream)),
                "gist_pool_write")
@@ -153,9 +171,9 @@ def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: tor
         out = torch.empty_like(q)
     kv_shape = (P, ell, pool.H, pool.d)
     dt = pool.act_dtype
-    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q, "q", dt),
-            _dev(k_new, "k_new", dt, kv_shape), _dev(v_new, "v_new", dt, kv_shape),
-            _dev(out, "out", dt, q.shape))
+    ptrs = _ptrs((item_ids, "item_ids", torch.int32, (P,)), (q, "q", dt, (P, ell, Hq, pool.d)),
+                 (k_new, "k_new", dt, kv_shape), (v_new, "v_new", dt, kv_shape),
+                 (out, "out", dt, q.shape))
     qh, qi = None, None
     if qpool is not None:
         qh = qpool.handle
@@ -185,9 +203,9 @@ def gist_attn_forward_last(pool: GistPool, layer: int, item_ids: torch.Tensor, q
         out = torch.empty_like(q_last)
     kv_shape = (P, ell, pool.H, pool.d)
     dt = pool.act_dtype
-    ptrs = (_dev(item_ids, "item_ids", torch.int32, (P,)), _dev(q_last, "q_last", dt),
-            _dev(k_new, "k_new", dt, kv_shape), _dev(v_new, "v_new", dt, kv_shape),
-            _dev(out, "out", dt, q_last.shape))
+    ptrs = _ptrs((item_ids, "item_ids", torch.int32, (P,)), (q_last, "q_last", dt, (P, Hq, pool.d)),
+                 (k_new, "k_new", dt, kv_shape), (v_new, "v_new", dt, kv_shape),
+                 (out, "out", dt, q_last.shape))
     qh, qi = None, None
     if qpool is not None:
         qh = qpool.handle
@@ -217,11 +235,11 @@ def gist_attn_forward_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, item_b
     if out is None:
         out = torch.empty_like(q)
     bf = torch.bfloat16
-    ptrs = (_dev(k_cache, "k_cache", bf), _dev(v_cache, "v_cache", bf, k_cache.shape),
-            _dev(item_blocks, "item_blocks", torch.int32, (P,)),
-            _dev(query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
-            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (P, H, d)), _dev(v_new, "v_new", bf, (P, H, d)),
-            _dev(out, "out", bf, q.shape))
+    ptrs = _ptrs((k_cache, "k_cache", bf), (v_cache, "v_cache", bf, k_cache.shape),
+                 (item_blocks, "item_blocks", torch.int32, (P,)),
+                 (query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
+                 (q, "q", bf, (P, Hq, d)), (k_new, "k_new", bf, (P, H, d)), (v_new, "v_new", bf, (P, H, d)),
+                 (out, "out", bf, q.shape))
     _lib.check(_lib.lib().gist_attn_forward_paged(
         ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], k, ptrs[3], kq, q_row0, P, Hq, H, d, ptrs[4],
         ptrs[5], ptrs[6], pos0, rope_base, scale, ptrs[7], _stream_ptr(stream)),
@@ -249,13 +267,13 @@ def gist_attn_forward_paged_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
     if out is None:
         out = torch.empty_like(q)
     bf = torch.bfloat16
-    ptrs = (_dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8, k_cache.shape),
-            _dev(k_scale, "k_scale", torch.float32, (n_blocks, H)),
-            _dev(v_scale, "v_scale", torch.float32, (n_blocks, H)),
-            _dev(item_blocks, "item_blocks", torch.int32, (P,)),
-            _dev(query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
-            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (P, H, d)), _dev(v_new, "v_new", bf, (P, H, d)),
-            _dev(out, "out", bf, q.shape))
+    ptrs = _ptrs((k_cache, "k_cache", torch.uint8), (v_cache, "v_cache", torch.uint8, k_cache.shape),
+                 (k_scale, "k_scale", torch.float32, (n_blocks, H)),
+                 (v_scale, "v_scale", torch.float32, (n_blocks, H)),
+                 (item_blocks, "item_blocks", torch.int32, (P,)),
+                 (query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
+                 (q, "q", bf, (P, Hq, d)), (k_new, "k_new", bf, (P, H, d)), (v_new, "v_new", bf, (P, H, d)),
+                 (out, "out", bf, q.shape))
     _lib.check(_lib.lib().gist_attn_forward_paged_fp8(
         ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], k, ptrs[5], kq, q_row0, P, Hq, H,
         d, ptrs[6], ptrs[7], ptrs[8], pos0, rope_base, scale, ptrs[9], _stream_ptr(stream)),
@@ -293,9 +311,9 @@ def gist_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_sta
         workspace = torch.empty(max(gist_prefill_workspace_bytes(T, H, d), 16), dtype=torch.uint8,
                                 device=q.device)
     bf = torch.bfloat16
-    ptrs = (_dev(q, "q", bf), _dev(k, "k", bf, (T, H, d)), _dev(v, "v", bf, (T, H, d)),
-            _dev(seq_start, "seq_start", torch.int32), _dev(out, "out", bf, q.shape),
-            _dev(workspace, "workspace"))
+    ptrs = _ptrs((q, "q", bf), (k, "k", bf, (T, H, d)), (v, "v", bf, (T, H, d)),
+                 (seq_start, "seq_start", torch.int32), (out, "out", bf, q.shape),
+                 (workspace, "workspace"))
     ph, ids = None, None
     if pool is not None:
         ph = pool.handle
@@ -321,7 +339,9 @@ def paged_decode_attn(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table:
     q [R, Hq, d]; k_new, v_new [R, H, d]; returns out [R, Hq, d]."""
     n_blocks, H, bs, d = k_cache.shape
     R, Hq, _ = q.shape
-    max_blocks = block_table.shape[1] if block_table.dim() == 2 else 0
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [R, max_blocks]")
+    max_blocks = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -330,12 +350,12 @@ def paged_decode_attn(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table:
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     dt = k_cache.dtype
-    ptrs = (_dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt, k_cache.shape),
-            _dev(block_table, "block_table", torch.int32), _dev(context_lens, "context_lens",
-                                                               torch.int32, (R,)),
-            _dev(q, "q", dt), _dev(k_new, "k_new", dt, (R, H, d)), _dev(v_new, "v_new", dt, (R, H, d)),
-            _dev(positions, "positions", torch.int32, (R,)), _dev(out, "out", dt, q.shape),
-            _dev(workspace, "workspace"))
+    ptrs = _ptrs((k_cache, "k_cache", dt), (v_cache, "v_cache", dt, k_cache.shape),
+                 (block_table, "block_table", torch.int32, (R, max_blocks)),
+                 (context_lens, "context_lens", torch.int32, (R,)),
+                 (q, "q", dt, (R, Hq, d)), (k_new, "k_new", dt, (R, H, d)), (v_new, "v_new", dt, (R, H, d)),
+                 (positions, "positions", torch.int32, (R,)), (out, "out", dt, q.shape),
+                 (workspace, "workspace"))
     _lib.check(_lib.lib().paged_decode_attn(
         ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], max_blocks, ptrs[3], R, ptrs[4], ptrs[5], ptrs[6],
         ptrs[7], Hq, H, d, _code(dt), rope_base, scale, ptrs[8], ptrs[9],
@@ -354,7 +374,9 @@ def paged_decode_attn_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale:
     fp32 [n_blocks, H]; q [R, Hq, d], k_new, v_new [R, H, d] bf16; returns out [R, Hq, d]."""
     n_blocks, H, bs, d = k_cache.shape
     R, Hq, _ = q.shape
-    max_blocks = block_table.shape[1] if block_table.dim() == 2 else 0
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [R, max_blocks]")
+    max_blocks = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -363,14 +385,14 @@ def paged_decode_attn_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale:
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     bf = torch.bfloat16
-    ptrs = (_dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8, k_cache.shape),
-            _dev(k_scale, "k_scale", torch.float32, (n_blocks, H)),
-            _dev(v_scale, "v_scale", torch.float32, (n_blocks, H)),
-            _dev(block_table, "block_table", torch.int32),
-            _dev(context_lens, "context_lens", torch.int32, (R,)),
-            _dev(q, "q", bf), _dev(k_new, "k_new", bf, (R, H, d)), _dev(v_new, "v_new", bf, (R, H, d)),
-            _dev(positions, "positions", torch.int32, (R,)), _dev(out, "out", bf, q.shape),
-            _dev(workspace, "workspace"))
+    ptrs = _ptrs((k_cache, "k_cache", torch.uint8), (v_cache, "v_cache", torch.uint8, k_cache.shape),
+                 (k_scale, "k_scale", torch.float32, (n_blocks, H)),
+                 (v_scale, "v_scale", torch.float32, (n_blocks, H)),
+                 (block_table, "block_table", torch.int32, (R, max_blocks)),
+                 (context_lens, "context_lens", torch.int32, (R,)),
+                 (q, "q", bf, (R, Hq, d)), (k_new, "k_new", bf, (R, H, d)), (v_new, "v_new", bf, (R, H, d)),
+                 (positions, "positions", torch.int32, (R,)), (out, "out", bf, q.shape),
+                 (workspace, "workspace"))
     _lib.check(_lib.lib().paged_decode_attn_fp8(
         ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], max_blocks, ptrs[5], R, ptrs[6],
         ptrs[7], ptrs[8], ptrs[9], Hq, H, d, rope_base, scale, ptrs[10], ptrs[11],
