@@ -833,3 +833,45 @@ def test_paged_gist_pools_round_trip_and_attention():
     assert np.array_equal(gp1, pool) and np.array_equal(gq1, qpool)
     gp0, gq0 = O.paged_gist_pools(kc, vc, ib, k, None, 0, 0)
     assert gq0 is None and np.array_equal(gp0, pool)
+
+
+# ---------------------------------------------------------------------------
+# Direct pins of the mask and gather helpers (also covered through the
+# attention pins above)
+# ---------------------------------------------------------------------------
+
+
+def test_causal_mask_is_torch_tril():
+    for n in (1, 2, 7, 64):
+        want = torch.tril(torch.ones(n, n, dtype=torch.bool)).numpy()
+        assert np.array_equal(O.causal_mask(n), want)
+
+
+def test_gist_online_mask_is_the_training_mask_seen_from_the_query():
+    # [GIST] 论文做了什么: the sequence [item ; gist ; query] is causal, and
+    # every token after the gist has the item block dug out.  The query rows
+    # over the [gist ; query] columns are the online pass's mask.
+    for n_item, n_gist, ell in ((5, 3, 4), (1, 8, 1), (9, 1, 6), (2, 4, 16)):
+        n = n_item + n_gist + ell
+        m = torch.tril(torch.ones(n, n, dtype=torch.bool)).numpy()
+        m[n_item + n_gist:, :n_item] = False
+        assert np.array_equal(O.gist_online_mask(n_gist, ell), m[n_item + n_gist:, n_item:])
+
+
+def test_gather_logical_inverts_a_block_table_scatter():
+    # a logical sequence written block by block into the physical blocks a
+    # permuted table names (the other rows hold unrelated values) comes back
+    # in order
+    rng = np.random.default_rng(5)
+    n_blocks, h, bs, d, g = 9, 2, 4, 3, 1
+    for n_tokens in (0, 1, 4, 5, 13):
+        x = rng.standard_normal((n_tokens, d))
+        nb = -(-n_tokens // bs)
+        table = rng.permutation(n_blocks)[:max(nb, 1)]
+        cache = rng.standard_normal((n_blocks, h, bs, d))
+        for i in range(nb):
+            chunk = x[i * bs:(i + 1) * bs]
+            cache[table[i], g, :len(chunk)] = chunk
+        got = O.gather_logical(cache, table, n_tokens, g)
+        assert got.shape == (n_tokens, d)
+        assert np.array_equal(got, x)
