@@ -619,7 +619,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       for_each_const<QPF>([&](auto slot) {
         const int hh = hb + decltype(slot)::value;
         // refill with the head QPF further on (clamped: always a valid row,
-        // so the load is unconditional)
+        // so the load is unconditional; the last QPF heads thus read head
+        // G-1 again, which is why the common group sizes have instances with
+        // the group size fixed at compile time)
         if (hh < G) head(slot, hh, [&] { load_q(slot, hh + QPF < G ? hh + QPF : G - 1); });
       });
     }
@@ -1317,14 +1319,28 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     constexpr bool L = decltype(last_c)::value;
     const int nkt = nk_pad / 16;
     const int G = a.G;
+    // the whole grid resident at once (see the Q prefetch depth below)
+    const bool one_gen = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
     if (fp8) {
-      // fp8 pools: the instances with the group size taken from the arguments
-      if (d == 64 && nkt <= 5)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<64, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
+      // fp8 pools: the common group sizes at compile time (no Q row past the
+      // group is loaded), the rest with the group size from the arguments
+      const size_t lds5 = MfmaLds<64, 5>::bytes(nk_pad, ell);
+      if (d == 64 && nkt <= 5 && G == 7 && one_gen)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
+      else if (d == 64 && nkt <= 5 && G == 7)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
+      else if (d == 64 && nkt <= 5 && G == 8 && one_gen)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
+      else if (d == 64 && nkt <= 5 && G == 8)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
+      else if (d == 64 && nkt <= 5)
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
       else if (d == 64)
         hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, true>), grid, dim3(256),
                            (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+      else if (nkt <= 5 && G == 8)
+        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, true>), grid, dim3(256),
+                           (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
       else if (nkt <= 5)
         hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, true>), grid, dim3(256),
                            (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
@@ -1340,12 +1356,11 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
         // every workgroup issues its staging loads at the same moment and a
         // deeper Q prefetch only delays them: prefetch one head ahead.  With
         // several generations of workgroups, two heads ahead.
-        const bool one_generation = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
-        if (G == 7 && one_generation)
+        if (G == 7 && one_gen)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 7)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else if (G == 8 && one_generation)
+        else if (G == 8 && one_gen)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else if (G == 8)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
@@ -1358,7 +1373,12 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     } else {
       if (nkt <= 5) {
         const size_t lds = MfmaLds<128, 5>::bytes(nk_pad, ell);
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
+        // a compile-time group size loads no Q row past the group (the
+        // generic instance's clamped ring refills re-read the last head)
+        if (G == 8)
+          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
+        else
+          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
         hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, false>), grid, dim3(256),
                            (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
