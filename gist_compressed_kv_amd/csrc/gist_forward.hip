@@ -105,6 +105,17 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// Orders the LDS accesses of one wave around an exchange between its lanes
+// (one lane writes what another reads).  A wave's LDS accesses already
+// complete in program order, so this emits no instruction; it keeps the
+// compiler from moving or reusing a lane's LDS loads across the point as if
+// no other lane wrote there.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <typename T>
 __device__ __forceinline__ T nan_value() {
   if constexpr (sizeof(T) == 2)
@@ -154,23 +165,38 @@ __device__ __host__ constexpr int vt_stride(int keys) {
 
 template <int D, int NKT>
 struct MfmaLds {
-  static constexpr int KS = D + 8;          // K row stride (elements): 16*odd bytes
   static constexpr int VS = vt_stride(16 * NKT);  // Vᵀ row stride (elements)
-  // RoPE table: one row per new token, (cos, sin) of each channel pair,
-  // rows padded by 16 bytes so 16 lanes reading 16 consecutive rows (or 4
-  // rows x 4 chunks) hit distinct banks
-  static constexpr int CS_ROW = D / 2 * 2 + 4;  // floats per table row
-  static constexpr size_t kv_bytes(int nk_pad) {
-    return ((size_t)nk_pad * KS + (size_t)D * VS + 4 * (D / 8)) * sizeof(bf16_t);
-  }
-  // after the staging barrier the table's space becomes four per-wave
-  // transpose buffers of 16 rows x 2*D bytes
+  // K rows hold D channels, no padding: the 16-byte chunks of row r are
+  // XOR-swizzled by r & 7 (kchunk), so sixteen consecutive rows read at one
+  // chunk position hit distinct banks.  Two arrays: the bf16 value of each
+  // key (hi) and the bf16 rounding of what hi leaves out (lo).
+  static constexpr size_t k_bytes(int nk_pad) { return (size_t)nk_pad * D * sizeof(bf16_t); }
+  static constexpr size_t vt_bytes = ((size_t)D * VS + 4 * (D / 8)) * sizeof(bf16_t);
+  static constexpr size_t kv_bytes(int nk_pad) { return 2 * k_bytes(nk_pad) + vt_bytes; }
+  // four per-wave transpose buffers of 16 rows x 2*D bytes
   static constexpr size_t xpose_bytes = 4 * 16 * 2 * D;
-  static constexpr size_t bytes(int nk_pad, int ell) {
-    const size_t table = (size_t)ell * CS_ROW * sizeof(float);
-    return kv_bytes(nk_pad) + (table > xpose_bytes ? table : xpose_bytes);
-  }
+  static constexpr size_t bytes(int nk_pad) { return kv_bytes(nk_pad) + xpose_bytes; }
 };
+
+// element offset of 16-byte chunk c of K row r
+template <int D>
+__device__ __forceinline__ int kchunk(int r, int c) {
+  return r * D + ((c ^ (r & 7)) << 3);
+}
+
+// Split fp32 values into a bf16 pair hi + lo: hi is the nearest bf16 of x,
+// lo the nearest bf16 of x - hi (exact in fp32), so hi + lo carries 16
+// significant bits.  The product q·k of two such pairs, taken as
+// qhi·khi + qlo·khi + qhi·klo on the matrix cores, has a relative error of
+// about 2^-16, against 2^-8 for the product of the rounded values.
+__device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo) {
+  hi = pack8_bf16(y);
+  float h[8], r[8];
+  unpack8(hi, h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = y[e] - h[e];
+  lo = pack8_bf16(r);
+}
 
 // D: head_dim.  NKT: maximum number of 16-key tiles (keys <= 16*NKT).
 // QPF: Q ring depth: once head h has taken its Q out of the ring, the
@@ -181,34 +207,47 @@ struct MfmaLds {
 // output stores (which share the vector-memory counter) before a Q load.
 //
 // LDS holds the pair's keys in reverse order: key κ (0 = first gist row) is
-// row nk_pad-1-κ of Ks and column nk_pad-1-κ of Vᵀ.  A wave visits its key
-// tiles from the causal edge backwards (j = 0 is the tile with the last
+// row nk_pad-1-κ of Khi/Klo and column nk_pad-1-κ of Vᵀ.  A wave visits its
+// key tiles from the causal edge backwards (j = 0 is the tile with the last
 // visible key), so tile j sits at a compile-time offset from one per-wave
 // base address, and only tiles j = 0 and j = 1 can hold keys that some token
 // of the wave may not see.
+// Precision: the rotated Q and the rotated new keys are carried as bf16
+// pairs hi + lo (split8_bf16) and the logits take three products per tile,
+// K_hi·Q_hi + K_hi·Q_lo + K_lo·Q_hi, so they hold the fp32 rotation to about
+// 2^-16; the stored gist K is bf16 already (its lo rows are zero).  P is
+// rounded to bf16 for the P·V product.
+// RoPE: wave w rotates the new keys of token block w and, in the same lanes,
+// the query rows of that block (lane (n, q4): token 16w + n, channel pairs
+// 32s + 8*q4 + e), so each lane evaluates the angles of its own token once
+// and uses them for both; no angle table and one barrier.
 // LAST: only the last token's rows are produced (q and out hold one token
 // per pair).  The keys are staged as for every token; every wave takes the
 // 16-token block that holds the last token and the group's heads are spread
 // over the four waves (head h on wave h mod 4), each storing that token alone.
 // FP8: the gist pools hold E4M3 codes.  Each staged gist element is the
-// decoded code times its block's scale, rounded to bf16 once; the rest of the
-// kernel is the bf16 one.
+// decoded code times its block's scale in fp32, staged as a bf16 pair like
+// the new keys (V: rounded to bf16 once); the rest of the kernel is the bf16
+// one.
+// Waves per SIMD: four workgroups per CU fit the LDS at d = 64 with up to
+// 80 keys (so up to 128 VGPRs); otherwise two (up to 256 VGPRs).
 template <int D, int NKT, int QPF, int GT, bool LAST, bool FP8>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NKT <= 5 ? 4 : 2)))
 gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
-  constexpr int KS = MfmaLds<D, NKT>::KS;
   constexpr int VS = MfmaLds<D, NKT>::VS;
   constexpr int NS = D / 32;   // 32-channel k-steps of the Q·Kᵀ product
   constexpr int NP = NS / 2;   // RoPE: step s pairs with step s + NP
   constexpr int NDT = D / 16;  // 16-channel tiles of the output
-  constexpr int CH = D / 16;   // K staging units per row (8 channels + partners)
   constexpr int CV = D / 8;    // V staging units per key pair (8 channels)
-  constexpr int IT = D / 32;   // staging units per thread (nk_pad <= 128)
-  constexpr int CS_ROW = MfmaLds<D, NKT>::CS_ROW;
-  bf16_t* Ks = smem;                // [nk_pad][KS], reversed key order
-  bf16_t* Vt = smem + nk_pad * KS;  // [D][VS], reversed key order
-  float* cst = (float*)((char*)smem + MfmaLds<D, NKT>::kv_bytes(nk_pad));  // [ell][CS_ROW]
+  constexpr int IT = D / 32;   // V staging units per thread (nk_pad <= 128)
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR; // token rows per coalesced instruction
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  bf16_t* Khi = smem;                   // [nk_pad][D], reversed key order
+  bf16_t* Klo = smem + nk_pad * D;      // [nk_pad][D]
+  bf16_t* Vt = smem + 2 * nk_pad * D;   // [D][VS], reversed key order
+  char* xbuf = (char*)smem + MfmaLds<D, NKT>::kv_bytes(nk_pad);
 
   const int p = blockIdx.x / a.H;
   const int g = blockIdx.x - p * a.H;
@@ -234,6 +273,9 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   const bool tvalid = t < ell;
   // rows past ell read the last valid token (finite values, never stored)
   const int tl = tvalid ? t : ell - 1;
+  // the new keys this wave rotates and stages: token block wv
+  const int tk = 16 * wv + n;
+  const int tkl = tk < ell ? tk : ell - 1;
   // Q and O move between HBM and registers in a coalesced layout: lane l
   // covers chunk l % CPR (8 channels, 16 bytes) of token row l / CPR, so
   // every 128-byte line of a (token, head) row is read or written whole by
@@ -242,8 +284,6 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // offsets (scalar-base addressing form).
   // Q is read once, in whole lines: its loads are non-temporal (the staging
   // loads are not: they touch parts of lines that other loads then reuse)
-  constexpr int CPR = D / 8;   // 16-byte chunks per (token, head) row
-  constexpr int RPI = 64 / CPR; // token rows per instruction
   const int cl = lane % CPR, rl = lane / CPR;
   const int64_t pair_off = (int64_t)p * (LAST ? 1 : ell) * Hq * D;
   const char* qpair = (const char*)((const bf16_t*)a.q + pair_off);
@@ -262,7 +302,6 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   }
   // Q ring held in native vectors (not the HIP uint4 struct) so it always
   // stays in registers
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   u32x4_t raw[QPF][NS];
   auto load_q = [&](auto slot, const int hq) {
 #pragma unroll
@@ -316,112 +355,167 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       svq = sq[a.H + g];
     }
   }
-  // eight channels from channel ch of key row j as bf16.  fp8 gist rows are
-  // decoded, multiplied by their block's scale in fp32 and rounded to bf16
-  // once, so past the staging the kernel runs as over a bf16 pool; the new
-  // rows are bf16 activations.  With fp8 pools every lane still issues one
-  // 16-byte load, from its gist row or its new row (the address is the only
-  // per-lane choice), so the staging loads stay unconditional: a gist lane
-  // reads the aligned 16 codes that hold its 8 and decodes its half.
-  auto load8 = [&](int j, bool v, int ch) -> uint4 {
+  // Eight gist elements (channels ch.., K or V of gist key j < kg) as fp32.
+  // fp8 gist rows are decoded and multiplied by their block's scale.  Every
+  // lane issues one 16-byte load (fp8: the aligned 16 codes that hold its 8).
+  auto gist_row = [&](int j, bool v) -> const C* {
+    return j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
+                   : qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+  };
+  auto gist_raw = [&](int j, bool v, int ch) -> u32x4_t {
+    if constexpr (FP8) return *(const u32x4_t*)(gist_row(j, v) + (ch & ~15));
+    else return *(const u32x4_t*)(gist_row(j, v) + ch);
+  };
+  auto gist_f32 = [&](const u32x4_t& raw, int j, bool v, int ch, float* f) {
     if constexpr (FP8) {
-      typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
-      const bool gist = j < kg;
-      const C* grow = j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
-                      : (a.kq && gist) ? qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D
-                                       : gK;
-      const bf16_t* nrow = (const bf16_t*)(v ? a.v_new : a.k_new) +
-                           (((int64_t)p * a.ell + (gist ? 0 : j - kg)) * a.H + g) * D;
-      const u4_t raw = *(const u4_t*)(gist ? (const void*)(grow + (ch & ~15)) : (const void*)(nrow + ch));
       const float sc = j < a.k ? (v ? svi : ski) : (v ? svq : skq);
-      float f[8];
       decode4_e4m3((ch & 8) ? raw.z : raw.x, f);
       decode4_e4m3((ch & 8) ? raw.w : raw.y, f + 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] *= sc;
-      const uint4 dec = pack8_bf16(f);
-      return gist ? dec : make_uint4(raw.x, raw.y, raw.z, raw.w);
     } else {
-      return *(const uint4*)(key_row(a, gK, qK, p, g, j, kg, D, v) + ch);
+      unpack8(make_uint4(raw.x, raw.y, raw.z, raw.w), f);
     }
   };
+  // V of key j (< nk) as eight bf16: gist rows through gist_f32 (fp8:
+  // rounded to bf16 once), new rows as loaded
+  auto v_load = [&](int j, int ch) -> u32x4_t {
+    const bf16_t* nrow = (const bf16_t*)a.v_new + (((int64_t)p * ell + (j < kg ? 0 : j - kg)) * a.H + g) * D;
+    if constexpr (FP8) {
+      // one unconditional load per lane: its gist row or its new row
+      const bool gist = j < kg;
+      return *(const u32x4_t*)(gist ? (const void*)(gist_row(j, true) + (ch & ~15))
+                                    : (const void*)(nrow + ch));
+    } else {
+      return *(const u32x4_t*)(j < kg ? gist_row(j, true) + ch : nrow + ch);
+    }
+  };
+  auto v_bf16 = [&](const u32x4_t& raw, int j, int ch) -> uint4 {
+    if constexpr (FP8) {
+      if (j < kg) {
+        float f[8];
+        gist_f32(raw, j, true, ch, f);
+        return pack8_bf16(f);
+      }
+    }
+    return make_uint4(raw.x, raw.y, raw.z, raw.w);
+  };
+
   // ---- issue every staging load of this thread ----------------------------
-  // Every load below is unconditional (out-of-range units read row 0 and
-  // are zeroed afterwards), so the compiler can count the loads in flight
-  // exactly and later waits never have to drain the Q prefetch (with fp8
-  // pools too: load8 issues one load per unit whichever row it reads).
-  uint4 klo[IT], khi[IT], v0[IT], v1[IT];
+  // Every load below is unconditional (out-of-range units read a valid row
+  // and are dropped or zeroed afterwards), so the compiler can count the
+  // loads in flight exactly and later waits never have to drain the Q
+  // prefetch.
+  // new keys of token block wv, in the MFMA-operand channel layout of this
+  // lane's own query token: step s holds channels 32s + 8*q4 .. +7
+  u32x4_t kn[NS];
+  {
+    const bf16_t* krow = (const bf16_t*)a.k_new + (((int64_t)p * ell + tkl) * a.H + g) * D + 8 * q4;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kn[s] = *(const u32x4_t*)(krow + 32 * s);
+  }
+  // first gist K unit of this thread (the rest, if kg*CPR > 256, below)
+  const int gu_row = tid / CPR, gu_c = tid % CPR;
+  const u32x4_t graw = gist_raw(gu_row < kg ? gu_row : 0, false, 8 * gu_c);
+  // V unit (key pair jp, 8-channel chunk cv), chunks fastest: the lanes of
+  // one instruction read whole rows of eight keys (pairs past nk read row 0)
+  u32x4_t v0[IT], v1[IT];
   const int npairs = nk_pad >> 1;
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int u = tid + 256 * it;
-    const int j = u / CH, c = u - j * CH;
-    const int jc = j < nk ? j : 0;
-    klo[it] = load8(jc, false, 8 * c);
-    khi[it] = load8(jc, false, D / 2 + 8 * c);
-    // V unit (key pair jp, 8-channel chunk cv), chunks fastest: the lanes of
-    // one instruction read whole rows of eight keys, not one chunk of each of
-    // 64 rows (fewer cache lines per instruction; pairs past nk read row 0)
     const int jp = u / CV, cv = u - jp * CV;
-    v0[it] = load8(2 * jp < nk ? 2 * jp : 0, true, 8 * cv);
-    v1[it] = load8(2 * jp + 1 < nk ? 2 * jp + 1 : 0, true, 8 * cv);
+    v0[it] = v_load(2 * jp < nk ? 2 * jp : 0, 8 * cv);
+    v1[it] = v_load(2 * jp + 1 < nk ? 2 * jp + 1 : 0, 8 * cv);
   }
 
   // keep the staging loads together (the Q prefetch above was issued first
   // and has returned by the time the LDS stores wait for them)
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- RoPE table: wave w evaluates channel pairs [w*D/8, (w+1)*D/8) for
-  // position pos0 + lane (the pair index is wave-uniform, so the frequency
-  // comes from a scalar load), while the loads above are in flight --------
-  {
-    const int wraw = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tpos = tid & 63;
-    if (tpos < ell) {
-      const double pos = (double)a.pos0 + tpos;  // no int32 overflow near INT_MAX
+  // ---- RoPE angles of this lane's token(s) while the loads are in flight:
+  // channel pairs i = 32s + 8*q4 + e (s < NP), position pos0 + token --------
+  // The frequency of pair i is rev_i = rev_0 * r^i with r = base^(-2/d);
+  // this lane's pairs are rev_{32s+e} (scalars) times r^(8*q4), formed from
+  // the scalar powers r^8 and r^16, so no lane-indexed table is read.
+  float qc[NP][8], qsn[NP][8];
+  const double rq = ((q4 & 1) ? a.rev_step[3] : 1.0) * ((q4 & 2) ? a.rev_step[4] : 1.0);
+  auto angles = [&](int tok, float (*c)[8], float (*sn)[8]) {
+    const double pos = (double)a.pos0 + tok;  // no int32 overflow near INT_MAX
 #pragma unroll
-      for (int k = 0; k < D / 8; ++k) {
-        const int i = wraw * (D / 8) + k;
-        float cs, sn;
-        rope_cos_sin(pos, a.freqs.rev[i], cs, sn);
-        *(float2*)(cst + tpos * CS_ROW + 2 * i) = make_float2(cs, sn);
+    for (int s = 0; s < NP; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        rope_cos_sin(pos, a.freqs.rev[32 * s + e] * rq, c[s][e], sn[s][e]);
+  };
+  angles(tl, qc, qsn);
+
+  // ---- new keys: rotate (fp32), split into bf16 hi + lo, store reversed ----
+  if (16 * wv < ell) {
+    float kcs[NP][8], ksn[NP][8];
+    if constexpr (LAST) angles(tkl, kcs, ksn);
+    const float(*c)[8] = LAST ? kcs : qc;
+    const float(*sn)[8] = LAST ? ksn : qsn;
+    if (tk < ell) {
+      const int R = nk_pad - 1 - (kg + tk);
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        float xl[8], xh[8], yl[8], yh[8];
+        unpack8(make_uint4(kn[s].x, kn[s].y, kn[s].z, kn[s].w), xl);
+        unpack8(make_uint4(kn[s + NP].x, kn[s + NP].y, kn[s + NP].z, kn[s + NP].w), xh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          yl[e] = __builtin_fmaf(xl[e], c[s][e], -(xh[e] * sn[s][e]));
+          yh[e] = __builtin_fmaf(xh[e], c[s][e], xl[e] * sn[s][e]);
+        }
+        uint4 hl, ll, hh, lh;
+        split8_bf16(yl, hl, ll);
+        split8_bf16(yh, hh, lh);
+        const int ol = kchunk<D>(R, 4 * s + q4), oh = kchunk<D>(R, 4 * (s + NP) + q4);
+        *(uint4*)(Khi + ol) = hl;
+        *(uint4*)(Klo + ol) = ll;
+        *(uint4*)(Khi + oh) = hh;
+        *(uint4*)(Klo + oh) = lh;
       }
     }
   }
-  __syncthreads();
-
-  // ---- K: rotate the new rows, store; V: transpose, store (reversed) -------
+  // ---- gist K rows (hi: the stored value; fp8: decoded times scale, lo its
+  // remainder) and zero padding rows past nk ------------------------------
+  auto put_gist = [&](const u32x4_t& raw, int j, int c) {
+    const int R = nk_pad - 1 - j;
+    uint4 hi, lo;
+    if constexpr (FP8) {
+      float f[8];
+      gist_f32(raw, j, false, 8 * c, f);
+      split8_bf16(f, hi, lo);
+    } else {
+      hi = make_uint4(raw.x, raw.y, raw.z, raw.w);
+      lo = make_uint4(0, 0, 0, 0);
+    }
+    *(uint4*)(Khi + kchunk<D>(R, c)) = hi;
+    *(uint4*)(Klo + kchunk<D>(R, c)) = lo;
+  };
+  if (gu_row < kg) put_gist(graw, gu_row, gu_c);
+  for (int u = tid + 256; u < kg * CPR; u += 256) {  // long gists only
+    const int j = u / CPR, c = u % CPR;
+    put_gist(gist_raw(j, false, 8 * c), j, c);
+  }
+  for (int u = tid; u < (nk_pad - nk) * CPR; u += 256) {
+    const int R = nk_pad - 1 - (nk + u / CPR), c = u % CPR;
+    *(uint4*)(Khi + kchunk<D>(R, c)) = make_uint4(0, 0, 0, 0);
+    *(uint4*)(Klo + kchunk<D>(R, c)) = make_uint4(0, 0, 0, 0);
+  }
+  // ---- V: transpose, store (reversed) ---------------------------------------
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int u = tid + 256 * it;
-    const int j = u / CH, c = u - j * CH;
-    if (j < nk_pad) {
-      const uint4 zero = make_uint4(0, 0, 0, 0);
-      uint4 lo = j < nk ? klo[it] : zero, hi = j < nk ? khi[it] : zero;
-      if (j >= kg && j < nk) {
-        float xl[8], xh[8], yl[8], yh[8];
-        unpack8(lo, xl);
-        unpack8(hi, xh);
-        const float* crow = cst + (j - kg) * CS_ROW + 16 * c;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 cssn = *(const float2*)(crow + 2 * e);
-          yl[e] = __builtin_fmaf(xl[e], cssn.x, -(xh[e] * cssn.y));
-          yh[e] = __builtin_fmaf(xh[e], cssn.x, xl[e] * cssn.y);
-        }
-        lo = pack8_bf16(yl);
-        hi = pack8_bf16(yh);
-      }
-      bf16_t* dst = Ks + (nk_pad - 1 - j) * KS;
-      *(uint4*)(dst + 8 * c) = lo;
-      *(uint4*)(dst + D / 2 + 8 * c) = hi;
-    }
     const int jp = u / CV, cv = u - jp * CV;
     if (jp < npairs) {
       // keys 2jp, 2jp+1 land in reversed columns nk_pad-2-2jp (key 2jp+1)
       // and nk_pad-1-2jp (key 2jp): one dword, high key in the low half
       const uint4 zero = make_uint4(0, 0, 0, 0);
-      const uint4 w0 = 2 * jp < nk ? v0[it] : zero, w1 = 2 * jp + 1 < nk ? v1[it] : zero;
+      const uint4 w0 = 2 * jp < nk ? v_bf16(v0[it], 2 * jp, 8 * cv) : zero;
+      const uint4 w1 = 2 * jp + 1 < nk ? v_bf16(v1[it], 2 * jp + 1, 8 * cv) : zero;
       const uint32_t a0[4] = {w0.x, w0.y, w0.z, w0.w};
       const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w};
       const int col = nk_pad - 2 - 2 * jp;
@@ -435,33 +529,12 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     }
   }
 
-  // ---- RoPE angles of this lane's token (channels 32s + 8*q4 + e).  The
-  // softmax scale (with log2 e) is applied to the fp32 logits inside the
-  // exponent, so Q is rounded to bf16 as the rotated Q itself, the rounding
-  // point of an unfused RoPE-then-attention pipeline ----------------------
-  const float sl2 = a.scale_log2;
-  float qc[NP][8], qsn[NP][8];
-  {
-    const float* crow = cst + tl * CS_ROW;
-#pragma unroll
-    for (int s = 0; s < NP; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 cssn = *(const float2*)(crow + 2 * (32 * s + 8 * q4 + e));
-        qc[s][e] = cssn.x;
-        qsn[s][e] = cssn.y;
-      }
-  }
-  __syncthreads();
-  if (!wave_active) return;
-
-  // per-wave transpose buffer (the RoPE table is dead past the barrier):
-  // 16 rows of 2*D bytes, chunk c of row r stored at chunk c ^ r.  A 16-byte
-  // access is served eight lanes per clock; the coalesced side has those
-  // lanes on one row (distinct chunks), the MFMA side has them on rows
-  // 0..7 of one chunk, which the XOR sends to eight distinct chunks: both
-  // sides are free of bank conflicts.
-  char* xb = (char*)cst + (tid >> 6) * (16 * 2 * D);
+  // per-wave transpose buffer: 16 rows of 2*D bytes, chunk c of row r stored
+  // at chunk c ^ r.  A 16-byte access is served eight lanes per clock; the
+  // coalesced side has those lanes on one row (distinct chunks), the MFMA
+  // side has them on rows 0..7 of one chunk, which the XOR sends to eight
+  // distinct chunks: both sides are free of bank conflicts.
+  char* xb = xbuf + (tid >> 6) * (16 * 2 * D);
   auto xpos = [](int r, int c) -> uint32_t {
     return (uint32_t)(r * 2 * D + ((c ^ r) & (CPR - 1)) * 16);
   };
@@ -472,11 +545,54 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     xr[s] = xpos(n, 4 * s + q4);
   }
 
+  // Q of the head in ring slot i: to the MFMA layout through the wave's
+  // buffer, rotated in fp32 and split into bf16 hi + lo
+  auto prep_q = [&](auto slot, bf16x8_t* qh, bf16x8_t* ql) {
+    constexpr int i = decltype(slot)::value;
+    uint4 qm[NS];
+    wave_lds_sync();  // the previous reads of the buffer are done
+#pragma unroll
+    for (int s = 0; s < NS; ++s) *(u32x4_t*)(xb + xw[s]) = raw[i][s];
+    wave_lds_sync();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4_t m = *(const u32x4_t*)(xb + xr[s]);
+      qm[s] = make_uint4(m.x, m.y, m.z, m.w);
+    }
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+      float xl[8], xh[8], yl[8], yh[8];
+      unpack8(qm[s], xl);
+      unpack8(qm[s + NP], xh);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        yl[e] = __builtin_fmaf(xl[e], qc[s][e], -(xh[e] * qsn[s][e]));
+        yh[e] = __builtin_fmaf(xh[e], qc[s][e], xl[e] * qsn[s][e]);
+      }
+      uint4 h0, l0, h1, l1;
+      split8_bf16(yl, h0, l0);
+      split8_bf16(yh, h1, l1);
+      qh[s] = __builtin_bit_cast(bf16x8_t, h0);
+      ql[s] = __builtin_bit_cast(bf16x8_t, l0);
+      qh[s + NP] = __builtin_bit_cast(bf16x8_t, h1);
+      ql[s + NP] = __builtin_bit_cast(bf16x8_t, l1);
+    }
+  };
+  // the wave's first head, before the barrier (its buffer is its own)
+  bf16x8_t qh[NS], ql[NS];
+  if (wave_active) prep_q(std::integral_constant<int, 0>{}, qh, ql);
+  __syncthreads();
+  if (!wave_active) return;
+
   const int tlast = min(t0 + 15, ell - 1);
   const int nkt = (kg + tlast + 1 + 15) >> 4;  // tiles holding any visible key
-  // reversed-order base rows of tile j = 0 (key tile nkt-1)
+  // reversed-order base rows of tile j = 0 (key tile nkt-1); row0 is a
+  // multiple of 16, so lane n reads rows with (row & 7) == (n & 7) in every
+  // tile and its swizzled chunk offsets are fixed
   const int row0 = nk_pad - 16 * nkt;
-  const bf16_t* kbase = Ks + (row0 + n) * KS + 8 * q4;
+  int koff[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) koff[s] = kchunk<D>(row0 + n, 4 * s + q4);
   // (the block pad of vt_off is the same for every d-tile: vt_row(dt, n) >> 3
   // differs from vt_row(0, n) >> 3 by 4*(dt >> 1), folded into the offsets)
   const bf16_t* vbase = Vt + vt_off(vt_row(0, n), row0 + 4 * q4, VS);
@@ -491,138 +607,142 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   }
   // ds_bpermute byte addresses of the lanes that hold the same token
   const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
+  const float sl2 = a.scale_log2;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-
-  // One query head: i is its Q ring slot, hh the head within the group;
-  // refill() issues the next Q loads once the slot has been consumed.
-  auto head = [&](auto slot, const int hh, auto&& refill) {
-    constexpr int i = decltype(slot)::value;
-        // Q tile to the MFMA layout through the wave's LDS buffer
-        uint4 qm[NS];
+  bf16x8_t ones8;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) *(u32x4_t*)(xb + xw[s]) = raw[i][s];
+  for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
+
+  // Attention of one query head (Q in qh/ql), output rows of head hh.
+  auto attend = [&](const int hh) {
+    // logits Sᵀ = K·Qᵀ (unscaled; scale*log2 e is applied in the exponent)
+    f32x4_t sacc[NKT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NKT; ++j) {
+      if (j == 0 || j < nkt) {  // an active wave has at least one tile
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if (j < 2) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[r] = (j == 0 ? vis0[r] : vis1[r]) ? 0.f : -INFINITY;
+        }
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-          const u32x4_t m = *(const u32x4_t*)(xb + xr[s]);
-          qm[s] = make_uint4(m.x, m.y, m.z, m.w);
+          const bf16x8_t kh = *(const bf16x8_t*)(Khi + koff[s] + 16 * D * j);
+          const bf16x8_t kl = *(const bf16x8_t*)(Klo + koff[s] + 16 * D * j);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[s], acc, 0, 0, 0);
         }
-        // rotate this head's Q (fp32 math, bf16 for the MFMA)
-        bf16x8_t qf[NS];
-#pragma unroll
-        for (int s = 0; s < NP; ++s) {
-          float xl[8], xh[8], yl[8], yh[8];
-          unpack8(qm[s], xl);
-          unpack8(qm[s + NP], xh);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            yl[e] = __builtin_fmaf(xl[e], qc[s][e], -(xh[e] * qsn[s][e]));
-            yh[e] = __builtin_fmaf(xh[e], qc[s][e], xl[e] * qsn[s][e]);
-          }
-          qf[s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
-          qf[s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
-        }
-        refill();
+        sacc[j] = acc;
+        mx = vmax3(mx, acc[0], acc[1]);
+        mx = vmax3(mx, acc[2], acc[3]);
+      }
+    }
+    // row max across the four lanes that share a token
+    mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
+    mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
 
-        // logits Sᵀ = K·Qᵀ (unscaled; scale*log2 e is applied in the exponent)
-        f32x4_t sacc[NKT];
-        float mx = -INFINITY;
+    // P = exp2((s - max) * scale*log2 e) in bf16, the product as one fma;
+    // O = P·V and the row sum (P against a ones tile) both on the matrix
+    // cores.  Key tiles go in pairs through v_mfma_f32_16x16x32_bf16:
+    // contraction index 8*q4 + e stands for key row 4*q4 + e of tile j0
+    // (e < 4) and 4*q4 + e - 4 of tile j0 + 1, which is what a lane's weights
+    // of the two tiles are and what two 8-byte reads of Vᵀ give the A
+    // operand.  An unpaired last tile takes the 16x16x16 form.
+    const float nmx = -mx * sl2;
+    f32x4_t o[NDT];
 #pragma unroll
-        for (int j = 0; j < NKT; ++j) {
-          if (j == 0 || j < nkt) {  // an active wave has at least one tile
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-            if (j < 2) {
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+    auto weights = [&](int j) {
+      float w[4];
 #pragma unroll
-              for (int r = 0; r < 4; ++r) acc[r] = (j == 0 ? vis0[r] : vis1[r]) ? 0.f : -INFINITY;
-            }
+      for (int r = 0; r < 4; ++r) w[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r], sl2, nmx));
+      return make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]));
+    };
+    auto vfrag = [&](int dt, int j) {
+      return *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
+    };
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              const bf16x8_t kf = *(const bf16x8_t*)(kbase + 16 * KS * j + 32 * s);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
-            }
-            sacc[j] = acc;
-            mx = vmax3(mx, acc[0], acc[1]);
-            mx = vmax3(mx, acc[2], acc[3]);
-          }
+    for (int j0 = 0; j0 < NKT; j0 += 2) {
+      if (j0 + 1 < NKT && j0 + 1 < nkt) {
+        const uint2 p0 = weights(j0), p1 = weights(j0 + 1);
+        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y));
+        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf, lacc, 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t vf = __builtin_shufflevector(vfrag(dt, j0), vfrag(dt, j0 + 1), 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
         }
-        // row max across the four lanes that share a token
-        mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
-        mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
-
-        // P = exp2((s - max) * scale*log2 e) in bf16, the product as one fma;
-        // O = P·V and the row sum (P against a ones tile) both on the matrix
-        // cores
-        const float nmx = -mx * sl2;
-        f32x4_t o[NDT];
+      } else if (j0 == 0 || j0 < nkt) {
+        const bf16x4v pf = __builtin_bit_cast(bf16x4v, weights(j0));
+        lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < NDT; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag(dt, j0), pf, o[dt], 0, 0, 0);
+      }
+    }
+    // O tile back to the coalesced layout through the same buffer, then
+    // whole-line non-temporal stores (the output is not read again here)
+    const float inv = __builtin_amdgcn_rcpf(lacc[0]);
+    wave_lds_sync();  // the Q reads of the buffer are done
 #pragma unroll
-        for (int j = 0; j < NKT; ++j) {
-          if (j == 0 || j < nkt) {
-            float w[4];
+    for (int s = 0; s < NS; ++s) {
+      float v[8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][r], sl2, nmx));
-            const uint2 pk = make_uint2(pack2_bf16(w[0], w[1]), pack2_bf16(w[2], w[3]));
-            const bf16x4v pf = __builtin_bit_cast(bf16x4v, pk);
-            lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
+      for (int r = 0; r < 4; ++r) {
+        v[r] = o[2 * s][r] * inv;
+        v[4 + r] = o[2 * s + 1][r] * inv;
+      }
+      *(uint4*)(xb + xr[s]) = pack8_bf16(v);
+    }
+    wave_lds_sync();
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-              const bf16x4_t vf = *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
-              o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
-            }
-          }
-        }
-        // O tile back to the coalesced layout through the same buffer, then
-        // whole-line non-temporal stores (the output is not read again here)
-        {
-          const float inv = __builtin_amdgcn_rcpf(lacc[0]);
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            float v[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              v[r] = o[2 * s][r] * inv;
-              v[4 + r] = o[2 * s + 1][r] * inv;
-            }
-            *(uint4*)(xb + xr[s]) = pack8_bf16(v);
-          }
-#pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            const u32x4_t x = *(const u32x4_t*)(xb + xw[s]);
-            if (ovalid[s])
-              __builtin_nontemporal_store(x, (u32x4_t*)(opair + olane[s] + (uint32_t)(hh * D) * 2));
-          }
-        }
-        };
+    for (int s = 0; s < NS; ++s) {
+      const u32x4_t x = *(const u32x4_t*)(xb + xw[s]);
+      if (ovalid[s])
+        __builtin_nontemporal_store(x, (u32x4_t*)(opair + olane[s] + (uint32_t)(hh * D) * 2));
+    }
+  };
 
   if constexpr (LAST) {
     // heads wv, wv + 4, ...: the first from the prefetch, the next loaded here
     using S0 = std::integral_constant<int, 0>;
     for (int hh = wv; hh < G; hh += 4) {
-      if (hh != wv) load_q(S0{}, hh);
-      head(S0{}, hh, [] {});
+      if (hh != wv) {
+        load_q(S0{}, hh);
+        prep_q(S0{}, qh, ql);
+      }
+      attend(hh);
     }
   } else if constexpr (GT > 0) {
     // compile-time group size: the whole head sequence unrolls, so the ring
-    // slot of every head and every wait count is known to the compiler
+    // slot of every head and every wait count is known to the compiler.
+    // Head h's Q was prepared before this point; its slot is refilled with
+    // head h + QPF (heads past the group are not loaded, so the waits stay
+    // exact), then head h attends and head h + 1's Q is prepared.
     for_each_const<GT>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
-      // head h + QPF into the slot just consumed; heads past the group are
-      // not loaded (their count is known here, so the waits stay exact)
-      head(std::integral_constant<int, h % QPF>{}, h, [&] {
-        if constexpr (h + QPF < GT) load_q(std::integral_constant<int, h % QPF>{}, h + QPF);
-      });
+      if constexpr (h + QPF < GT) load_q(std::integral_constant<int, h % QPF>{}, h + QPF);
+      attend(h);
+      if constexpr (h + 1 < GT) prep_q(std::integral_constant<int, (h + 1) % QPF>{}, qh, ql);
     });
   } else {
+    // the ring is refilled with the head QPF further on (clamped: always a
+    // valid row, so the load is unconditional; the last QPF heads thus read
+    // head G-1 again, which is why the common group sizes have instances
+    // with the group size fixed at compile time)
     for (int hb = 0; hb < G; hb += QPF) {
       for_each_const<QPF>([&](auto slot) {
-        const int hh = hb + decltype(slot)::value;
-        // refill with the head QPF further on (clamped: always a valid row,
-        // so the load is unconditional; the last QPF heads thus read head
-        // G-1 again, which is why the common group sizes have instances with
-        // the group size fixed at compile time)
-        if (hh < G) head(slot, hh, [&] { load_q(slot, hh + QPF < G ? hh + QPF : G - 1); });
+        constexpr int i = decltype(slot)::value;
+        const int hh = hb + i;
+        if (hh < G) {
+          if (hh > 0) prep_q(slot, qh, ql);
+          load_q(slot, hh + QPF < G ? hh + QPF : G - 1);
+          attend(hh);
+        }
       });
     }
   }
@@ -637,9 +757,13 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 // slice, so no workgroup barrier is involved.
 //   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
 //   gist (kg = k + k' rows, padded with copies of row 0 that the mask
-//   removes); tile NGT holds the token's own key alone, rotated at pos0 like
-//   the query.  Rotated Q and K_new are rounded to bf16 for the MFMAs, and
-//   the softmax scale is applied to the fp32 logits in the exponent.
+//   removes), then the token's own key, rotated at pos0 like the query.
+//   The rotated Q is carried as a bf16 pair hi + lo (split8_bf16) and a gist
+//   tile takes K·Q_hi + K·Q_lo on the matrix cores (the stored gist K is
+//   exact in bf16).  The token's own logit is a single key per head: it is
+//   the fp32 dot product of the rotated Q and K_new on the VALU, and its V
+//   row enters the output by fp32 FMAs.  The softmax scale is applied to the
+//   fp32 logits in the exponent.
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
 // FP8: the gist pools hold E4M3 codes.  Every E4M3 value is also a bf16
 // value, so the codes are decoded exactly into the bf16 MFMA operands; the K
@@ -648,16 +772,13 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 // the unscaled weight).
 // QU: Q staging units per lane, G*D/16 units over 64 lanes (1 or 2).
 template <int D, int NGT, bool FP8, int QU>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
 gist_fwd_eos(const FwdArgs a) {
   constexpr int NS = D / 32;
-  constexpr int NP = NS / 2;
   constexpr int NDT = D / 16;
-  constexpr int NT = NGT + 1;            // gist tiles + self tile
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int VSELF = 16 * NGT;        // LDS row of V_new
-  constexpr int KSELF = 16 * NGT + 1;    // LDS row of K_new
-  constexpr int ROWS = 16 * NGT + 2;
+  constexpr int ROWS = 16 * NGT + 1;
   constexpr int RITG = 16 * NGT * CPR / 64;  // gist V row chunks per lane
   static_assert(16 * NGT * CPR % 64 == 0 && 2 * CPR <= 64, "staging layout");
   __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
@@ -685,10 +806,13 @@ gist_fwd_eos(const FwdArgs a) {
   // Q, coalesced: unit u = lane + 64*i covers head u / (D/16) and its chunk
   // pair (channels 8c..8c+7 and their RoPE partners D/2 + 8c..), so each
   // head's row is read whole and once; units past the group read its last
-  // head's first pair
+  // head's first pair.  The same chunk pair of K_new goes with it (the
+  // group's lanes share the one 128- or 256-byte row).
   constexpr int QCH = D / 16;  // chunk pairs per head
   const bf16_t* qgrp = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G) * D;
-  u32x4_t qlo[QU], qhi[QU];
+  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
+  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
+  u32x4_t qlo[QU], qhi[QU], klo[QU], khi[QU];
 #pragma unroll
   for (int i = 0; i < QU; ++i) {
     const int u = lane + 64 * i;
@@ -696,13 +820,13 @@ gist_fwd_eos(const FwdArgs a) {
     const bf16_t* src = qgrp + (uc / QCH) * D + 8 * (uc % QCH);
     qlo[i] = *(const u32x4_t*)src;
     qhi[i] = *(const u32x4_t*)(src + D / 2);
+    klo[i] = *(const u32x4_t*)(knew + 8 * (uc % QCH));
+    khi[i] = *(const u32x4_t*)(knew + D / 2 + 8 * (uc % QCH));
   }
-  // V_new and K_new as whole rows: lane l covers chunk l % CPR of row l / CPR
-  // (0 = V_new, 1 = K_new; lanes past the two rows read K_new again)
-  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
-  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
-  const int sr = lane / CPR, sc = lane - (lane / CPR) * CPR;
-  const u32x4_t rself = *(const u32x4_t*)((sr == 0 ? vnew : knew) + 8 * sc);
+  // V_new as a whole row: lane l covers chunk l % CPR (lanes past the row
+  // read it again)
+  const int sc = lane % CPR;
+  const u32x4_t rself = *(const u32x4_t*)(vnew + 8 * sc);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN); the
@@ -808,46 +932,88 @@ gist_fwd_eos(const FwdArgs a) {
     rope_cos_sin((double)a.pos0, rev, csc, css);
     cst[lane] = make_float2(csc, css);
   }
+  wave_lds_sync();
 
-  // ---- rotate Q at pos0 in the coalesced layout, then turn it into the MFMA
-  // B layout (lane n = query head, 8 channels of step s) through this wave's
-  // row buffer, whose rows are written only after the B fragments are read.
-  // Row h holds head h; chunk c sits at chunk c ^ h, so the eight lanes of a
+  // ---- rotate Q at pos0 in the coalesced layout, split it into bf16 hi +
+  // lo, then turn each into the MFMA B layout (lane n = query head, 8
+  // channels of step s) through this wave's row buffer: hi first, then lo in
+  // the same place (a wave's LDS accesses complete in order).  The buffer's
+  // rows are written with keys only after the B fragments are read.  Row h
+  // holds head h; chunk c sits at chunk c ^ h, so the eight lanes of a
   // 16-byte access phase hit distinct banks on both sides.
   bf16_t* Rl = rows_lds[wv];
   static_assert(16 * D <= ROWS * (D + 4), "Q staging fits the row buffer");
+  uint4 qlo_st[QU][2];
+  float sdot[QU];  // this lane's part of the token's own logit q·k
   auto qpos = [](int h, int c) { return h * D + (((c ^ h) & (CPR - 1)) << 3); };
 #pragma unroll
   for (int i = 0; i < QU; ++i) {
     const int u = lane + 64 * i;
     const int h = u / QCH, c = u - (u / QCH) * QCH;
-    float xl[8], xh[8], yl[8], yh[8];
+    float xl[8], xh[8], yl[8], yh[8], kl[8], kh[8];
     unpack8(make_uint4(qlo[i].x, qlo[i].y, qlo[i].z, qlo[i].w), xl);
     unpack8(make_uint4(qhi[i].x, qhi[i].y, qhi[i].z, qhi[i].w), xh);
+    unpack8(make_uint4(klo[i].x, klo[i].y, klo[i].z, klo[i].w), kl);
+    unpack8(make_uint4(khi[i].x, khi[i].y, khi[i].z, khi[i].w), kh);
+    float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 cs = cst[8 * c + e];
       yl[e] = __builtin_fmaf(xl[e], cs.x, -(xh[e] * cs.y));
       yh[e] = __builtin_fmaf(xh[e], cs.x, xl[e] * cs.y);
+      const float rl = __builtin_fmaf(kl[e], cs.x, -(kh[e] * cs.y));
+      const float rh = __builtin_fmaf(kh[e], cs.x, kl[e] * cs.y);
+      dot = __builtin_fmaf(yl[e], rl, dot);
+      dot = __builtin_fmaf(yh[e], rh, dot);
     }
+    // sum over the QCH lanes of head h (aligned groups of 4 or 8 lanes)
+    dot += dpp_f<0xB1>(dot);
+    dot += dpp_f<0x4E>(dot);
+    if constexpr (QCH == 8) dot += dpp_f<0x141>(dot);
+    sdot[i] = dot;
+    uint4 hl, hh;
+    split8_bf16(yl, hl, qlo_st[i][0]);
+    split8_bf16(yh, hh, qlo_st[i][1]);
     if (u < G * QCH) {
-      *(uint4*)(Rl + qpos(h, c)) = pack8_bf16(yl);
-      *(uint4*)(Rl + qpos(h, c + QCH)) = pack8_bf16(yh);
+      *(uint4*)(Rl + qpos(h, c)) = hl;
+      *(uint4*)(Rl + qpos(h, c + QCH)) = hh;
     }
   }
-  bf16x8_t qf[NS];
+  bf16x8_t qh[NS], ql[NS];
+  // columns past the group read its last head (finite, never stored)
+  const int hcol = n < G ? n : G - 1;
+  // the token's own logit of column n: head hcol's sum, held by its units
+  float sself;
   {
-    // columns past the group read its last head (finite, never stored)
-    const int hcol = n < G ? n : G - 1;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qf[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
+    const int su = hcol * QCH;
+    sself = __int_as_float(__builtin_amdgcn_ds_bpermute((su & 63) << 2, __float_as_int(sdot[0])));
+    if constexpr (QU == 2) {
+      const float s1 = __int_as_float(__builtin_amdgcn_ds_bpermute((su & 63) << 2, __float_as_int(sdot[1])));
+      sself = su >= 64 ? s1 : sself;
+    }
   }
+  wave_lds_sync();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) qh[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < QU; ++i) {
+    const int u = lane + 64 * i;
+    const int h = u / QCH, c = u - (u / QCH) * QCH;
+    if (u < G * QCH) {
+      *(uint4*)(Rl + qpos(h, c)) = qlo_st[i][0];
+      *(uint4*)(Rl + qpos(h, c + QCH)) = qlo_st[i][1];
+    }
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int s = 0; s < NS; ++s) ql[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
+  wave_lds_sync();  // the rows below overwrite the Q buffer
 
   // ---- logits Sᵀ[key][head] of the gist tiles (unscaled: scale*log2 e is
-  // applied in the exponent, so Q is rounded to bf16 as the rotated Q) ------
-  f32x4_t sacc[NT];
-  float mx = -INFINITY;
+  // applied in the exponent); the stored gist K is exact in bf16 ------------
+  f32x4_t sacc[NGT];
+  float mx = sself;
 #pragma unroll
   for (int kt = 0; kt < NGT; ++kt) {
     if (kt == 0 || kt < ngt) {
@@ -855,9 +1021,11 @@ gist_fwd_eos(const FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[r] = (FP8 || 16 * kt + 4 * q4 + r < kg) ? 0.f : -INFINITY;
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, to_bf16x8(kraw[kt][s])), qf[s], acc, 0, 0, 0);
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, to_bf16x8(kraw[kt][s]));
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qh[s], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[s], acc, 0, 0, 0);
+      }
       if constexpr (FP8) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -871,7 +1039,7 @@ gist_fwd_eos(const FwdArgs a) {
     }
   }
 
-  // ---- rows to LDS: the gist V rows, then V_new and K_new -------------------
+  // ---- rows to LDS: the gist V rows, then V_new ------------------------------
   auto put = [&](int r, int c, const u32x4_t& w) {
     // rows are 8-byte aligned: two 8-byte stores
     uint2* dst = (uint2*)(Rl + vrow_off(r, 8 * c, D));
@@ -883,39 +1051,8 @@ gist_fwd_eos(const FwdArgs a) {
     const int u = lane + 64 * it;
     put(u / CPR, u - (u / CPR) * CPR, to_bf16x8(graw[it]));
   }
-  if (sr < 2) put(VSELF + sr, sc, rself);
-  // K_new rotated at pos0 in place: lane i < D/2 turns channel pair
-  // (i, i + D/2) with its own cos/sin and rounds the pair to bf16
-  if (lane < D / 2) {
-    bf16_t* kl = Rl + vrow_off(KSELF, lane, D);
-    bf16_t* kh = Rl + vrow_off(KSELF, lane + D / 2, D);
-    const float xl = bf16_bits_to_f32(*kl), xh = bf16_bits_to_f32(*kh);
-    const uint32_t pk = pack2_bf16(__builtin_fmaf(xl, csc, -(xh * css)),
-                                   __builtin_fmaf(xh, csc, xl * css));
-    *kl = (bf16_t)(pk & 0xffffu);
-    *kh = (bf16_t)(pk >> 16);
-  }
-
-  {
-    // self tile: the rotated K_new in every MFMA row (rows other than 0 are
-    // removed by the bias) against the rotated Q
-    bf16x8_t kf[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const uint2* src = (const uint2*)(Rl + vrow_off(KSELF, 32 * s + 8 * q4, D));
-      const uint2 lo = src[0], hi = src[1];
-      kf[s] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-    }
-    f32x4_t acc;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = (q4 == 0 && r == 0) ? 0.f : -INFINITY;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], acc, 0, 0, 0);
-    sacc[NGT] = acc;
-    mx = vmax3(mx, acc[0], acc[1]);
-    mx = vmax3(mx, acc[2], acc[3]);
-  }
+  if (lane < CPR) put(VSELF, sc, rself);
+  wave_lds_sync();
   const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
@@ -926,15 +1063,17 @@ gist_fwd_eos(const FwdArgs a) {
   // 32*(dt >> 1) + 4*(dt & 1) + 8*(lane & 3) .. +3, so MFMA row r of the tile
   // is channel vt_row(dt, r) and key k of the tile is MFMA column k
   // The weights are normalized before the P·V product: the row sums come
-  // first (on the matrix cores, against a ones tile), then each lane scales
-  // its four weights by 1/l of its column, so the products land normalized.
+  // first (gist tiles on the matrix cores, against a ones tile, plus the
+  // token's own weight), then each lane scales its four weights by 1/l of
+  // its column, so the products land normalized.
   const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
   const float sl2 = a.scale_log2, nmx = -mx * sl2;
-  float w[NT][4];
+  const float wself = __builtin_amdgcn_exp2f(__builtin_fmaf(sself, sl2, nmx));
+  float w[NGT][4];
   f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    if (kt == 0 || kt < ngt || kt == NGT) {
+  for (int kt = 0; kt < NGT; ++kt) {
+    if (kt == 0 || kt < ngt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         w[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], sl2, nmx));
@@ -943,22 +1082,35 @@ gist_fwd_eos(const FwdArgs a) {
       lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
     }
   }
-  const float inv = __builtin_amdgcn_rcpf(lacc[0]);
+  const float inv = __builtin_amdgcn_rcpf(lacc[0] + wself);
   const float invi = FP8 ? inv * svi : inv, invq = FP8 ? inv * svq : inv;
+  // the token's own value row, by fp32 FMAs: lane (n, q4) holds output
+  // channels 32s + 8*q4 .. +7 of column n (see the stores below)
   f32x4_t o[NDT];
+  {
+    const float ws = wself * inv;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NS; ++s) {
+      const uint2* src = (const uint2*)(Rl + vrow_off(VSELF, 32 * s + 8 * q4, D));
+      float v[8];
+      unpack8(make_uint4(src[0].x, src[0].y, src[1].x, src[1].y), v);
 #pragma unroll
-  for (int kt = 0; kt < NT; ++kt) {
-    if (kt == 0 || kt < ngt || kt == NGT) {
+      for (int r = 0; r < 4; ++r) {
+        o[2 * s][r] = ws * v[r];
+        o[2 * s + 1][r] = ws * v[4 + r];
+      }
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < NGT; ++kt) {
+    if (kt == 0 || kt < ngt) {
       float wn[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        wn[r] = w[kt][r] * (kt == NGT ? inv : (16 * kt + 4 * q4 + r < a.k ? invi : invq));
+        wn[r] = w[kt][r] * (16 * kt + 4 * q4 + r < a.k ? invi : invq);
       const bf16x4v pv =
           __builtin_bit_cast(bf16x4v, make_uint2(pack2_bf16(wn[0], wn[1]), pack2_bf16(wn[2], wn[3])));
-      // the self tile has one key: every lane reads the V_new row
-      const int R = kt == NGT ? VSELF : 16 * kt + (lane >> 2);
+      const int R = 16 * kt + (lane >> 2);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int ch = 32 * (dt >> 1) + 4 * (dt & 1) + 8 * (lane & 3);
@@ -1313,7 +1465,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
 
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  if ((pool->dtype == GIST_BF16 || fp8) && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 104 KiB per workgroup
+  if ((pool->dtype == GIST_BF16 || fp8) && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 116 KiB per workgroup
     const dim3 grid((unsigned)((int64_t)P * H));
     auto go = [&](auto last_c) {
     constexpr bool L = decltype(last_c)::value;
@@ -1324,7 +1476,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     if (fp8) {
       // fp8 pools: the common group sizes at compile time (no Q row past the
       // group is loaded), the rest with the group size from the arguments
-      const size_t lds5 = MfmaLds<64, 5>::bytes(nk_pad, ell);
+      const size_t lds5 = MfmaLds<64, 5>::bytes(nk_pad);
       if (d == 64 && nkt <= 5 && G == 7 && one_gen)
         hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
       else if (d == 64 && nkt <= 5 && G == 7)
@@ -1334,24 +1486,24 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
       else if (d == 64 && nkt <= 5 && G == 8)
         hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
       else if (d == 64 && nkt <= 5)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
       else if (d == 64)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, true>), grid, dim3(256),
+                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
       else if (nkt <= 5 && G == 8)
         hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
+                           (MfmaLds<128, 5>::bytes(nk_pad)), s, a, nk_pad);
       else if (nkt <= 5)
         hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 5>::bytes(nk_pad, ell)), s, a, nk_pad);
+                           (MfmaLds<128, 5>::bytes(nk_pad)), s, a, nk_pad);
       else
         hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
       return;
     }
     if (d == 64) {
       if (nkt <= 5) {
-        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad, ell);
+        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
         // When the whole grid is resident at once (four workgroups per CU),
         // every workgroup issues its staging loads at the same moment and a
         // deeper Q prefetch only delays them: prefetch one head ahead.  With
@@ -1365,14 +1517,14 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
         else if (G == 8)
           hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
         else
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 4, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
+          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 2, 0, L, false>), grid, dim3(256),
-                           (MfmaLds<64, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, false>), grid, dim3(256),
+                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
       }
     } else {
       if (nkt <= 5) {
-        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad, ell);
+        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
         // a compile-time group size loads no Q row past the group (the
         // generic instance's clamped ring refills re-read the last head)
         if (G == 8)
@@ -1381,7 +1533,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
           hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
       } else {
         hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, false>), grid, dim3(256),
-                           (MfmaLds<128, 8>::bytes(nk_pad, ell)), s, a, nk_pad);
+                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
       }
     }
     };

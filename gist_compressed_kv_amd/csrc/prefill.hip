@@ -9,10 +9,15 @@
 // tokens after the gist, and none are present.
 //
 // Two launches per call:
-//   prefill_prep   rotates every K row at its own position (bf16, into the
-//                  caller's workspace) and, for the last k rows of each
-//                  sequence, writes K rotated at 1..k and V into the pool;
+//   prefill_prep   rotates every K row at its own position (a bf16 pair hi +
+//                  lo, into the caller's workspace) and, for the last k rows
+//                  of each sequence, writes K rotated at 1..k and V into the
+//                  pool;
 //   prefill_attn   causal attention (MFMA), Q rotated on load.
+// Precision: the rotated Q (times the softmax scale and log2 e) and the
+// rotated K are each carried as bf16 pairs hi + lo, and the logits take
+// K_hi·Q_hi + K_hi·Q_lo + K_lo·Q_hi, which holds the fp32 rotation to about
+// 2^-16 of |q||k|; P is rounded to bf16 for the P·V product.
 // K is rotated once in the first launch: every query block and every query
 // head of the group reads it again, and rotating it there would repeat the
 // rotation Hq/H times per query block.
@@ -27,7 +32,7 @@ struct PrefillArgs {
   const bf16_t* k;      // [T][H][d], not rotated
   const bf16_t* v;      // [T][H][d]
   const int32_t* seq_start;  // [B + 1]
-  bf16_t* k_rot;        // workspace [T][H][d]
+  bf16_t* k_rot;        // workspace [2][T][H][d]: rotated K, hi then lo
   bf16_t* out;          // [T][Hq][d]
   int64_t T;
   int B, max_len, Hq, H, G;
@@ -50,11 +55,22 @@ __device__ __forceinline__ bool seq_bounds(const PrefillArgs& a, int b, int64_t&
   return true;
 }
 
+// Split fp32 values into a bf16 pair hi + lo: hi the nearest bf16 of x, lo
+// the nearest bf16 of x - hi (exact in fp32).
+__device__ __forceinline__ void split8(const float* y, uint4& hi, uint4& lo) {
+  hi = pack8_bf16(y);
+  float h[8], r[8];
+  unpack8(hi, h);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = y[e] - h[e];
+  lo = pack8_bf16(r);
+}
+
 // One thread per (sequence b, token t, KV head g, chunk pair c): channels
 // 8c..8c+7 and their RoPE partners d/2 + 8c..  K is rotated at position t+1
-// and rounded to bf16 (the rounding point of a RoPE-then-attention pipeline);
-// a gist row i (the last k of the sequence) is also rotated at its canonical
-// position 1+i and stored with its V in the pool record of item_ids[b].
+// and stored as a bf16 pair hi + lo; a gist row i (the last k of the
+// sequence) is also rotated at its canonical position 1+i and stored, rounded
+// to bf16, with its V in the pool record of item_ids[b].
 template <int D>
 __global__ void __launch_bounds__(256) prefill_prep(const PrefillArgs a) {
   constexpr int CP = D / 16;  // chunk pairs per row
@@ -72,7 +88,8 @@ __global__ void __launch_bounds__(256) prefill_prep(const PrefillArgs a) {
   float xl[8], xh[8];
   unpack8(*(const uint4*)(a.k + row + 8 * c), xl);
   unpack8(*(const uint4*)(a.k + row + D / 2 + 8 * c), xh);
-  auto rotate_store = [&](double pos, bf16_t* dst) {
+  // lo_dst: where the bf16 remainders go (nullptr: rounded to bf16 only)
+  auto rotate_store = [&](double pos, bf16_t* dst, bf16_t* lo_dst) {
     float yl[8], yh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -81,16 +98,23 @@ __global__ void __launch_bounds__(256) prefill_prep(const PrefillArgs a) {
       yl[e] = __builtin_fmaf(xl[e], cs, -(xh[e] * sn));
       yh[e] = __builtin_fmaf(xh[e], cs, xl[e] * sn);
     }
-    *(uint4*)(dst + 8 * c) = pack8_bf16(yl);
-    *(uint4*)(dst + D / 2 + 8 * c) = pack8_bf16(yh);
+    uint4 hl, ll, hh, lh;
+    split8(yl, hl, ll);
+    split8(yh, hh, lh);
+    *(uint4*)(dst + 8 * c) = hl;
+    *(uint4*)(dst + D / 2 + 8 * c) = hh;
+    if (lo_dst) {
+      *(uint4*)(lo_dst + 8 * c) = ll;
+      *(uint4*)(lo_dst + D / 2 + 8 * c) = lh;
+    }
   };
-  rotate_store((double)(t + 1), a.k_rot + row);
+  rotate_store((double)(t + 1), a.k_rot + row, a.k_rot + a.T * a.H * D + row);
   if (a.pool != nullptr && len >= a.kk && t >= len - a.kk) {
     const int32_t item = a.item_ids[b];
     if (item < 0 || item >= a.N) return;  // out-of-range destination: skipped
     const int i = (int)(t - (len - a.kk));
     bf16_t* rec = a.pool + (int64_t)item * 2 * a.H * a.kk * D;
-    rotate_store((double)(1 + i), rec + ((int64_t)g * a.kk + i) * D);
+    rotate_store((double)(1 + i), rec + ((int64_t)g * a.kk + i) * D, nullptr);
     bf16_t* vdst = rec + ((int64_t)(a.H + g) * a.kk + i) * D;
     *(uint4*)(vdst + 8 * c) = *(const uint4*)(a.v + row + 8 * c);
     *(uint4*)(vdst + D / 2 + 8 * c) = *(const uint4*)(a.v + row + D / 2 + 8 * c);
@@ -114,9 +138,10 @@ __device__ __forceinline__ float xmax16(float x) {
 // Causal attention, flash style.  Workgroup = 128 query tokens of one
 // sequence and one query head; wave w holds tokens q0 + 32w .. +31 as two
 // 16-token MFMA column tiles.  Key blocks of 32 tokens are staged in LDS (K
-// rotated, from the workspace; V) with the next block's loads in flight
-// while the current one is computed.  Per key block and column tile:
-//   Sᵀ = K·Qᵀ       two 16-key tiles, v_mfma_f32_16x16x32_bf16 (keys are
+// rotated, hi and lo, from the workspace; V) with the next block's loads in
+// flight while the current one is computed.  Per key block and column tile:
+//   Sᵀ = K·Qᵀ       two 16-key tiles, three v_mfma_f32_16x16x32_bf16 per
+//                   32 channels (K_hi·Q_hi + K_hi·Q_lo + K_lo·Q_hi; keys are
 //                   MFMA rows, so a lane's logits belong to its own query and
 //                   the softmax weights are the B operand of the P·V product)
 //   l += Pᵀ·1, Oᵀ += Vᵀ·Pᵀ   v_mfma_f32_16x16x32_bf16 over all 32 keys: K-index
@@ -145,6 +170,7 @@ prefill_attn(const PrefillArgs a) {
   constexpr int SU = BN * CPR / 256;  // staging chunks per thread per tensor
   static_assert(SU >= 1 && BN * CPR % 256 == 0, "staging layout");
   __shared__ __align__(16) bf16_t Ks[BN * KS];
+  __shared__ __align__(16) bf16_t Kl[BN * KS];
   // V row r holds channel ch at vpos(ch): the four channels that a lane of
   // the transposed read takes for output tile dt sit at 16 dt + 4 (lane & 3),
   // so the four lanes of a row read 32 contiguous bytes
@@ -172,9 +198,10 @@ prefill_attn(const PrefillArgs a) {
   const bool wave_active = qw < len;
 
   // ---- Q of the wave's two column tiles, rotated at t+1 and multiplied by
-  // scale * log2(e) (the logits then come out in log2 units), MFMA B layout --
+  // scale * log2(e) (the logits then come out in log2 units), as bf16 pairs
+  // hi + lo in the MFMA B layout --------------------------------------------
   const float sl2 = a.scale_log2;
-  bf16x8_t qf[2][NS];
+  bf16x8_t qf[2][NS], qfl[2][NS];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int t = min(qw + 16 * ct + n, len - 1);
@@ -194,8 +221,13 @@ prefill_attn(const PrefillArgs a) {
         yl[e] = __builtin_fmaf(xl[e], cs, -(xh[e] * sn)) * sl2;
         yh[e] = __builtin_fmaf(xh[e], cs, xl[e] * sn) * sl2;
       }
-      qf[ct][s] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yl));
-      qf[ct][s + NP] = __builtin_bit_cast(bf16x8_t, pack8_bf16(yh));
+      uint4 hl, ll, hh, lh;
+      split8(yl, hl, ll);
+      split8(yh, hh, lh);
+      qf[ct][s] = __builtin_bit_cast(bf16x8_t, hl);
+      qfl[ct][s] = __builtin_bit_cast(bf16x8_t, ll);
+      qf[ct][s + NP] = __builtin_bit_cast(bf16x8_t, hh);
+      qfl[ct][s + NP] = __builtin_bit_cast(bf16x8_t, lh);
     }
   }
 
@@ -203,11 +235,12 @@ prefill_attn(const PrefillArgs a) {
   // rows past the sequence read its last row (masked: they follow every
   // query of the workgroup) -------------------------------------------------
   const bf16_t* kseq = a.k_rot + (s0 * a.H + g) * D;
+  const bf16_t* klseq = kseq + a.T * a.H * D;
   const bf16_t* vseq = a.v + (s0 * a.H + g) * D;
   // element offsets inside the sequence fit 32 bits (len * H * d < 2^31 is
   // checked on the host) and rows times the row stride fit a 24-bit product
   const unsigned rstride = (unsigned)(a.H * D);
-  u32x4_t kst[SU], vst[SU];
+  u32x4_t kst[SU], klst[SU], vst[SU];
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < SU; ++i) {
@@ -215,6 +248,7 @@ prefill_attn(const PrefillArgs a) {
       const unsigned r = (unsigned)min(BN * kb + u / CPR, len - 1), c = u % CPR;
       const unsigned e = __umul24(r, rstride) + 8 * c;
       kst[i] = *(const u32x4_t*)(kseq + e);
+      klst[i] = *(const u32x4_t*)(klseq + e);
       vst[i] = *(const u32x4_t*)(vseq + e);
     }
   };
@@ -224,6 +258,7 @@ prefill_attn(const PrefillArgs a) {
       const int u = tid + 256 * i;
       const int r = u / CPR, c = u % CPR;
       *(u32x4_t*)(Ks + r * KS + 8 * c) = kst[i];
+      *(u32x4_t*)(Kl + r * KS + 8 * c) = klst[i];
       // channels 8c..8c+3 go to vpos(8c) = 32 (c >> 2) + 4 (c & 3), and
       // 8c+4..8c+7 sixteen elements further
       bf16_t* vrow = Vs + r * KS + 32 * (c >> 2) + 4 * (c & 3);
@@ -262,16 +297,21 @@ prefill_attn(const PrefillArgs a) {
     f32x4_t sacc[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      bf16x8_t kf[NS];
+      bf16x8_t kf[NS], kfl[NS];
 #pragma unroll
-      for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s) {
         kf[s] = *(const bf16x8_t*)(Ks + (16 * kt + n) * KS + 32 * s + 8 * q4);
+        kfl[s] = *(const bf16x8_t*)(Kl + (16 * kt + n) * KS + 32 * s + 8 * q4);
+      }
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         f32x4_t acc = negm[ct];
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+        for (int s = 0; s < NS; ++s) {
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[ct][s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qfl[ct][s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfl[s], qf[ct][s], acc, 0, 0, 0);
+        }
         sacc[ct][kt] = acc;
       }
     }
@@ -392,7 +432,7 @@ using namespace gist;
 
 extern "C" size_t gist_prefill_workspace_bytes(int64_t n_tokens, int H, int d) {
   if (n_tokens < 0 || H <= 0 || d <= 0) return 0;
-  return (size_t)n_tokens * H * d * sizeof(bf16_t);
+  return 2 * (size_t)n_tokens * H * d * sizeof(bf16_t);
 }
 
 extern "C" gist_status gist_prefill_attn(const void* q, const void* k, const void* v,

@@ -151,8 +151,14 @@ gist_status gist_pool_write(const gist_pool* pool, int layer, const int32_t* ids
  * With ell == 1 the codes enter the matrix products exactly, a key's K scale
  * multiplies its fp32 logit and its V scale its softmax weight in the product
  * with V (the softmax denominator takes the unscaled weight).  With ell >= 2
- * each gist element, decode(code) * scale in fp32, is rounded to bf16 once
- * as it is staged.
+ * each gist K element, decode(code) * scale in fp32, is staged as a bf16
+ * pair (see Precision) and each gist V element is rounded to bf16 once.
+ * Precision (bf16 MFMA and EOS kernels): the rotated Q and the rotated
+ * K_new are carried as bf16 pairs hi + lo, hi the nearest bf16 value and lo
+ * the nearest bf16 value of the remainder, and each logit takes
+ * K_hi·Q_hi + K_hi·Q_lo + K_lo·Q_hi on the matrix cores with fp32
+ * accumulation, about 2^-16 of |q||k|.  The softmax weights are rounded to
+ * bf16 for the product with V.  The VALU kernel computes in fp32.
  */
 gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P,
                               int ell, int Hq, const void* q, const void* k_new,
@@ -232,8 +238,10 @@ gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32
 
 /*
  * gist_prefill_workspace_bytes — bytes of the workspace gist_prefill_attn
- * needs for n_tokens packed tokens, H KV heads and head size d (every K row
- * rotated, bf16).  Returns 0 for invalid shapes.
+ * needs for n_tokens packed tokens, H KV heads and head size d: every K row
+ * rotated, as a pair of bf16 arrays (the nearest bf16 values and the bf16
+ * roundings of their remainders), 2 * n_tokens * H * d * 2 bytes.  Returns 0
+ * for invalid shapes.
  */
 size_t gist_prefill_workspace_bytes(int64_t n_tokens, int H, int d);
 
@@ -256,7 +264,7 @@ size_t gist_prefill_workspace_bytes(int64_t n_tokens, int H, int d);
  *              softmax(scale * q_t·K^T) V over its keys 0..t
  *   workspace  device buffer of >= gist_prefill_workspace_bytes(n_tokens, H,
  *              d) bytes, 16-byte aligned; receives every K row rotated at
- *              its position (the K the attention reads)
+ *              its position, as a bf16 pair (the K the attention reads)
  *   pool, layer, item_ids  optional bf16 gist pool with the call's H and d:
  *              the K of the last pool->k tokens of sequence b, rotated at
  *              1..k, and their V are stored at item item_ids[b] (device int32

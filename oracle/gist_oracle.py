@@ -35,11 +35,6 @@ library makes identically):
 * Query head h reads KV head h // (Hq/H) (contiguous GQA groups).
 * A query token sees every gist key and the new keys up to and including
   itself; a decode token sees the whole cache and itself.
-* bf16 rounding points (used only when asked for, by ``round_rotated``): the
-  rotated Q and the rotated new K are rounded to bf16, as an unfused
-  RoPE-then-attention pipeline stores them; the stored gist K and every V
-  are bf16 inputs already.  For the prefill the rounded Q may carry a factor
-  (``q_factor``: the softmax scale folded into Q before its rounding).
 * fp8 storage (the pages name KV quantization as a lever but fix no scheme):
   OCP FP8 E4M3 codes with one fp32 scale per block (a paged-cache (block,
   head); a gist pool's (item, K or V, head)), scale = amax / 448, codes the
@@ -129,16 +124,6 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, mask: np.ndarray,
     return w @ v
 
 
-def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Nearest bfloat16 value (8 significant bits, ties to even) of each
-    element, returned in fp64.  frexp gives x = m * 2**e with 0.5 <= |m| < 1,
-    so m * 2**8 carries exactly the 8 significant bits; numpy rounds half to
-    even."""
-    x = np.asarray(x, np.float64)
-    m, e = np.frexp(x)
-    return np.ldexp(np.round(m * 256.0), e - 8)
-
-
 def gist_online_mask(n_gist: int, ell: int) -> np.ndarray:
     """Mask of the online sequence [gist (n_gist) ; new tokens (ell)].
 
@@ -151,36 +136,32 @@ def gist_online_mask(n_gist: int, ell: int) -> np.ndarray:
 
 def gist_pair_attention(gist_k: np.ndarray, gist_v: np.ndarray,
                         q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
-                        pos0: int, base: float, scale: float,
-                        round_rotated: bool = False) -> np.ndarray:
+                        pos0: int, base: float, scale: float) -> np.ndarray:
     """One (item, query) pair, one query head ([GIST] "在线的一次 attention").
 
     gist_k, gist_v: [n_gist, d], K already rotated at its canonical
     positions.  q, k_new, v_new: [ell, d], not yet rotated; they sit at
     positions pos0 .. pos0+ell-1.  Keys are cat(gist, new); values likewise.
-    With round_rotated the rotated Q and new K are rounded to bf16 first.
     """
     ell = q.shape[0]
     n_gist = gist_k.shape[0]
     pos = pos0 + np.arange(ell)
-    rnd = round_bf16 if round_rotated else (lambda x: x)
-    keys = np.concatenate([gist_k, rnd(rope(k_new, pos, base))], axis=0)
+    keys = np.concatenate([gist_k, rope(k_new, pos, base)], axis=0)
     vals = np.concatenate([gist_v, v_new], axis=0)
-    return attention(rnd(rope(q, pos, base)), keys, vals,
+    return attention(rope(q, pos, base), keys, vals,
                      gist_online_mask(n_gist, ell), scale)
 
 
 def gist_attn_forward(pool: np.ndarray, layer: int, item_ids, q: np.ndarray,
                       k_new: np.ndarray, v_new: np.ndarray, pos0: int,
                       base: float, scale: float, qpool: np.ndarray | None = None,
-                      q_ids=None, round_rotated: bool = False) -> np.ndarray:
+                      q_ids=None) -> np.ndarray:
     """Gist attention of a batch of pairs in one layer.
 
     pool:  [L][N][2][H][k][d]  (index 0 of the third axis = K, 1 = V)
     q:     [P][ell][Hq][d];  k_new, v_new: [P][ell][H][d]
     qpool: optional query-gist pool [L][Nq][2][H][k'][d], row q_ids[p]; its
            rows follow the item gist in key order ([GIST] "能不能再进一步").
-    round_rotated: round the rotated Q and new K to bf16 (see the header).
     Returns [P][ell][Hq][d].
     """
     pool = np.asarray(pool, np.float64)
@@ -204,7 +185,7 @@ def gist_attn_forward(pool: np.ndarray, layer: int, item_ids, q: np.ndarray,
                 gv = np.concatenate([gv, np.asarray(qpool[layer, qrow, 1, g], np.float64)], axis=0)
             out[p, :, h, :] = gist_pair_attention(
                 gk, gv, q[p, :, h, :], k_new[p, :, g, :], v_new[p, :, g, :],
-                pos0, base, scale, round_rotated)
+                pos0, base, scale)
     return out
 
 
@@ -261,18 +242,14 @@ def causal_mask(n: int) -> np.ndarray:
 
 
 def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, base: float,
-                      scale: float, round_rotated: bool = False,
-                      q_factor: float = 1.0) -> np.ndarray:
+                      scale: float) -> np.ndarray:
     """Causal self-attention of B packed sequences [item tokens ; gist tokens].
 
     q [T][Hq][d]; k, v [T][H][d], not rotated.  Sequence b is tokens
     seq_start[b] .. seq_start[b+1]-1, at positions 1..len.  Query head h reads
     KV head h // (Hq/H).  Over [item ; gist] alone the gist mask of training
     is the causal mask: it only removes item keys from tokens after the gist,
-    and none are present.  With round_rotated the rotated Q and K are rounded
-    to bf16 first; the Q rounded is the rotated Q times q_factor, divided by it
-    again after rounding (a pipeline that folds the softmax scale into Q rounds
-    that product).  Without rounding q_factor changes nothing.
+    and none are present.
     Returns out [T][Hq][d].
     """
     q = np.asarray(q, np.float64)
@@ -293,8 +270,6 @@ def prefill_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_start, ba
             g = hh // group
             qr = rope(q[s0:s1, hh], pos, base)
             kr = rope(k[s0:s1, g], pos, base)
-            if round_rotated:
-                qr, kr = round_bf16(qr * q_factor) / q_factor, round_bf16(kr)
             out[s0:s1, hh] = attention(qr, kr, v[s0:s1, g], mask, scale)
     return out
 

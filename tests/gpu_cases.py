@@ -78,9 +78,9 @@ class GistCase:
                                         self.kn[layer], self.vn[layer], self.pos0, ROPE_BASE,
                                         self.scale, qpool=self.qpool, q_ids=self.q_ids, out=out)
 
-    def oracle(self, layer, sample, rounded=False):
+    def oracle(self, layer, sample):
         """Oracle rows for the sampled pairs; only the referenced pool rows are
-        copied back.  rounded: round the rotated Q and new K to bf16 first."""
+        copied back."""
         sample = np.asarray(sample)
         idx = torch.as_tensor(sample, device=self.ids.device)
         ids = self.ids[idx].long()
@@ -92,8 +92,7 @@ class GistCase:
             qids = np.arange(len(sample))
         return O.gist_attn_forward(pool, 0, np.arange(len(sample)), f64(self.q[layer][idx]),
                                    f64(self.kn[layer][idx]), f64(self.vn[layer][idx]),
-                                   self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids,
-                                   round_rotated=rounded)
+                                   self.pos0, ROPE_BASE, self.scale, qpool=qpool, q_ids=qids)
 
     @staticmethod
     def _rows(pool, layer, rows):
@@ -104,8 +103,8 @@ class GistCase:
                                      pool.scales[layer][rows].cpu().numpy())[None]
         return f64(pool.storage[layer][rows])[None]
 
-    def max_err(self, layer, out, sample, rounded=False):
-        ref = self.oracle(layer, sample, rounded)
+    def max_err(self, layer, out, sample):
+        ref = self.oracle(layer, sample)
         got = f64(out[torch.as_tensor(np.asarray(sample), device=out.device)])
         assert np.isfinite(got).all(), "non-finite output"
         return float(np.abs(got - ref).max())
@@ -184,15 +183,12 @@ class PrefillCase:
         self.k = synth.randn((T, h, d), synth.tensor_seed(seed, 22), torch.bfloat16, device)
         self.v = synth.randn((T, h, d), synth.tensor_seed(seed, 23), torch.bfloat16, device)
         self.scale = 1.0 / math.sqrt(d)
-        # the kernel rounds the rotated Q times scale * log2(e) (an fp32
-        # product) to bf16; the rounded oracle rounds the same product
-        self.q_factor = float(np.float32(self.scale) * np.float32(1.4426950408889634))
 
     def run(self, out=None, pool=None, layer=0, item_ids=None):
         return G.gist_prefill_attn(self.q, self.k, self.v, self.seq_start, max(self.lens), ROPE_BASE,
                                    self.scale, out=out, pool=pool, layer=layer, item_ids=item_ids)
 
-    def oracle(self, seqs=None, rounded=False):
+    def oracle(self, seqs=None):
         """Oracle rows of the listed sequences, as (rows index, values)."""
         seqs = range(len(self.lens)) if seqs is None else seqs
         st = self.seq_start.cpu().numpy()
@@ -200,14 +196,13 @@ class PrefillCase:
         for b in seqs:
             s = slice(int(st[b]), int(st[b + 1]))
             ref = O.prefill_attention(f64(self.q[s]), f64(self.k[s]), f64(self.v[s]),
-                                      [0, self.lens[b]], ROPE_BASE, self.scale, round_rotated=rounded,
-                                      q_factor=self.q_factor)
+                                      [0, self.lens[b]], ROPE_BASE, self.scale)
             idx.append(np.arange(s.start, s.stop))
             vals.append(ref)
         return np.concatenate(idx), np.concatenate(vals)
 
-    def max_err(self, out, seqs=None, rounded=False):
-        idx, ref = self.oracle(seqs, rounded)
+    def max_err(self, out, seqs=None):
+        idx, ref = self.oracle(seqs)
         got = f64(out[torch.as_tensor(idx, device=out.device)])
         assert np.isfinite(got).all(), "non-finite output"
         return float(np.abs(got - ref).max())

@@ -238,7 +238,8 @@ def _pf(L, B=2, T=100, max_len=64, Hq=4, H=2, d=64, ptr=FAKE, ws=None, pool=None
 
 
 def test_prefill_validation(L):
-    assert L.gist_prefill_workspace_bytes(1000, 2, 64) == 1000 * 2 * 64 * 2
+    # the rotated K as a bf16 pair: two bf16 values per element
+    assert L.gist_prefill_workspace_bytes(1000, 2, 64) == 2 * 1000 * 2 * 64 * 2
     assert L.gist_prefill_workspace_bytes(-1, 2, 64) == 0
     assert _pf(L, B=-1) == _lib.GIST_ERR_INVALID_ARG
     assert _pf(L, max_len=0) == _lib.GIST_ERR_INVALID_ARG

@@ -503,43 +503,6 @@ def test_multi_token_block_equals_successive_decode_steps():
 
 
 # ---------------------------------------------------------------------------
-# bf16 rounding helper (used by the robustness parity cases)
-# ---------------------------------------------------------------------------
-
-
-def test_round_bf16_matches_torch_conversion():
-    # fp32-representable values: torch's fp32 -> bf16 conversion (round to
-    # nearest even) is an independent implementation of the same rounding
-    rng = np.random.default_rng(11)
-    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
-                        [0.0, -0.0, 1.0, -3.5]]).astype(np.float32)
-    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
-    np.testing.assert_array_equal(O.round_bf16(x.astype(np.float64)), ref)
-
-
-def test_round_bf16_ties_to_even():
-    # bf16 spacing just above 1 is 2**-7: halfway points go to the even
-    # significand, others to the nearest
-    assert O.round_bf16(np.array(1.0 + 2.0 ** -8)) == 1.0
-    assert O.round_bf16(np.array(1.0 + 3 * 2.0 ** -8)) == 1.0 + 2.0 ** -6
-    assert O.round_bf16(np.array(1.0 + 2.0 ** -8 + 2.0 ** -20)) == 1.0 + 2.0 ** -7
-    assert O.round_bf16(np.array(-(1.0 + 3 * 2.0 ** -8))) == -(1.0 + 2.0 ** -6)
-
-
-def test_round_rotated_changes_only_rounding():
-    # on bf16-representable inputs the rounded oracle differs from the exact
-    # one (the rotated values are not bf16 values), but only by what rounding
-    # the rotated Q and new K can move a softmax-weighted average
-    rng = np.random.default_rng(12)
-    gk, gv = rng.standard_normal((4, 8)), rng.standard_normal((4, 8))
-    q, kn, vn = (O.round_bf16(rng.standard_normal((3, 8))) for _ in range(3))
-    exact = O.gist_pair_attention(gk, gv, q, kn, vn, 5, 1e4, 0.35)
-    rounded = O.gist_pair_attention(gk, gv, q, kn, vn, 5, 1e4, 0.35, round_rotated=True)
-    assert not np.array_equal(exact, rounded)
-    assert np.abs(exact - rounded).max() < 2e-2
-
-
-# ---------------------------------------------------------------------------
 # fp8 (OCP E4M3) cache decode
 # ---------------------------------------------------------------------------
 
@@ -713,24 +676,6 @@ def test_prefill_sequences_are_independent_and_causal():
     out2 = O.prefill_attention(q2, k2, v2, st, 1e4, 0.5)
     assert np.array_equal(out2[:t + 1], out[:t + 1]) and not np.allclose(out2[t + 1:7], out[t + 1:7])
     assert np.array_equal(out2[7:], out[7:])
-
-
-def test_prefill_q_factor_moves_only_the_rounding_point():
-    # q_factor acts only inside the bf16 rounding of the rotated Q: the exact
-    # result ignores it, a power of two commutes with the rounding (the same
-    # result bit for bit), and another factor rounds a different product,
-    # which moves the output only by what rounding Q can move it
-    r = rng(43)
-    lens = [11, 6]
-    q, k, v, st = _packed(r, lens, 4, 2, 16)
-    exact = O.prefill_attention(q, k, v, st, 1e4, 0.25)
-    assert np.array_equal(O.prefill_attention(q, k, v, st, 1e4, 0.25, q_factor=0.18), exact)
-    rounded = O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True)
-    assert np.array_equal(
-        O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True, q_factor=0.125), rounded)
-    other = O.prefill_attention(q, k, v, st, 1e4, 0.25, round_rotated=True, q_factor=0.18)
-    assert not np.array_equal(other, rounded)
-    assert np.abs(other - exact).max() < 2e-2
 
 
 def test_gist_rows_equal_the_pool_write_of_the_prefill_keys():
