@@ -23,6 +23,7 @@ __all__ = [
     "gist_prefill_workspace_bytes",
     "gist_prefill_attn",
     "paged_decode_workspace_bytes", "paged_decode_attn", "paged_decode_attn_fp8",
+    "paged_decode_attn_noalloc",
 ]
 
 _DTYPES = {torch.bfloat16: GIST_BF16, torch.float32: GIST_F32}
@@ -397,4 +398,34 @@ def paged_decode_attn_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale:
         ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], max_blocks, ptrs[5], R, ptrs[6],
         ptrs[7], ptrs[8], ptrs[9], Hq, H, d, rope_base, scale, ptrs[10], ptrs[11],
         workspace.numel() * workspace.element_size(), _stream_ptr(stream)), "paged_decode_attn_fp8")
+    return out
+
+
+def paged_decode_attn_noalloc(k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, context_lens: torch.Tensor,
+                              q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                              positions: torch.Tensor, rope_base: float = 10000.0,
+                              scale: float | None = None, out: torch.Tensor | None = None,
+                              stream=None) -> torch.Tensor:
+    """paged_decode_attn with the library's own split-K scratch (no workspace;
+    the C call allocates nothing).  Calls that overlap on one GPU race."""
+    n_blocks, H, bs, d = k_cache.shape
+    R, Hq, _ = q.shape
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [R, max_blocks]")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    dt = k_cache.dtype
+    ptrs = _ptrs((k_cache, "k_cache", dt), (v_cache, "v_cache", dt, k_cache.shape),
+                 (block_table, "block_table", torch.int32, (R, max_blocks)),
+                 (context_lens, "context_lens", torch.int32, (R,)),
+                 (q, "q", dt, (R, Hq, d)), (k_new, "k_new", dt, (R, H, d)), (v_new, "v_new", dt, (R, H, d)),
+                 (positions, "positions", torch.int32, (R,)), (out, "out", dt, q.shape))
+    _lib.check(_lib.lib().paged_decode_attn_noalloc(
+        ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], max_blocks, ptrs[3], R, ptrs[4], ptrs[5], ptrs[6],
+        ptrs[7], Hq, H, d, _code(dt), rope_base, scale, ptrs[8], _stream_ptr(stream)),
+        "paged_decode_attn_noalloc")
     return out

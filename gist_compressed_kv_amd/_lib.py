@@ -59,6 +59,8 @@ SIGNATURES = {
     "paged_decode_attn_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp,
                                      _vp, _vp, _vp, _i32, _i32, _i32, _f32, _f32, _vp, _vp, _sz,
                                      _vp]),
+    "paged_decode_attn_noalloc": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp,
+                                         _vp, _i32, _i32, _i32, _i32, _f32, _f32, _vp, _vp]),
     "gist_last_error": (ctypes.c_char_p, []),
 }
 

@@ -23,6 +23,9 @@
 #include <type_traits>
 #include <utility>
 
+#include <mutex>
+#include <string>
+
 #include "common.hpp"
 
 namespace gist {
@@ -482,16 +485,60 @@ extern "C" size_t paged_decode_workspace_bytes(int R, int Hq, int max_blocks, in
   return (size_t)R * Hq * num_splits(max_blocks, block_size) * (d + kWsPad) * sizeof(float);
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned split-K scratch for paged_decode_attn_noalloc: one array per
+// GPU, alive until the process ends.  Host code never passes the array's name
+// to a kernel (in host code it is a host-side stand-in); it uses the device
+// address hipGetSymbolAddress returns, looked up once per device with that
+// device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
 namespace {
-// Shared by both entry points: fp8 selects the E4M3 cache with per-(block,
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure,
+// with the error recorded).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    set_error("paged_decode_attn_noalloc: no current HIP device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      set_error(std::string("paged_decode_attn_noalloc: hipGetSymbolAddress failed: ") +
+                hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+namespace {
+// Shared by the entry points: fp8 selects the E4M3 cache with per-(block,
 // KV head) scales (activations in bf16); `fn` names the entry point in errors.
+// use_scratch: the split-K partials go to the library's scratch array instead
+// of the caller's workspace (which is then ignored); every argument is checked
+// before the scratch address is looked up.
 gist_status decode_call(const char* fn, bool fp8, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale, int64_t n_blocks,
                         int block_size, const int32_t* block_table, int max_blocks,
                         const int32_t* context_lens, int R, const void* q, const void* k_new,
                         const void* v_new, const int32_t* positions, int Hq, int H, int d,
                         gist_dtype dtype, float rope_base, float scale, void* out,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        bool use_scratch = false) {
   clear_error();
   const std::string name(fn);
   if (dtype != GIST_BF16 && dtype != GIST_F32)
@@ -512,21 +559,31 @@ gist_status decode_call(const char* fn, bool fp8, const void* k_cache, const voi
     return fail(GIST_ERR_INVALID_ARG, name + ": rope_base must be positive");
   if (R == 0) return GIST_OK;
   if (!k_cache || !v_cache || !block_table || !context_lens || !q || !k_new || !v_new ||
-      !positions || !out || !workspace || (fp8 && (!k_scale || !v_scale)))
+      !positions || !out || (!use_scratch && !workspace) || (fp8 && (!k_scale || !v_scale)))
     return fail(GIST_ERR_INVALID_ARG, name + ": NULL pointer argument");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
-      !aligned16(v_new) || !aligned16(out) || !aligned16(workspace))
+      !aligned16(v_new) || !aligned16(out) || (!use_scratch && !aligned16(workspace)))
     return fail(GIST_ERR_INVALID_ARG, name + ": tensors must be 16-byte aligned");
   if (fp8 && ((((uintptr_t)k_scale) & 3) != 0 || (((uintptr_t)v_scale) & 3) != 0))
     return fail(GIST_ERR_INVALID_ARG, name + ": scales must be 4-byte aligned");
   const size_t need = paged_decode_workspace_bytes(R, Hq, max_blocks, block_size, d);
-  if (workspace_bytes < need)
+  if (use_scratch && need > kScratchBytes)
+    return fail(GIST_ERR_UNSUPPORTED, name + ": the call needs " + std::to_string(need) +
+                                          " bytes of split-K scratch, more than the " +
+                                          std::to_string(kScratchBytes) +
+                                          " the library holds (use paged_decode_attn with a "
+                                          "workspace)");
+  if (!use_scratch && workspace_bytes < need)
     return fail(GIST_ERR_INVALID_ARG, name + ": workspace too small (" +
                                           std::to_string(workspace_bytes) + " < " +
                                           std::to_string(need) + ")");
   const int nsplit = num_splits(max_blocks, block_size);
   if ((int64_t)R * H * nsplit > INT32_MAX)
     return fail(GIST_ERR_UNSUPPORTED, name + ": too many splits for one launch");
+  if (use_scratch) {
+    workspace = scratch_address();
+    if (!workspace) return GIST_ERR_HIP;
+  }
 
   DecodeArgs a;
   a.kc = k_cache;
@@ -598,4 +655,19 @@ extern "C" gist_status paged_decode_attn_fp8(const void* k_cache, const void* v_
                      n_blocks, block_size, block_table, max_blocks, context_lens, R, q, k_new,
                      v_new, positions, Hq, H, d, GIST_BF16, rope_base, scale, out, workspace,
                      workspace_bytes, stream);
+}
+
+extern "C" gist_status paged_decode_attn_noalloc(const void* k_cache, const void* v_cache,
+                                                 int64_t n_blocks, int block_size,
+                                                 const int32_t* block_table, int max_blocks,
+                                                 const int32_t* context_lens, int R,
+                                                 const void* q, const void* k_new,
+                                                 const void* v_new, const int32_t* positions,
+                                                 int Hq, int H, int d, gist_dtype dtype,
+                                                 float rope_base, float scale, void* out,
+                                                 void* stream) {
+  return decode_call("paged_decode_attn_noalloc", false, k_cache, v_cache, nullptr, nullptr,
+                     n_blocks, block_size, block_table, max_blocks, context_lens, R, q, k_new,
+                     v_new, positions, Hq, H, d, dtype, rope_base, scale, out, nullptr, 0, stream,
+                     true);
 }

@@ -340,6 +340,33 @@ gist_status paged_decode_attn_fp8(const void* k_cache, const void* v_cache, cons
                                   int Hq, int H, int d, float rope_base, float scale, void* out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * paged_decode_attn_noalloc — paged_decode_attn for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  It allocates
+ * nothing: the split-K partials go to a scratch array of 16 MiB that the
+ * library holds on each GPU it runs on until the process ends (its address is
+ * looked up once per device, on the first call with that device current).
+ *   Arguments, layouts, results and limits are those of paged_decode_attn
+ *   without the workspace; the results are identical to it.
+ *   A call whose partials need more than 16 MiB
+ *   (paged_decode_workspace_bytes(R, Hq, max_blocks, block_size, d) >
+ *   16 * 2^20) returns GIST_ERR_UNSUPPORTED before any HIP call; the 32
+ *   requests x 4096 tokens x 32 heads decode step needs 8.65 MB.
+ *   GIST_ERR_HIP if the scratch address cannot be obtained.
+ * Concurrency: every call on one GPU uses that GPU's one scratch array, so
+ * calls that may overlap on one GPU (other streams, other host threads) race
+ * and give wrong results; order them on one stream.  Nothing in the scratch
+ * needs clearing between calls: each call writes every partial it reads.
+ */
+gist_status paged_decode_attn_noalloc(const void* k_cache, const void* v_cache, int64_t n_blocks,
+                                      int block_size, const int32_t* block_table, int max_blocks,
+                                      const int32_t* context_lens, int R, const void* q,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* positions, int Hq, int H, int d,
+                                      gist_dtype dtype, float rope_base, float scale, void* out,
+                                      void* stream);
+
 /* gist_last_error — message of the last failed call on this thread ("" if none). */
 const char* gist_last_error(void);
 

@@ -170,6 +170,29 @@ def test_paged_decode_validation(L):
     assert _dec(L, R=0, ptr=None) == _lib.GIST_OK
 
 
+def _decn(L, R=2, Hq=4, H=2, d=64, bs=16, max_blk=4, nblk=8, dt=BF16, ptr=FAKE, scale=0.125):
+    return L.paged_decode_attn_noalloc(ptr, ptr, nblk, bs, ptr, max_blk, ptr, R, ptr, ptr, ptr,
+                                       ptr, Hq, H, d, dt, 1e4, scale, ptr, None)
+
+
+def test_paged_decode_noalloc_validation(L):
+    # every rejection happens on the host, before the scratch address is looked up
+    assert _decn(L, R=-1) == _lib.GIST_ERR_INVALID_ARG
+    assert _decn(L, Hq=5) == _lib.GIST_ERR_INVALID_ARG
+    assert _decn(L, d=96) == _lib.GIST_ERR_UNSUPPORTED
+    assert _decn(L, bs=24) == _lib.GIST_ERR_UNSUPPORTED
+    assert _decn(L, dt=FP8) == _lib.GIST_ERR_INVALID_ARG
+    assert _decn(L, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert "paged_decode_attn_noalloc" in L.gist_last_error().decode()
+    assert _decn(L, R=0, ptr=None) == _lib.GIST_OK
+    # 16 MiB of split-K partials at most: 32 x 32 x 16 splits fits, 64 x 32 x 64 does not
+    assert L.paged_decode_workspace_bytes(32, 32, 16, 256, 128) <= 16 << 20
+    assert L.paged_decode_workspace_bytes(64, 32, 64, 256, 128) > 16 << 20
+    assert _decn(L, R=64, Hq=32, H=32, d=128, bs=256, max_blk=64) == _lib.GIST_ERR_UNSUPPORTED
+    msg = L.gist_last_error().decode()
+    assert "scratch" in msg and str(16 << 20) in msg
+
+
 def _dec8(L, R=2, Hq=4, H=2, d=64, bs=16, max_blk=4, nblk=8, ws_bytes=None, ptr=FAKE, sptr=FAKE,
           scale=0.125):
     if ws_bytes is None:
