@@ -189,13 +189,21 @@ __device__ __forceinline__ int kchunk(int r, int c) {
 // significant bits.  The product q·k of two such pairs, taken as
 // qhi·khi + qlo·khi + qhi·klo on the matrix cores, has a relative error of
 // about 2^-16, against 2^-8 for the product of the rounded values.
+// Per pair of values: one conversion for hi, two bit operations to read its
+// halves back, two subtractions and one conversion for lo.
 __device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo) {
-  hi = pack8_bf16(y);
-  float h[8], r[8];
-  unpack8(hi, h);
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = y[e] - h[e];
-  lo = pack8_bf16(r);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w = pack2_bf16(y[2 * i], y[2 * i + 1]);
+    // opaque to the optimizer, which would otherwise convert y[2i] a second
+    // time to read the low half
+    asm volatile("" : "+v"(w));
+    h[i] = w;
+    l[i] = pack2_bf16(y[2 * i] - __uint_as_float(w << 16), y[2 * i + 1] - __uint_as_float(w & 0xffff0000u));
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
 // D: head_dim.  NKT: maximum number of 16-key tiles (keys <= 16*NKT).
@@ -599,20 +607,25 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // MFMA row m of tile j holds key 16*(nkt-1-j) + 15 - m; the S output slot
   // r of lane group q4 is row m = 4*q4 + r.  Visibility: key <= kg + t.
   const int lim = kg + t - (16 * (nkt - 1) + 15 - 4 * q4);  // key <= kg+t  <=>  -r - 16j <= lim
-  bool vis0[4], vis1[4];
+  // the causal bias of tiles j = 0 and 1 (0 or -inf per logit), the same for
+  // every head: computed once and used as the accumulators' initial value
+  f32x4_t bias0, bias1;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    vis0[r] = -r <= lim;
-    vis1[r] = -r - 16 <= lim;
+    bias0[r] = -r <= lim ? 0.f : -INFINITY;
+    bias1[r] = -r - 16 <= lim ? 0.f : -INFINITY;
   }
+  // (opaque, so the compiler keeps them in registers rather than rebuilding
+  // them for every head)
+  asm volatile("" : "+v"(bias0), "+v"(bias1));
   // ds_bpermute byte addresses of the lanes that hold the same token
   const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
   const float sl2 = a.scale_log2;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
-  const bf16x4v ones = {(__bf16)1.f, (__bf16)1.f, (__bf16)1.f, (__bf16)1.f};
-  bf16x8_t ones8;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones8[e] = (__bf16)1.f;
+  u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // eight bf16 1.0
+  asm volatile("" : "+v"(ones_w));
+  const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, ones_w);
+  const bf16x4v ones = __builtin_shufflevector(ones8, ones8, 0, 1, 2, 3);
 
   // Attention of one query head (Q in qh/ql), output rows of head hh.
   auto attend = [&](const int hh) {
@@ -622,11 +635,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
 #pragma unroll
     for (int j = 0; j < NKT; ++j) {
       if (j == 0 || j < nkt) {  // an active wave has at least one tile
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (j < 2) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = (j == 0 ? vis0[r] : vis1[r]) ? 0.f : -INFINITY;
-        }
+        f32x4_t acc = j == 0 ? bias0 : j == 1 ? bias1 : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const bf16x8_t kh = *(const bf16x8_t*)(Khi + koff[s] + 16 * D * j);
@@ -652,10 +661,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     // of the two tiles are and what two 8-byte reads of Vᵀ give the A
     // operand.  An unpaired last tile takes the 16x16x16 form.
     const float nmx = -mx * sl2;
-    f32x4_t o[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t o[NDT], lacc;
     auto weights = [&](int j) {
       float w[4];
 #pragma unroll
@@ -665,24 +671,36 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     auto vfrag = [&](int dt, int j) {
       return *(const bf16x4_t*)(vbase + (vt_off(vt_row(dt, 0), 0, VS) - vt_off(vt_row(0, 0), 0, VS)) + 16 * j);
     };
+    // tiles j, j + 1 through one 16x16x32 product; first: the accumulators
+    // start from zero (an inline constant, so nothing is zeroed beforehand)
+    auto pair = [&](int j, bool first) {
+      const uint2 p0 = weights(j), p1 = weights(j + 1);
+      const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y));
+      lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf, first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : lacc, 0, 0, 0);
 #pragma unroll
-    for (int j0 = 0; j0 < NKT; j0 += 2) {
-      if (j0 + 1 < NKT && j0 + 1 < nkt) {
-        const uint2 p0 = weights(j0), p1 = weights(j0 + 1);
-        const bf16x8_t pf = __builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y));
-        lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf, lacc, 0, 0, 0);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t vf = __builtin_shufflevector(vfrag(dt, j0), vfrag(dt, j0 + 1), 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[dt], 0, 0, 0);
-        }
-      } else if (j0 == 0 || j0 < nkt) {
-        const bf16x4v pf = __builtin_bit_cast(bf16x4v, weights(j0));
-        lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lacc, 0, 0, 0);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag(dt, j0), pf, o[dt], 0, 0, 0);
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8_t vf = __builtin_shufflevector(vfrag(dt, j), vfrag(dt, j + 1), 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o[dt], 0, 0, 0);
       }
+    };
+    auto single = [&](int j, bool first) {
+      const bf16x4v pf = __builtin_bit_cast(bf16x4v, weights(j));
+      lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : lacc, 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vfrag(dt, j), pf, first ? f32x4_t{0.f, 0.f, 0.f, 0.f} : o[dt], 0, 0, 0);
+    };
+    // tiles 0 (and 1) first, then the later pairs, then an unpaired last tile;
+    // the blocks after the first accumulate in place
+    if (nkt >= 2) pair(0, true);
+    else single(0, true);
+#pragma unroll
+    for (int j0 = 2; j0 + 1 < NKT; j0 += 2)
+      if (j0 + 1 < nkt) pair(j0, false);
+    if ((nkt & 1) && nkt >= 3) {
+#pragma unroll
+      for (int j = 2; j < NKT; j += 2)
+        if (j == nkt - 1) single(j, false);
     }
     // O tile back to the coalesced layout through the same buffer, then
     // whole-line non-temporal stores (the output is not read again here)
