@@ -77,7 +77,6 @@ def parse():
                              "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
                              "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-pairs", type=int, default=500)
     return ap.parse_args()
 
 
@@ -102,34 +101,206 @@ def measured_traffic(workload_name: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, wl, sample_pairs: int):
-    import numpy as np
+# ---------------------------------------------------------------------------
+# The fp64 oracle timed on the host (a baseline, not the target).  A seeded
+# sample of each workload is cut into tasks (one layer and a slice of its
+# pairs or requests), timed once on one thread and once on every core this
+# process may use: worker processes for the gist oracle (its Python loops hold
+# the interpreter), threads for decode and prefill (large numpy products).
+# BLAS runs one thread per task either way.
+# ---------------------------------------------------------------------------
+
+
+def _bits(t):
+    """A host copy of a tensor as numpy: bf16 as its uint16 bits (exact and
+    half the bytes of fp32), other dtypes as they are."""
     import torch
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    return t.numpy()
+
+
+def _f64(a):
+    """bf16 bits (uint16) or fp32 values as fp64 (exactly)."""
+    import numpy as np
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return np.asarray(a, np.float64)
+
+
+def _oracle_task(task):
+    """Run one oracle task (BLAS on one thread); returns its units of work."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import gist_oracle as O
 
-    sample = np.linspace(0, wl.pairs - 1, num=min(sample_pairs, wl.pairs)).astype(np.int64)
-    idx = torch.as_tensor(sample, device="cuda")
-
-    def f64(t):
-        return t.detach().to("cpu", torch.float64).numpy()
-
-    inputs = []
-    for li in range(wl.layers):
-        ids = case["ids"][idx].long()
-        pool = f64(case["pool"][li][ids])[None]
-        inputs.append((pool, f64(case["q"][li][idx]), f64(case["kn"][li][idx]),
-                       f64(case["vn"][li][idx])))
-    scale = 1.0 / math.sqrt(wl.d)
     with threadpool_limits(1):
+        if task["kind"] == "gist":
+            if task["fp8"]:
+                pool = O.dequantize_gist(*task["pool"])[None]
+                qpool = O.dequantize_gist(*task["qpool"])[None] if task["qpool"] is not None else None
+            else:
+                pool = _f64(task["pool"])[None]
+                qpool = _f64(task["qpool"])[None] if task["qpool"] is not None else None
+            n = pool.shape[1]
+            O.gist_attn_forward(pool, 0, np.arange(n), _f64(task["q"]), _f64(task["kn"]),
+                                _f64(task["vn"]), task["pos0"], 10000.0, task["scale"],
+                                qpool=qpool, q_ids=np.arange(n) if qpool is not None else None)
+            return n
+        if task["kind"] == "decode":
+            if task["fp8"]:
+                kc = O.dequantize_blocks(*task["kc"])
+                vc = O.dequantize_blocks(*task["vc"])
+            else:
+                kc, vc = _f64(task["kc"]), _f64(task["vc"])
+            O.paged_decode(kc, vc, task["table"], task["lens"], _f64(task["q"]), _f64(task["kn"]),
+                           _f64(task["vn"]), task["positions"], 10000.0, task["scale"])
+            return len(task["lens"])
+        if task["kind"] == "prefill":
+            O.prefill_attention(_f64(task["q"]), _f64(task["k"]), _f64(task["v"]), task["seq_start"],
+                                10000.0, task["scale"])
+            return int(task["seq_start"][-1])
+    raise ValueError(task["kind"])
+
+
+def _warm_worker(_):
+    # lowest priority: the workers must not slow the GPU launch loop
+    os.nice(19)
+    import numpy  # noqa: F401
+    import threadpoolctl  # noqa: F401
+
+    from oracle import gist_oracle  # noqa: F401
+    return 0
+
+
+def host_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+_ORACLE_POOL = None  # (pool, workers, warm-up result): started before the GPU is touched
+
+
+def start_oracle_pool():
+    """Start the oracle's worker processes (at most 16: a one-GPU share of a
+    box) from a process that has not touched the GPU yet; their interpreter
+    start-up and imports run while the GPU work goes on."""
+    global _ORACLE_POOL
+    import multiprocessing
+    n = max(1, min(len(os.sched_getaffinity(0)), 16))
+    # the workers inherit this environment: BLAS and OpenMP on one thread each
+    # (no idle thread pools spinning in sixteen processes)
+    keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in keys}
+    os.environ.update({k: "1" for k in keys})
+    try:
+        pool = multiprocessing.get_context("spawn").Pool(n)
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    _ORACLE_POOL = (pool, n, pool.map_async(_warm_worker, range(n)))
+
+
+def stop_oracle_pool():
+    global _ORACLE_POOL
+    if _ORACLE_POOL is not None:
+        _ORACLE_POOL[0].close()
+        _ORACLE_POOL[0].join()
+        _ORACLE_POOL = None
+
+
+def time_oracle(tasks, processes: bool):
+    """Seconds for all tasks on one thread, and on every core this process
+    may use (at most 16); returns (t1, tn, n).  processes: the worker pool
+    started by start_oracle_pool, else threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    t0 = time.perf_counter()
+    for task in tasks:
+        _oracle_task(task)
+    t1 = time.perf_counter() - t0
+    if processes:
+        pool, n, warm = _ORACLE_POOL
+        warm.get()
         t0 = time.perf_counter()
-        for pool, q, kn, vn in inputs:
-            O.gist_attn_forward(pool, 0, np.arange(len(sample)), q, kn, vn, wl.pos0, 10000.0, scale)
-        dt = time.perf_counter() - t0
-    return {"value": len(sample) / dt, "unit": "pairs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sample)} of {wl.pairs} pairs, all {wl.layers} layers, every head and "
-                      f"token; fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+        pool.map(_oracle_task, tasks, chunksize=1)
+        tn = time.perf_counter() - t0
+    else:
+        n = max(1, min(len(os.sched_getaffinity(0)), 16))
+        with ThreadPoolExecutor(n) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(_oracle_task, tasks))
+            tn = time.perf_counter() - t0
+    return t1, tn, n
+
+
+def baseline_record(unit, pass_units, pass_work, sample_work, t1, tn, n, sample, how):
+    """The oracle's throughput for whole passes: a pass yields pass_units
+    units (pairs, requests, tokens) from pass_work units of work (those per
+    layer, summed over the layers); sample_work of them took t1 s on one thread
+    and tn s on n cores."""
+    def rate(t):
+        return sample_work / t / pass_work * pass_units
+    return {"value": rate(tn), "unit": unit, "cores": n, "kind": "oracle",
+            "sample": f"{sample}; fp64 numpy, BLAS one thread per task; {how}; "
+                      f"{t1:.1f} s on one thread, {tn:.1f} s on {n}",
+            "one_thread": {"value": rate(t1), "unit": unit, "cores": 1},
+            "host": host_info()}
+
+
+def gist_baseline(wl, pool, ids, qs, kns, vns, n_sets, qpool=None, q_ids=None):
+    """cpu_baseline of a gist workload: a seeded sample of pairs in a sample
+    of layers (all layers where that stays near 10 s of one-thread work)."""
+    import numpy as np
+    import torch
+
+    if wl.d == 64:
+        layers = list(range(wl.layers))
+        npairs = wl.pairs if wl.layers == 1 else min(128, wl.pairs)
+    elif wl.ell > 1:
+        layers = sorted({0, wl.layers // 3, 2 * wl.layers // 3, wl.layers - 1})
+        npairs = 128
+    else:
+        layers = list(range(0, wl.layers, 4))
+        npairs = 128
+    g = torch.Generator().manual_seed(wl.seed * 7919 + 17)
+    sample = torch.randperm(wl.pairs, generator=g)[:npairs].sort().values
+    idx = sample.to(ids.device)
+    item = ids[idx].long()
+    qrow = q_ids[idx].long() if q_ids is not None else None
+    tasks = []
+    for li in layers:
+        si = li % n_sets
+        for c0 in range(0, npairs, 16):
+            sl = slice(c0, min(npairs, c0 + 16))
+            if pool.fp8:
+                prec = (_bits(pool.codes[li][item[sl]]), _bits(pool.scales[li][item[sl]]))
+                qrec = (_bits(qpool.codes[li][qrow[sl]]), _bits(qpool.scales[li][qrow[sl]])) if qpool else None
+            else:
+                prec = _bits(pool.storage[li][item[sl]])
+                qrec = _bits(qpool.storage[li][qrow[sl]]) if qpool else None
+            tasks.append({"kind": "gist", "fp8": pool.fp8, "pool": prec, "qpool": qrec,
+                          "q": _bits(qs[si][idx[sl]]), "kn": _bits(kns[si][idx[sl]]),
+                          "vn": _bits(vns[si][idx[sl]]), "pos0": wl.pos0,
+                          "scale": 1.0 / math.sqrt(wl.d)})
+    t1, tn, n = time_oracle(tasks, processes=True)
+    return baseline_record("pairs/s", wl.pairs, wl.pairs * wl.layers, npairs * len(layers), t1, tn, n,
+                           f"{npairs} of {wl.pairs} pairs (seeded) in layers "
+                           f"{layers if len(layers) < wl.layers else 'all ' + str(wl.layers)}, "
+                           f"every head and token", f"{len(tasks)} tasks of <= 16 pairs, worker processes")
 
 
 def copy_probe(args):
@@ -226,7 +397,7 @@ def paged_bench(args, fp8: bool = False):
     avg_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
     bytes_unit = decode_bytes_per_request_layer(wl, fp8)
     achieved = bytes_unit * wl.requests / avg_s / 1e9
-    print(json.dumps({
+    res = {
         "metric": "paged decode tokens/s (32 requests x 4096 cached tokens, 32 layers"
                   + (", fp8 E4M3 cache)" if fp8 else ")"),
         "value": wl.requests / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -241,7 +412,37 @@ def paged_bench(args, fp8: bool = False):
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic("paged_fp8" if fp8 else "paged"),
                      "bytes_per_unit": bytes_unit, "units_per_launch": wl.requests,
-                     "avg_launch_us": avg_s * 1e6}}), flush=True)
+                     "avg_launch_us": avg_s * 1e6}}
+    if not args.no_cpu_baseline:
+        import numpy as np
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        # every request in two layers, one task per (layer, request) holding
+        # the request's own blocks
+        layers_s = [0, wl.layers - 1]
+        tab = table.cpu().numpy()
+        tasks = []
+        for li in layers_s:
+            kc, vc, q, kn, vn, _ = layers[li]
+            for r in range(wl.requests):
+                blk = torch.as_tensor(tab[r], device=dev).long()
+                if fp8:
+                    kcr = (_bits(kc[0][blk]), _bits(kc[1][blk]))
+                    vcr = (_bits(vc[0][blk]), _bits(vc[1][blk]))
+                else:
+                    kcr, vcr = _bits(kc[blk]), _bits(vc[blk])
+                tasks.append({"kind": "decode", "fp8": fp8, "kc": kcr, "vc": vcr,
+                              "table": np.arange(wl.blocks_per_request)[None],
+                              "lens": np.array([wl.context]), "q": _bits(q[r:r + 1]),
+                              "kn": _bits(kn[r:r + 1]), "vn": _bits(vn[r:r + 1]),
+                              "positions": np.array([wl.context + 1]),
+                              "scale": 1.0 / math.sqrt(wl.d)})
+        t1, tn, n = time_oracle(tasks, processes=False)
+        res["cpu_baseline"] = baseline_record(
+            "tokens/s", wl.requests, wl.requests * wl.layers, wl.requests * len(layers_s), t1,
+            tn, n,
+            f"all {wl.requests} requests in layers {layers_s}, every head",
+            f"{len(tasks)} tasks (one per layer and request), threads")
+    print(json.dumps(res), flush=True)
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
@@ -259,7 +460,6 @@ def prefill_bench(args):
     a batch of items [item ; gist], with the gist rows stored into that
     layer's pool."""
     import torch
-    from threadpoolctl import threadpool_limits
 
     import gist_compressed_kv_amd as G
     from gist_compressed_kv_amd import synth
@@ -323,20 +523,28 @@ def prefill_bench(args):
                      "flops_per_launch": flops, "avg_launch_us": avg_s * 1e6},
     }
     if not args.no_cpu_baseline:
-        from oracle import gist_oracle as O
+        import numpy as np
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        nb = 4  # the first items, every layer
-        s1 = int(st[nb])
-        q, k, v = (t[:s1].to("cpu", torch.float64).numpy() for t in sets[0])
-        st_cpu = st[:nb + 1].cpu().numpy()
-        with threadpool_limits(1):
-            t0 = time.perf_counter()
-            for _ in range(wl.layers):
-                O.prefill_attention(q, k, v, st_cpu, 10000.0, scale)
-            dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": s1 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"items 0-{nb - 1} ({s1} tokens), all {wl.layers} layers; "
-                                         f"fp64 numpy, BLAS limited to 1 thread; {dt:.1f} s"}
+        # eight seeded items in four layers (each layer uses activation set
+        # layer % 2), one task per (layer, item)
+        g = torch.Generator().manual_seed(wl.seed * 7919 + 23)
+        items = torch.randperm(wl.items, generator=g)[:8].sort().values.tolist()
+        layers = [0, 7, 14, 23]
+        st_h = st.cpu().numpy()
+        tasks = []
+        for li in layers:
+            q, k, v = sets[li % 2]
+            for b in items:
+                s0, s1 = int(st_h[b]), int(st_h[b + 1])
+                tasks.append({"kind": "prefill", "q": _bits(q[s0:s1]), "k": _bits(k[s0:s1]),
+                              "v": _bits(v[s0:s1]), "seq_start": np.array([0, s1 - s0]),
+                              "scale": scale})
+        sample_tokens = sum(int(st_h[b + 1] - st_h[b]) for b in items) * len(layers)
+        t1, tn, n = time_oracle(tasks, processes=False)
+        res["cpu_baseline"] = baseline_record(
+            "tokens/s", T, T * wl.layers, sample_tokens, t1, tn, n,
+            f"items {items} ({sample_tokens // len(layers)} tokens) in layers {layers}, every head",
+            f"{len(tasks)} tasks (one per layer and item), threads")
     print(json.dumps(res), flush=True)
 
 
@@ -346,7 +554,15 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the gist path has no "
               "cross-GPU step in this build.", file=sys.stderr)
         sys.exit(2)
+    if not args.no_cpu_baseline and args.workload not in ("copy", "paged", "paged_fp8", "prefill"):
+        start_oracle_pool()  # before anything touches the GPU
+    try:
+        run(args)
+    finally:
+        stop_oracle_pool()
 
+
+def run(args):
     import torch
 
     if args.workload == "copy":
@@ -426,6 +642,15 @@ def main():
                                     qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
         passes[0] += 1
 
+    # the oracle baseline runs here, on the inputs just generated, and its
+    # worker processes are gone before the timed region: with them alive the
+    # host-side launch loop of the short-launch workloads ran up to 1.5x
+    # slower
+    cpu_base = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        cpu_base = gist_baseline(wl, pool, ids, qs, kns, vns, n_sets, qpool, q_ids)
+        stop_oracle_pool()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -434,17 +659,20 @@ def main():
     # HIP events on the launch stream bracket the region; every launch in it
     # runs the one kernel, back to back, so region time / launches is that
     # kernel's average launch duration
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # (an event after every pass as well, for the median pass)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / (args.steps * wl.layers)
+    avg_launch_s = evs[0].elapsed_time(evs[-1]) / 1e3 / (args.steps * wl.layers)
+    pass_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    median_pass_ms = pass_ms[len(pass_ms) // 2]
 
     bytes_unit = gist_bytes_per_pair_layer(wl)
     bytes_launch = bytes_unit * wl.pairs
@@ -494,15 +722,12 @@ def main():
             "bytes_per_unit": bytes_unit,
             "units_per_launch": wl.pairs,
             "avg_launch_us": avg_launch_s * 1e6,
+            "median_launch_us": median_pass_ms * 1e3 / wl.layers,
         },
+        "median_pass_ms": median_pass_ms,
     }
-    if not args.no_cpu_baseline:
-        case = {"pool": pool_t, "ids": ids, "q": qs, "kn": kns, "vn": vns}
-        if wl.kq or n_sets != wl.layers or last_layer_eos:
-            res["cpu_baseline"] = None
-        else:
-            print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-            res["cpu_baseline"] = cpu_baseline(case, wl, args.cpu_sample_pairs)
+    if cpu_base is not None:
+        res["cpu_baseline"] = cpu_base
     print(json.dumps(res), flush=True)
 
 
