@@ -31,7 +31,9 @@ class GistCase:
     """One layer-set of gist attention inputs on the GPU."""
 
     def __init__(self, layers, n_items, k, ell, hq, h, d, pairs, dtype, seed, kq=0,
-                 n_qrows=0, ids=None, q_ids=None, device="cuda", fp8=False):
+                 n_qrows=0, ids=None, q_ids=None, device="cuda", fp8=False, act_layers=None):
+        """act_layers: the layers that get activations (default: all); the
+        pools always hold every layer."""
         self.layers, self.n_items, self.k, self.ell = layers, n_items, k, ell
         self.hq, self.h, self.d, self.pairs, self.dtype, self.kq = hq, h, d, pairs, dtype, kq
         self.fp8 = fp8
@@ -59,11 +61,12 @@ class GistCase:
                                        dtype, device)
             self.qpool = G.GistPool(self.qpool_t)
             self.q_ids = q_ids.to(device=device, dtype=torch.int32)
-        self.q, self.kn, self.vn = [], [], []
-        for li in range(layers):
-            self.q.append(synth.randn((pairs, ell, hq, d), synth.tensor_seed(seed, 3, li), dtype, device))
-            self.kn.append(synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 4, li), dtype, device))
-            self.vn.append(synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 5, li), dtype, device))
+        self.act_layers = list(range(layers)) if act_layers is None else list(act_layers)
+        self.q, self.kn, self.vn = {}, {}, {}
+        for li in self.act_layers:
+            self.q[li] = synth.randn((pairs, ell, hq, d), synth.tensor_seed(seed, 3, li), dtype, device)
+            self.kn[li] = synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 4, li), dtype, device)
+            self.vn[li] = synth.randn((pairs, ell, h, d), synth.tensor_seed(seed, 5, li), dtype, device)
         self.pos0 = k + kq + 1
         self.scale = 1.0 / math.sqrt(d)
 

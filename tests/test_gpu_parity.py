@@ -26,7 +26,7 @@ def _cleanup():
 
 
 def check_gist(case, layers=None, sample=None, label=""):
-    layers = range(case.layers) if layers is None else layers
+    layers = case.act_layers if layers is None else layers
     worst = 0.0
     for li in layers:
         out = case.run(li)
@@ -147,37 +147,47 @@ def test_24_layer_workload_sampled(wl):
     check_gist(case, sample=sample, label=f"24 layers, {wl.pairs} pairs (sampled)")
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("hq", [14, 16], ids=["G7", "G8"])
-def test_several_workgroup_generations_sampled(hq):
+def test_several_workgroup_generations_sampled(hq, fp8):
     # 700 pairs x 2 KV heads = 1400 workgroups: more than the GPU holds at
     # once, which selects the deeper Q prefetch of the unrolled instances
-    case = GistCase(1, 3000, 8, 64, hq, 2, 64, 700, torch.bfloat16, 321 + hq)
+    # (bf16 and fp8 pools each have their own)
+    case = GistCase(1, 3000, 8, 64, hq, 2, 64, 700, torch.bfloat16, 321 + hq, fp8=fp8)
     sample = np.array([0, 1, 349, 511, 512, 698, 699])
-    check_gist(case, sample=sample, label=f"700 pairs, Hq={hq} (sampled)")
+    check_gist(case, sample=sample, label=f"700 pairs, Hq={hq}, {'fp8' if fp8 else 'bf16'} pool (sampled)")
+
+
+def _wide_sample(wl, seed):
+    # 32 seeded pairs plus the first and last two
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, wl.pairs - 2, wl.pairs - 1],
+                                     rng.choice(wl.pairs, 32, replace=False)]))
 
 
 def test_wide_ell64_workload_sampled():
     wl = synth.WIDE_ELL64
-    # two of the 28 layers, each with a full 100k-item pool layer
-    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
-                    ids=_ids(wl))
-    sample = np.array([0, 1, 777, wl.pairs - 1])
-    check_gist(case, sample=sample, label="wide ell=64, 2000 pairs (sampled)")
+    # the whole 28-layer pool (92 GB: layer 27's records lie past 2^31
+    # elements), activations for the first and the last layer
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed, ids=_ids(wl), act_layers=[0, wl.layers - 1])
+    check_gist(case, sample=_wide_sample(wl, 31), label="wide ell=64, 2000 pairs, layers 0 and 27 (sampled)")
 
 
 def test_wide_ell64_fp8_workload_sampled():
     wl = synth.WIDE_ELL64_FP8
-    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
-                    ids=_ids(wl), fp8=True)
-    sample = np.array([0, 1, 777, wl.pairs - 1])
-    check_gist(case, sample=sample, label="wide ell=64 over fp8 pools, 2000 pairs (sampled)")
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed, ids=_ids(wl), fp8=True, act_layers=[0, wl.layers - 1])
+    check_gist(case, sample=_wide_sample(wl, 32),
+               label="wide ell=64 over fp8 pools, 2000 pairs, layers 0 and 27 (sampled)")
 
 
 def test_wide_eos_query_gist_workload():
     wl = synth.WIDE_EOS
     qids = torch.arange(wl.pairs) // (wl.pairs // wl.queries)
-    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
-                    kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids)
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed, kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids,
+                    act_layers=[0, wl.layers - 1])
     rng = np.random.default_rng(7)
     sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 62)]))
     check_gist(case, sample=sample, label="wide EOS over item+query gist, 2000 pairs")
@@ -192,7 +202,7 @@ def test_paged_decode_workload():
     wl = synth.PAGED
     n_blocks = wl.requests * wl.blocks_per_request
     worst = 0.0
-    for layer in range(2):
+    for layer in (0, wl.layers - 1):
         case = DecodeCase(n_blocks, wl.h, wl.block_size, wl.d, wl.hq, [wl.context] * wl.requests,
                           wl.dtype, synth.tensor_seed(wl.seed, 0, layer),
                           table=synth.block_table(wl.requests, wl.blocks_per_request, n_blocks,
@@ -484,8 +494,9 @@ def test_eos_fp8_pool_shapes(shape):
 def test_wide_eos_fp8_workload_sampled():
     wl = synth.WIDE_EOS_FP8
     qids = torch.arange(wl.pairs) // (wl.pairs // wl.queries)
-    case = GistCase(2, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype, wl.seed,
-                    kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids, fp8=True)
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed, kq=wl.kq, n_qrows=wl.queries, ids=_ids(wl), q_ids=qids, fp8=True,
+                    act_layers=[0, wl.layers - 1])
     rng = np.random.default_rng(8)
     sample = np.unique(np.concatenate([[0, wl.pairs - 1], rng.integers(0, wl.pairs, 62)]))
     check_gist(case, sample=sample, label="wide EOS, fp8 item+query gist, 2000 pairs")
