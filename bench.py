@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b500_last", "24L_b2000", "1L_b500", "wide_ell64",
+                    choices=["24L_b500", "24L_b500_last", "24L_b2000", "1L_b500", "1L_b500_paged",
+                             "wide_ell64",
                              "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
                              "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -582,8 +583,8 @@ def run(args):
     # token's rows (what the score head reads)
     last_layer_eos = args.workload == "24L_b500_last"
     wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500, "24L_b2000": synth.L24_B2000,
-          "1L_b500": synth.SINGLE_LAYER, "wide_ell64": synth.WIDE_ELL64,
-          "wide_ell64_fp8": synth.WIDE_ELL64_FP8,
+          "1L_b500": synth.SINGLE_LAYER, "1L_b500_paged": synth.SINGLE_LAYER,
+          "wide_ell64": synth.WIDE_ELL64, "wide_ell64_fp8": synth.WIDE_ELL64_FP8,
           "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
     dev = "cuda"
     torch.cuda.init()
@@ -621,6 +622,13 @@ def run(args):
         kns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 4, li), wl.dtype, dev))
         vns.append(synth.randn((wl.pairs, wl.ell, wl.h, wl.d), synth.tensor_seed(wl.seed, 5, li), wl.dtype, dev))
         outs.append(torch.empty_like(qs[-1]))
+    # 1L_b500_paged: the same gists read from a paged cache of 16-row blocks,
+    # item i's gist in rows 0..k-1 of block i (the rest of each block unused)
+    paged = args.workload == "1L_b500_paged"
+    if paged:
+        kc = torch.zeros((wl.n_items, wl.h, 16, wl.d), dtype=wl.dtype, device=dev)
+        vc = torch.zeros_like(kc)
+        kc[:, :, :wl.k], vc[:, :, :wl.k] = pool_t[0, :, 0], pool_t[0, :, 1]
     q_lasts = [q[:, -1].contiguous() for q in qs] if last_layer_eos else None
     out_last = torch.empty_like(q_lasts[0]) if last_layer_eos else None
     torch.cuda.synchronize()
@@ -637,6 +645,9 @@ def run(args):
                 G.gist_attn_forward_last(pool, li, ids, q_lasts[si], kns[si], vns[si], wl.pos0,
                                          10000.0, scale, qpool=qpool, q_ids=q_ids, out=out_last,
                                          stream=stream)
+            elif paged:
+                G.gist_attn_forward_paged(kc, vc, ids, wl.k, qs[si], kns[si], vns[si], pos0=wl.pos0,
+                                          scale=scale, out=outs[si], stream=stream)
             else:
                 G.gist_attn_forward(pool, li, ids, qs[si], kns[si], vns[si], wl.pos0, 10000.0, scale,
                                     qpool=qpool, q_ids=q_ids, out=outs[si], stream=stream)
@@ -701,8 +712,9 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "data": "synthetic: N(0,1) pools" + (" (E4M3 codes, scale amax/448 per block)" if wl.fp8 else "")
-                + ", Q/K/V; seeded item ids (50 distinct candidates per query)",
-        "config": {"workload": wl.name, "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
+                + ", Q/K/V; seeded item ids (50 distinct candidates per query)"
+                + ("; gists read from a paged cache of 16-row blocks" if paged else ""),
+        "config": {"workload": wl.name + (", gists in a paged cache" if paged else ""), "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
                    "h": wl.h, "head_dim": wl.d, "k": wl.k, "k_query_gist": wl.kq, "ell": wl.ell,
                    "pool_items": wl.n_items, "parallelism": "single GPU"},
         "tokens_per_s": pairs_per_s * wl.ell,

@@ -217,18 +217,35 @@ def gist_attn_forward_last(pool: GistPool, layer: int, item_ids: torch.Tensor, q
     return out
 
 
+def _paged_shapes(k_cache, q, k_new):
+    """(n_blocks, H, block_size, d, P, ell, Hq, q shape, k_new shape) of a
+    paged-gist call: q is [P, Hq, d] (ell = 1) or [P, ell, Hq, d]."""
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [n_blocks, H, block_size, d]")
+    n_blocks, H, bs, d = k_cache.shape
+    if q.dim() == 3:
+        (P, Hq, _), ell = q.shape, 1
+        q_shape, kv_shape = (P, Hq, d), (P, H, d)
+    elif q.dim() == 4:
+        P, ell, Hq, _ = q.shape
+        q_shape, kv_shape = (P, ell, Hq, d), (P, ell, H, d)
+    else:
+        raise ValueError("q must be [P, Hq, d] or [P, ell, Hq, d]")
+    return n_blocks, H, bs, d, P, ell, Hq, q_shape, kv_shape
+
+
 def gist_attn_forward_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, item_blocks: torch.Tensor,
                             k: int, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                             query_blocks: torch.Tensor | None = None, kq: int = 0, q_row0: int = 0,
                             pos0: int | None = None, rope_base: float = 10000.0,
                             scale: float | None = None, out: torch.Tensor | None = None,
                             stream=None) -> torch.Tensor:
-    """EOS step over gists held in a paged cache: k_cache, v_cache bf16
+    """Gist attention over gists held in a paged cache: k_cache, v_cache bf16
     [n_blocks, H, block_size, d]; item gist = rows 0..k-1 of item_blocks[p],
-    query gist = rows q_row0..q_row0+kq-1 of query_blocks[p]; q [P, Hq, d],
-    k_new, v_new [P, H, d]; returns out [P, Hq, d]."""
-    n_blocks, H, bs, d = k_cache.shape
-    P, Hq, _ = q.shape
+    query gist = rows q_row0..q_row0+kq-1 of query_blocks[p]; q [P, Hq, d]
+    (the EOS step, ell = 1) or [P, ell, Hq, d], k_new and v_new [P, H, d] or
+    [P, ell, H, d]; returns out shaped like q."""
+    n_blocks, H, bs, d, P, ell, Hq, q_shape, kv_shape = _paged_shapes(k_cache, q, k_new)
     if pos0 is None:
         pos0 = k + kq + 1
     if scale is None:
@@ -239,10 +256,10 @@ def gist_attn_forward_paged(k_cache: torch.Tensor, v_cache: torch.Tensor, item_b
     ptrs = _ptrs((k_cache, "k_cache", bf), (v_cache, "v_cache", bf, k_cache.shape),
                  (item_blocks, "item_blocks", torch.int32, (P,)),
                  (query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
-                 (q, "q", bf, (P, Hq, d)), (k_new, "k_new", bf, (P, H, d)), (v_new, "v_new", bf, (P, H, d)),
+                 (q, "q", bf, q_shape), (k_new, "k_new", bf, kv_shape), (v_new, "v_new", bf, kv_shape),
                  (out, "out", bf, q.shape))
     _lib.check(_lib.lib().gist_attn_forward_paged(
-        ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], k, ptrs[3], kq, q_row0, P, Hq, H, d, ptrs[4],
+        ptrs[0], ptrs[1], n_blocks, bs, ptrs[2], k, ptrs[3], kq, q_row0, P, ell, Hq, H, d, ptrs[4],
         ptrs[5], ptrs[6], pos0, rope_base, scale, ptrs[7], _stream_ptr(stream)),
         "gist_attn_forward_paged")
     return out
@@ -258,9 +275,9 @@ def gist_attn_forward_paged_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """gist_attn_forward_paged over an fp8 cache: k_cache, v_cache uint8 E4M3
     codes [n_blocks, H, block_size, d]; k_scale, v_scale fp32 [n_blocks, H];
-    q [P, Hq, d], k_new, v_new [P, H, d] bf16; returns out [P, Hq, d]."""
-    n_blocks, H, bs, d = k_cache.shape
-    P, Hq, _ = q.shape
+    q, k_new, v_new bf16 as in gist_attn_forward_paged; returns out shaped
+    like q."""
+    n_blocks, H, bs, d, P, ell, Hq, q_shape, kv_shape = _paged_shapes(k_cache, q, k_new)
     if pos0 is None:
         pos0 = k + kq + 1
     if scale is None:
@@ -273,11 +290,11 @@ def gist_attn_forward_paged_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor,
                  (v_scale, "v_scale", torch.float32, (n_blocks, H)),
                  (item_blocks, "item_blocks", torch.int32, (P,)),
                  (query_blocks, "query_blocks", torch.int32, (P,)) if kq else None,
-                 (q, "q", bf, (P, Hq, d)), (k_new, "k_new", bf, (P, H, d)), (v_new, "v_new", bf, (P, H, d)),
+                 (q, "q", bf, q_shape), (k_new, "k_new", bf, kv_shape), (v_new, "v_new", bf, kv_shape),
                  (out, "out", bf, q.shape))
     _lib.check(_lib.lib().gist_attn_forward_paged_fp8(
-        ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], k, ptrs[5], kq, q_row0, P, Hq, H,
-        d, ptrs[6], ptrs[7], ptrs[8], pos0, rope_base, scale, ptrs[9], _stream_ptr(stream)),
+        ptrs[0], ptrs[1], ptrs[2], ptrs[3], n_blocks, bs, ptrs[4], k, ptrs[5], kq, q_row0, P, ell, Hq,
+        H, d, ptrs[6], ptrs[7], ptrs[8], pos0, rope_base, scale, ptrs[9], _stream_ptr(stream)),
         "gist_attn_forward_paged_fp8")
     return out
 

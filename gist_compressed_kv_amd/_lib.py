@@ -43,11 +43,11 @@ SIGNATURES = {
     "gist_attn_forward": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32,
                                  _f32, _vp, _vp, _vp, _vp]),
     "gist_attn_forward_paged": (_i32, [_vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32, _i32, _i32,
-                                       _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _f32, _vp,
-                                       _vp]),
+                                       _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32, _f32,
+                                       _vp, _vp]),
     "gist_attn_forward_paged_fp8": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _vp, _i32, _vp, _i32,
-                                           _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _f32,
-                                           _f32, _vp, _vp]),
+                                           _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
+                                           _f32, _f32, _vp, _vp]),
     "gist_attn_forward_last": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                       _f32, _f32, _vp, _vp, _vp, _vp]),
     "gist_prefill_workspace_bytes": (_sz, [_i64, _i32, _i32]),

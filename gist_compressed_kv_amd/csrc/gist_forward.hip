@@ -345,30 +345,55 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
     return;
   }
   typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
-  const C* gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-                (int64_t)g * a.k * D;
-  const C* qK = nullptr;
-  if (a.kq)
-    qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
-         (int64_t)g * a.kq * D;
+  // first K and V rows of the item gist and of the query gist: a pool record
+  // (K of every head, then V of every head), or rows of the item's and the
+  // query's blocks in a paged cache [N][H][block_size][d]
+  const C *gK, *gV, *qK = nullptr, *qV = nullptr;
+  if (a.paged) {
+    const int64_t ib = ((int64_t)item * a.H + g) * a.block_size * D;
+    gK = (const C*)a.paged_k + ib;
+    gV = (const C*)a.paged_v + ib;
+    if (a.kq) {
+      const int64_t qb = (((int64_t)qid * a.H + g) * a.block_size + a.q_row0) * D;
+      qK = (const C*)a.paged_k + qb;
+      qV = (const C*)a.paged_v + qb;
+    }
+  } else {
+    gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+         (int64_t)g * a.k * D;
+    gV = gK + (int64_t)a.H * a.k * D;
+    if (a.kq) {
+      qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+           (int64_t)g * a.kq * D;
+      qV = qK + (int64_t)a.H * a.kq * D;
+    }
+  }
   // fp8: K and V scales of the item gist and of the query gist (scalars)
   float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
   if constexpr (FP8) {
-    const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
-    ski = si[g];
-    svi = si[a.H + g];
-    if (a.kq) {
-      const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
-      skq = sq[g];
-      svq = sq[a.H + g];
+    if (a.paged) {
+      ski = a.paged_kscales[(int64_t)item * a.H + g];
+      svi = a.paged_vscales[(int64_t)item * a.H + g];
+      if (a.kq) {
+        skq = a.paged_kscales[(int64_t)qid * a.H + g];
+        svq = a.paged_vscales[(int64_t)qid * a.H + g];
+      }
+    } else {
+      const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+      ski = si[g];
+      svi = si[a.H + g];
+      if (a.kq) {
+        const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+        skq = sq[g];
+        svq = sq[a.H + g];
+      }
     }
   }
   // Eight gist elements (channels ch.., K or V of gist key j < kg) as fp32.
   // fp8 gist rows are decoded and multiplied by their block's scale.  Every
   // lane issues one 16-byte load (fp8: the aligned 16 codes that hold its 8).
   auto gist_row = [&](int j, bool v) -> const C* {
-    return j < a.k ? gK + (int64_t)((v ? a.H * a.k : 0) + j) * D
-                   : qK + (int64_t)((v ? a.H * a.kq : 0) + (j - a.k)) * D;
+    return j < a.k ? (v ? gV : gK) + (int64_t)j * D : (v ? qV : qK) + (int64_t)(j - a.k) * D;
   };
   auto gist_raw = [&](int j, bool v, int ch) -> u32x4_t {
     if constexpr (FP8) return *(const u32x4_t*)(gist_row(j, v) + (ch & ~15));
@@ -1399,6 +1424,80 @@ int device_cu_count() {
   return n;
 }
 
+// The l >= 2 kernel for a call's shape: head size, key tiles, gist element
+// type, group size (compile-time instances for the common ones) and Q
+// prefetch depth.
+template <bool L, bool F8>
+void launch_mfma_t(const FwdArgs& a, int d, int nk_pad, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)a.P * a.H));
+  const int nkt = nk_pad / 16;
+  const int G = a.G;
+  // When the whole grid is resident at once (four workgroups per CU), every
+  // workgroup issues its staging loads at the same moment and a deeper Q
+  // prefetch only delays them: prefetch one head ahead.  With several
+  // generations of workgroups, two heads ahead.  A compile-time group size
+  // loads no Q row past the group (the generic instance's clamped ring
+  // refills re-read the last head).
+  const bool one_gen = (int64_t)a.P * a.H <= 4 * (int64_t)device_cu_count();
+  if (d == 64 && nkt <= 5) {
+    const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
+    if (G == 7 && one_gen)
+      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    else if (G == 7)
+      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    else if (G == 8 && one_gen)
+      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    else if (G == 8)
+      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    else
+      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+  } else if (d == 64) {
+    hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, F8>), grid, dim3(256),
+                       (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
+  } else if (nkt <= 5) {
+    const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
+    if (G == 8)
+      hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    else
+      hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+  } else {
+    hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, F8>), grid, dim3(256),
+                       (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
+  }
+}
+
+void launch_mfma(const FwdArgs& a, int d, int nk_pad, bool fp8, bool last, hipStream_t s) {
+  if (last && fp8) launch_mfma_t<true, true>(a, d, nk_pad, s);
+  else if (last) launch_mfma_t<true, false>(a, d, nk_pad, s);
+  else if (fp8) launch_mfma_t<false, true>(a, d, nk_pad, s);
+  else launch_mfma_t<false, false>(a, d, nk_pad, s);
+}
+
+// The l = 1 (EOS) kernel for a call's shape.
+void launch_eos(const FwdArgs& a, int d, int kg, bool fp8, hipStream_t s) {
+  const dim3 grid((unsigned)(((int64_t)a.P * a.H + 3) / 4));
+  // Q staging units per lane: G heads x d/16 chunk pairs over 64 lanes
+  const bool qu2 = a.G * (d / 16) > 64;
+  auto go = [&](auto d_c, auto ngt_c) {
+    constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
+    if (fp8 && qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
+    else if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
+    else if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (d == 64) {
+    if (kg <= 16) go(I64{}, I1{});
+    else go(I64{}, I2{});
+  } else {
+    if (kg <= 16) go(I128{}, I1{});
+    else go(I128{}, I2{});
+  }
+}
+
 // gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
 // last token of each pair)
 gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_ids, int P, int ell,
@@ -1484,103 +1583,11 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
   const int kg = a.k + a.kq;
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
   if ((pool->dtype == GIST_BF16 || fp8) && ell >= 2 && ell <= 64 && nk_pad <= 128) {  // LDS <= 116 KiB per workgroup
-    const dim3 grid((unsigned)((int64_t)P * H));
-    auto go = [&](auto last_c) {
-    constexpr bool L = decltype(last_c)::value;
-    const int nkt = nk_pad / 16;
-    const int G = a.G;
-    // the whole grid resident at once (see the Q prefetch depth below)
-    const bool one_gen = (int64_t)P * H <= 4 * (int64_t)device_cu_count();
-    if (fp8) {
-      // fp8 pools: the common group sizes at compile time (no Q row past the
-      // group is loaded), the rest with the group size from the arguments
-      const size_t lds5 = MfmaLds<64, 5>::bytes(nk_pad);
-      if (d == 64 && nkt <= 5 && G == 7 && one_gen)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
-      else if (d == 64 && nkt <= 5 && G == 7)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
-      else if (d == 64 && nkt <= 5 && G == 8 && one_gen)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
-      else if (d == 64 && nkt <= 5 && G == 8)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
-      else if (d == 64 && nkt <= 5)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, true>), grid, dim3(256), lds5, s, a, nk_pad);
-      else if (d == 64)
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
-      else if (nkt <= 5 && G == 8)
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 5>::bytes(nk_pad)), s, a, nk_pad);
-      else if (nkt <= 5)
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 5>::bytes(nk_pad)), s, a, nk_pad);
-      else
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, true>), grid, dim3(256),
-                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
-      return;
-    }
-    if (d == 64) {
-      if (nkt <= 5) {
-        const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
-        // When the whole grid is resident at once (four workgroups per CU),
-        // every workgroup issues its staging loads at the same moment and a
-        // deeper Q prefetch only delays them: prefetch one head ahead.  With
-        // several generations of workgroups, two heads ahead.
-        if (G == 7 && one_gen)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else if (G == 7)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else if (G == 8 && one_gen)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else
-          hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-      } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, false>), grid, dim3(256),
-                           (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
-      }
-    } else {
-      if (nkt <= 5) {
-        const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
-        // a compile-time group size loads no Q row past the group (the
-        // generic instance's clamped ring refills re-read the last head)
-        if (G == 8)
-          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-        else
-          hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, false>), grid, dim3(256), lds, s, a, nk_pad);
-      } else {
-        hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, false>), grid, dim3(256),
-                           (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
-      }
-    }
-    };
-    if (last) go(std::true_type{});
-    else go(std::false_type{});
+    launch_mfma(a, d, nk_pad, fp8, last, s);
     return check_launch("gist_attn_forward(mfma)");
   }
   if ((pool->dtype == GIST_BF16 || fp8) && ell == 1 && a.G <= 16 && kg <= 32) {
-    const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
-    // Q staging units per lane: G heads x d/16 chunk pairs over 64 lanes
-    const bool qu2 = a.G * (d / 16) > 64;
-    auto go = [&](auto d_c, auto ngt_c) {
-      constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
-      if (fp8 && qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
-      else if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
-      else if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
-    };
-    using I64 = std::integral_constant<int, 64>;
-    using I128 = std::integral_constant<int, 128>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    if (d == 64) {
-      if (kg <= 16) go(I64{}, I1{});
-      else go(I64{}, I2{});
-    } else {
-      if (kg <= 16) go(I128{}, I1{});
-      else go(I128{}, I2{});
-    }
+    launch_eos(a, d, kg, fp8, s);
     return check_launch("gist_attn_forward(eos)");
   }
   if (pool->dtype == GIST_BF16) {
@@ -1606,43 +1613,49 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
 
 namespace {
 // gist_attn_forward_paged (k_scale == v_scale == NULL: bf16 cache) and
-// gist_attn_forward_paged_fp8
+// gist_attn_forward_paged_fp8: ell = 1 runs the EOS kernel, 2 <= ell <= 64
+// the l >= 2 kernel, both reading the gists through block indices
 gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const float* k_scale,
                                const float* v_scale, bool fp8, int64_t n_blocks, int block_size,
                                const int32_t* item_blocks, int k, const int32_t* query_blocks,
-                               int kq, int q_row0, int P, int Hq, int H, int d, const void* q,
-                               const void* k_new, const void* v_new, int pos0, float rope_base,
-                               float scale, void* out, void* stream) {
+                               int kq, int q_row0, int P, int ell, int Hq, int H, int d,
+                               const void* q, const void* k_new, const void* v_new, int pos0,
+                               float rope_base, float scale, void* out, void* stream) {
   clear_error();
-  if (P < 0) return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: P < 0");
+  const char* fn = fp8 ? "gist_attn_forward_paged_fp8" : "gist_attn_forward_paged";
+  auto err = [&](gist_status c, const char* m) { return fail(c, std::string(fn) + ": " + m); };
+  if (P < 0) return err(GIST_ERR_INVALID_ARG, "P < 0");
   if (n_blocks < 1 || n_blocks > INT32_MAX || block_size < 1)
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: bad n_blocks or block_size");
-  if (d != 64 && d != 128)
-    return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: d must be 64 or 128");
+    return err(GIST_ERR_INVALID_ARG, "bad n_blocks or block_size");
+  if (d != 64 && d != 128) return err(GIST_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (H < 1 || Hq < H || Hq % H != 0)
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: Hq must be a positive multiple of H");
-  if (Hq / H > 16) return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: Hq/H must be <= 16");
+    return err(GIST_ERR_INVALID_ARG, "Hq must be a positive multiple of H");
   if (k < 1 || kq < 0 || q_row0 < 0 || k > block_size || q_row0 + kq > block_size)
-    return fail(GIST_ERR_INVALID_ARG,
-                "gist_attn_forward_paged: gist rows must lie within one block (k >= 1)");
-  if (k + kq > 32) return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: k + k' must be <= 32");
+    return err(GIST_ERR_INVALID_ARG, "gist rows must lie within one block (k >= 1)");
+  if (ell < 1 || ell > 64) return err(GIST_ERR_UNSUPPORTED, "ell must be in [1, 64]");
+  if (ell == 1) {
+    if (Hq / H > 16) return err(GIST_ERR_UNSUPPORTED, "Hq/H must be <= 16 for ell = 1");
+    if (k + kq > 32) return err(GIST_ERR_UNSUPPORTED, "k + k' must be <= 32 for ell = 1");
+  } else {
+    if (Hq / H > 32) return err(GIST_ERR_UNSUPPORTED, "Hq/H must be <= 32");
+    if ((k + kq + ell + 15) / 16 * 16 > 128)
+      return err(GIST_ERR_UNSUPPORTED, "k + k' + ell must fit 128 keys (16-key tiles)");
+  }
   if (!(scale > 0.f) || !std::isfinite(scale))
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: scale must be positive and finite");
+    return err(GIST_ERR_INVALID_ARG, "scale must be positive and finite");
   if (!(rope_base > 0.f) || !std::isfinite(rope_base))
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: rope_base must be positive");
-  if (kq > 0 && !query_blocks)
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: query_blocks is NULL");
+    return err(GIST_ERR_INVALID_ARG, "rope_base must be positive");
+  if (kq > 0 && !query_blocks) return err(GIST_ERR_INVALID_ARG, "query_blocks is NULL");
   if (P == 0) return GIST_OK;
   if (!k_cache || !v_cache || !item_blocks || !q || !k_new || !v_new || !out ||
       (fp8 && (!k_scale || !v_scale)))
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: NULL tensor argument");
+    return err(GIST_ERR_INVALID_ARG, "NULL tensor argument");
   if (fp8 && ((((uintptr_t)k_scale) | ((uintptr_t)v_scale)) & 3) != 0)
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: scales must be 4-byte aligned");
+    return err(GIST_ERR_INVALID_ARG, "scales must be 4-byte aligned");
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_new) ||
       !aligned16(v_new) || !aligned16(out))
-    return fail(GIST_ERR_INVALID_ARG, "gist_attn_forward_paged: tensors must be 16-byte aligned");
-  if ((int64_t)P * H > INT32_MAX)
-    return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward_paged: P*H too large for one launch");
+    return err(GIST_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if ((int64_t)P * H * ell > INT32_MAX) return err(GIST_ERR_UNSUPPORTED, "P*H*ell too large for one launch");
 
   FwdArgs a = {};
   a.N = n_blocks;
@@ -1656,7 +1669,7 @@ gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const f
   a.v_new = v_new;
   a.out = out;
   a.P = P;
-  a.ell = 1;
+  a.ell = ell;
   a.Hq = Hq;
   a.H = H;
   a.G = Hq / H;
@@ -1675,31 +1688,9 @@ gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const f
   a.paged_kscales = fp8 ? k_scale : nullptr;
   a.paged_vscales = fp8 ? v_scale : nullptr;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)(((int64_t)P * H + 3) / 4));
-  const int kg = k + kq;
-  const bool qu2 = a.G * (d / 16) > 64;
-  auto go = [&](auto d_c, auto ngt_c) {
-    constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
-    if (fp8) {
-      if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
-    } else {
-      if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
-    }
-  };
-  using I64 = std::integral_constant<int, 64>;
-  using I128 = std::integral_constant<int, 128>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  if (d == 64) {
-    if (kg <= 16) go(I64{}, I1{});
-    else go(I64{}, I2{});
-  } else {
-    if (kg <= 16) go(I128{}, I1{});
-    else go(I128{}, I2{});
-  }
-  return check_launch(fp8 ? "gist_attn_forward_paged_fp8" : "gist_attn_forward_paged");
+  if (ell == 1) launch_eos(a, d, k + kq, fp8, s);
+  else launch_mfma(a, d, (k + kq + ell + 15) / 16 * 16, fp8, false, s);
+  return check_launch(fn);
 }
 }  // namespace
 
@@ -1707,12 +1698,12 @@ extern "C" gist_status gist_attn_forward_paged(const void* k_cache, const void* 
                                                int64_t n_blocks, int block_size,
                                                const int32_t* item_blocks, int k,
                                                const int32_t* query_blocks, int kq, int q_row0,
-                                               int P, int Hq, int H, int d, const void* q,
-                                               const void* k_new, const void* v_new, int pos0,
-                                               float rope_base, float scale, void* out,
-                                               void* stream) {
+                                               int P, int ell, int Hq, int H, int d,
+                                               const void* q, const void* k_new,
+                                               const void* v_new, int pos0, float rope_base,
+                                               float scale, void* out, void* stream) {
   return attn_forward_paged(k_cache, v_cache, nullptr, nullptr, false, n_blocks, block_size,
-                            item_blocks, k, query_blocks, kq, q_row0, P, Hq, H, d, q, k_new,
+                            item_blocks, k, query_blocks, kq, q_row0, P, ell, Hq, H, d, q, k_new,
                             v_new, pos0, rope_base, scale, out, stream);
 }
 
@@ -1721,12 +1712,12 @@ extern "C" gist_status gist_attn_forward_paged_fp8(const void* k_cache, const vo
                                                    int64_t n_blocks, int block_size,
                                                    const int32_t* item_blocks, int k,
                                                    const int32_t* query_blocks, int kq, int q_row0,
-                                                   int P, int Hq, int H, int d, const void* q,
-                                                   const void* k_new, const void* v_new, int pos0,
-                                                   float rope_base, float scale, void* out,
-                                                   void* stream) {
+                                                   int P, int ell, int Hq, int H, int d,
+                                                   const void* q, const void* k_new,
+                                                   const void* v_new, int pos0, float rope_base,
+                                                   float scale, void* out, void* stream) {
   return attn_forward_paged(k_cache, v_cache, k_scale, v_scale, true, n_blocks, block_size,
-                            item_blocks, k, query_blocks, kq, q_row0, P, Hq, H, d, q, k_new,
+                            item_blocks, k, query_blocks, kq, q_row0, P, ell, Hq, H, d, q, k_new,
                             v_new, pos0, rope_base, scale, out, stream);
 }
 

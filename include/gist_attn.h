@@ -167,12 +167,15 @@ gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* i
                               void* stream);
 
 /*
- * gist_attn_forward_paged — the query-gist EOS step (ell = 1, [GIST]
- * 能不能再进一步: one token over the item gist, the query gist and itself)
- * with both gists read from a paged KV cache in the layout paged decode uses,
- * so gist rows and decode sequences can live in one block pool.  With
- * 16-token blocks, k + k' = 8 + 8 fills one block exactly (the alignment the
- * same section recommends): pass query_blocks = item_blocks and q_row0 = k.
+ * gist_attn_forward_paged — gist attention with the gists read from a paged
+ * KV cache in the layout paged decode uses, so gist rows and decode sequences
+ * can live in one block pool ([GIST] 能不能再进一步: align the gist rows to the
+ * serving engine's block size).  With 16-token blocks, k + k' = 8 + 8 fills
+ * one block exactly (the alignment the same section recommends): pass
+ * query_blocks = item_blocks and q_row0 = k.  ell = 1 is the query-gist EOS
+ * step (one token over the item gist, the query gist and itself); 2 <= ell
+ * <= 64 is the item-only or query-gist online pass of gist_attn_forward with
+ * the gist rows taken from blocks instead of pool records.
  *   k_cache, v_cache  device bf16 [n_blocks][H][block_size][d]; gist K rows
  *                     already rotated at their canonical positions (item
  *                     gist 1..k, query gist k+1..k+k')
@@ -180,19 +183,22 @@ gist_status gist_attn_forward(const gist_pool* pool, int layer, const int32_t* i
  *                     0..k-1 of block item_blocks[p]
  *   query_blocks      device int32 [P] (NULL when k' = 0): the query gist is
  *                     rows q_row0 .. q_row0+k'-1 of block query_blocks[p]
- *   q, k_new, v_new, out  as gist_attn_forward with ell = 1: q, out
- *                     [P][Hq][d]; k_new, v_new [P][H][d]
- *   pos0              position of the token: k + k' + 1
- * Limits: d in {64, 128}; Hq % H == 0, Hq/H <= 16; 1 <= k; k + k' <= 32;
- * both gists within a block.  Block indices are bounds-checked on the
- * device (out-of-range: the pair's rows are NaN).  P == 0 is a no-op.
+ *   q, k_new, v_new, out  as gist_attn_forward: q, out [P][ell][Hq][d];
+ *                     k_new, v_new [P][ell][H][d]
+ *   pos0              position of the first new token: k + k' + 1
+ * Limits: d in {64, 128}; Hq % H == 0; 1 <= k; both gists within a block;
+ * ell = 1: Hq/H <= 16 and k + k' <= 32; 2 <= ell <= 64: Hq/H <= 32 and
+ * k + k' + ell <= 128 rounded up to 16 (else GIST_ERR_UNSUPPORTED).  Block
+ * indices are bounds-checked on the device (out-of-range: the pair's rows are
+ * NaN).  The results equal gist_attn_forward's over pools holding the same
+ * rows, bit for bit.  P == 0 is a no-op.
  */
 gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache, int64_t n_blocks,
                                     int block_size, const int32_t* item_blocks, int k,
-                                    const int32_t* query_blocks, int kq, int q_row0, int P, int Hq,
-                                    int H, int d, const void* q, const void* k_new,
-                                    const void* v_new, int pos0, float rope_base, float scale,
-                                    void* out, void* stream);
+                                    const int32_t* query_blocks, int kq, int q_row0, int P,
+                                    int ell, int Hq, int H, int d, const void* q,
+                                    const void* k_new, const void* v_new, int pos0,
+                                    float rope_base, float scale, void* out, void* stream);
 
 /*
  * gist_attn_forward_paged_fp8 — gist_attn_forward_paged over a paged cache of
@@ -205,17 +211,19 @@ gist_status gist_attn_forward_paged(const void* k_cache, const void* v_cache, in
  *                     (resp. v_scale)
  *   k_scale, v_scale  device fp32 [n_blocks][H], 4-byte aligned
  * q, k_new, v_new and out are bf16; every other argument, limit and error
- * behaviour is that of gist_attn_forward_paged.  A key's K scale multiplies
- * its fp32 logit and its V scale its softmax weight.
+ * behaviour is that of gist_attn_forward_paged.  With ell = 1 a key's K
+ * scale multiplies its fp32 logit and its V scale its softmax weight; with
+ * ell >= 2 each gist element, decode(code) * scale, is staged as for an fp8
+ * pool (see gist_attn_forward).
  */
 gist_status gist_attn_forward_paged_fp8(const void* k_cache, const void* v_cache,
                                         const float* k_scale, const float* v_scale,
                                         int64_t n_blocks, int block_size,
                                         const int32_t* item_blocks, int k,
                                         const int32_t* query_blocks, int kq, int q_row0, int P,
-                                        int Hq, int H, int d, const void* q, const void* k_new,
-                                        const void* v_new, int pos0, float rope_base, float scale,
-                                        void* out, void* stream);
+                                        int ell, int Hq, int H, int d, const void* q,
+                                        const void* k_new, const void* v_new, int pos0,
+                                        float rope_base, float scale, void* out, void* stream);
 
 /*
  * gist_attn_forward_last — gist_attn_forward for the last query token of

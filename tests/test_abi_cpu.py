@@ -290,9 +290,10 @@ def test_prefill_validation(L):
             L.gist_pool_destroy(hd)
 
 
-def _pg(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE, scale=0.125):
-    return L.gist_attn_forward_paged(ptr, ptr, nblk, bs, ptr, k, qb, kq, q_row0, P, Hq, H, d, ptr,
-                                     ptr, ptr, k + kq + 1, 1e4, scale, ptr, None)
+def _pg(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, ell=1, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE,
+        scale=0.125):
+    return L.gist_attn_forward_paged(ptr, ptr, nblk, bs, ptr, k, qb, kq, q_row0, P, ell, Hq, H, d,
+                                     ptr, ptr, ptr, k + kq + 1, 1e4, scale, ptr, None)
 
 
 def test_paged_gist_validation(L):
@@ -311,12 +312,20 @@ def test_paged_gist_validation(L):
     assert _pg(L, ptr=ctypes.c_void_p((1 << 20) + 4)) == _lib.GIST_ERR_INVALID_ARG
     assert _pg(L, P=0, ptr=None) == _lib.GIST_OK
     assert _pg(L, kq=0, qb=None, P=0, ptr=None) == _lib.GIST_OK
+    # ell >= 2 (the l >= 2 kernel over paged gists)
+    assert _pg(L, ell=0) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg(L, ell=65) == _lib.GIST_ERR_UNSUPPORTED
+    assert _pg(L, ell=2, Hq=66, H=2) == _lib.GIST_ERR_UNSUPPORTED           # Hq/H > 32
+    assert _pg(L, ell=64, bs=64, k=64, kq=1, q_row0=63) == _lib.GIST_ERR_UNSUPPORTED  # 129 keys
+    assert _pg(L, ell=64, bs=64, k=20, kq=20, q_row0=20, ptr=None) == _lib.GIST_ERR_INVALID_ARG
+    assert "keys" not in L.gist_last_error().decode()  # k + k' > 32 is fine for ell >= 2
+    assert _pg(L, ell=16, Hq=34, H=2, P=0, ptr=None) == _lib.GIST_OK         # Hq/H = 17
 
 
-def _pg8(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE,
+def _pg8(L, nblk=8, bs=16, k=8, kq=8, q_row0=8, P=4, ell=1, Hq=16, H=2, d=64, ptr=FAKE, qb=FAKE,
          ks=FAKE, vs=FAKE):
-    return L.gist_attn_forward_paged_fp8(ptr, ptr, ks, vs, nblk, bs, ptr, k, qb, kq, q_row0, P, Hq,
-                                         H, d, ptr, ptr, ptr, k + kq + 1, 1e4, 0.125, ptr, None)
+    return L.gist_attn_forward_paged_fp8(ptr, ptr, ks, vs, nblk, bs, ptr, k, qb, kq, q_row0, P, ell,
+                                         Hq, H, d, ptr, ptr, ptr, k + kq + 1, 1e4, 0.125, ptr, None)
 
 
 def test_paged_gist_fp8_validation(L):

@@ -952,3 +952,90 @@ def test_paged_gist_bad_block_gives_nan_rows():
                                       case.vn[0][:, 0], query_blocks=qb, kq=8, q_row0=8))
     torch.cuda.synchronize()
     assert np.isnan(o[[1, 2]]).all() and np.isfinite(o[[0, 3]]).all()
+
+
+# ell >= 2: the ell-token kernel reading its gists from the paged cache
+PAGED_GIST_ELL_SHAPES = [
+    # k, kq, ell, hq, h, d, pairs, block size, same block
+    (8, 0, 64, 14, 2, 64, 40, 16, False),    # the 500-pair workload's shape
+    (8, 8, 64, 14, 2, 64, 24, 16, True),
+    (8, 8, 64, 64, 8, 128, 6, 16, False),    # the wide workload's shape
+    (8, 0, 64, 64, 8, 128, 6, 16, True),
+    (12, 12, 16, 16, 2, 128, 9, 32, True),
+    (20, 12, 37, 8, 1, 64, 5, 32, False),    # ragged key and query tiles
+]
+
+
+def _ell_ids(s):
+    return "k%d_kq%d_l%d_hq%d_h%d_d%d_p%d_bs%d_%s" % (*s[:8], "one" if s[8] else "two")
+
+
+@pytest.mark.parametrize("shape", PAGED_GIST_ELL_SHAPES, ids=_ell_ids)
+def test_paged_gist_ell_equals_pooled(shape):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    k, kq, ell, hq, h, d, P, bs, same = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 11, k, ell, hq, h, d, P, torch.bfloat16, 1000 + k + kq + ell + hq, kq=kq,
+                    n_qrows=3, q_ids=qids)
+    pooled = case.run(0)
+    kc, vc, ib, qb, q_row0 = _paged_from_case(case, bs, same)
+    paged = G.gist_attn_forward_paged(kc, vc, ib, k, case.q[0], case.kn[0], case.vn[0],
+                                      query_blocks=qb if kq else None, kq=kq, q_row0=q_row0,
+                                      pos0=case.pos0, scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(paged, pooled)
+    pool, qpool = O.paged_gist_pools(f64(kc), f64(vc), ib.cpu().numpy(), k,
+                                     qb.cpu().numpy() if kq else None, kq, q_row0)
+    ref = O.gist_attn_forward(pool, 0, np.arange(P), f64(case.q[0]), f64(case.kn[0]), f64(case.vn[0]),
+                              case.pos0, ROPE_BASE, case.scale, qpool=qpool,
+                              q_ids=np.arange(P) if kq else None)
+    err = float(np.abs(f64(paged) - ref).max())
+    say(f"paged gist ell {shape}: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("shape", [s for s in PAGED_GIST_ELL_SHAPES if not s[8]], ids=_ell_ids)
+def test_paged_gist_ell_fp8_equals_pooled_fp8(shape):
+    import gist_compressed_kv_amd as G
+    from oracle import gist_oracle as O
+    k, kq, ell, hq, h, d, P, bs, _ = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 11, k, ell, hq, h, d, P, torch.bfloat16, 1040 + k + kq + ell + hq, kq=kq,
+                    n_qrows=3, q_ids=qids, fp8=True)
+    pooled = case.run(0)
+    kc, vc, ks, vs, ib, qb = _paged_fp8_from_case(case, bs)
+    paged = G.gist_attn_forward_paged_fp8(kc, vc, ks, vs, ib, k, case.q[0], case.kn[0], case.vn[0],
+                                          query_blocks=qb if kq else None, kq=kq, pos0=case.pos0,
+                                          scale=case.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(paged, pooled)
+    kf = O.dequantize_blocks(kc.cpu().numpy(), ks.cpu().numpy())
+    vf = O.dequantize_blocks(vc.cpu().numpy(), vs.cpu().numpy())
+    pool, qpool = O.paged_gist_pools(kf, vf, ib.cpu().numpy(), k, qb.cpu().numpy() if kq else None,
+                                     kq, 0)
+    ref = O.gist_attn_forward(pool, 0, np.arange(P), f64(case.q[0]), f64(case.kn[0]), f64(case.vn[0]),
+                              case.pos0, ROPE_BASE, case.scale, qpool=qpool,
+                              q_ids=np.arange(P) if kq else None)
+    err = float(np.abs(f64(paged) - ref).max())
+    say(f"paged fp8 gist ell {shape}: max-abs err {err:.3g}")
+    assert err <= 2e-2
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_paged_gist_ell_bad_block_gives_nan_rows(fp8):
+    import gist_compressed_kv_amd as G
+    case = GistCase(1, 11, 8, 64, 14, 2, 64, 4, torch.bfloat16, 1090, kq=8, n_qrows=3,
+                    q_ids=torch.tensor([0, 1, 2, 0]), fp8=fp8)
+    if fp8:
+        kc, vc, ks, vs, ib, qb = _paged_fp8_from_case(case, 16)
+    else:
+        kc, vc, ib, qb, q_row0 = _paged_from_case(case, 16, False)
+    ib[1] = 99
+    qb[2] = -1
+    args = (ib, 8, case.q[0], case.kn[0], case.vn[0])
+    o = (G.gist_attn_forward_paged_fp8(kc, vc, ks, vs, *args, query_blocks=qb, kq=8) if fp8 else
+         G.gist_attn_forward_paged(kc, vc, *args, query_blocks=qb, kq=8))
+    o = f64(o)
+    torch.cuda.synchronize()
+    assert np.isnan(o[[1, 2]]).all() and np.isfinite(o[[0, 3]]).all()
