@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b500_last", "24L_b2000", "1L_b500", "1L_b500_paged",
+                    choices=["24L_b500", "24L_b500_last", "24L_b500_grouped", "24L_b2000", "1L_b500",
+                             "1L_b500_paged",
                              "wide_ell64",
                              "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
                              "prefill", "copy"])
@@ -582,7 +583,8 @@ def run(args):
     # 24L_b500_last: the same pass with the final layer producing only the last
     # token's rows (what the score head reads)
     last_layer_eos = args.workload == "24L_b500_last"
-    wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500, "24L_b2000": synth.L24_B2000,
+    wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500,
+          "24L_b500_grouped": synth.L24_B500, "24L_b2000": synth.L24_B2000,
           "1L_b500": synth.SINGLE_LAYER, "1L_b500_paged": synth.SINGLE_LAYER,
           "wide_ell64": synth.WIDE_ELL64, "wide_ell64_fp8": synth.WIDE_ELL64_FP8,
           "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
@@ -629,6 +631,14 @@ def run(args):
         kc = torch.zeros((wl.n_items, wl.h, 16, wl.d), dtype=wl.dtype, device=dev)
         vc = torch.zeros_like(kc)
         kc[:, :, :wl.k], vc[:, :, :wl.k] = pool_t[0, :, 0], pool_t[0, :, 1]
+    # 24L_b500_grouped: the pass's 24 layer calls as one grouped launch (each
+    # layer a group with its own activation set)
+    grouped = None
+    if args.workload == "24L_b500_grouped":
+        grouped = G.GroupedForward(pool, [{"layer": li, "item_ids": ids, "q": qs[li], "k_new": kns[li],
+                                           "v_new": vns[li], "out": outs[li]}
+                                          for li in range(wl.layers)], pos0=wl.pos0,
+                                   rope_base=10000.0, scale=1.0 / math.sqrt(wl.d))
     q_lasts = [q[:, -1].contiguous() for q in qs] if last_layer_eos else None
     out_last = torch.empty_like(q_lasts[0]) if last_layer_eos else None
     torch.cuda.synchronize()
@@ -638,6 +648,10 @@ def run(args):
     passes = [0]
 
     def step():
+        if grouped is not None:
+            grouped(stream)
+            passes[0] += 1
+            return
         base = passes[0] * wl.layers
         for li in range(wl.layers):
             si = (base + li) % n_sets
@@ -681,12 +695,14 @@ def run(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    avg_launch_s = evs[0].elapsed_time(evs[-1]) / 1e3 / (args.steps * wl.layers)
+    # the grouped workload runs the pass as one launch of all 24 layers
+    launches = 1 if grouped is not None else wl.layers
+    avg_launch_s = evs[0].elapsed_time(evs[-1]) / 1e3 / (args.steps * launches)
     pass_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     median_pass_ms = pass_ms[len(pass_ms) // 2]
 
     bytes_unit = gist_bytes_per_pair_layer(wl)
-    bytes_launch = bytes_unit * wl.pairs
+    bytes_launch = bytes_unit * wl.pairs * (wl.layers // launches)
     if last_layer_eos:
         # the pass moves L-1 full layers and one last-token layer; price the
         # pass's bytes over the pass's launches
@@ -713,16 +729,18 @@ def run(args):
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "data": "synthetic: N(0,1) pools" + (" (E4M3 codes, scale amax/448 per block)" if wl.fp8 else "")
                 + ", Q/K/V; seeded item ids (50 distinct candidates per query)"
-                + ("; gists read from a paged cache of 16-row blocks" if paged else ""),
+                + ("; gists read from a paged cache of 16-row blocks" if paged else "")
+                + ("; the 24 layer calls of a pass as one grouped launch" if grouped is not None else ""),
         "config": {"workload": wl.name + (", gists in a paged cache" if paged else ""), "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
                    "h": wl.h, "head_dim": wl.d, "k": wl.k, "k_query_gist": wl.kq, "ell": wl.ell,
                    "pool_items": wl.n_items, "parallelism": "single GPU"},
         "tokens_per_s": pairs_per_s * wl.ell,
-        "pass_hbm_gbps_algorithmic": bytes_launch * wl.layers / (ms_per_step / 1e3) / 1e9,
+        "pass_hbm_gbps_algorithmic": bytes_launch * launches / (ms_per_step / 1e3) / 1e9,
         "roofline": {
             "bound": "hbm",
             "kernel": "gist_fwd_mfma<64> (23 full layers + 1 last-token layer; pass bytes / "
                       "launches)" if last_layer_eos else
+                      "gist_fwd_mfma_grouped<64> (24 layer groups in one launch)" if grouped is not None else
                       "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
                       (("gist_fwd_mfma<128, fp8 gist>" if wl.fp8 else "gist_fwd_mfma<128>") if wl.ell > 1 else
                        ("gist_fwd_eos<128, fp8 gist>" if wl.fp8 else "gist_fwd_eos<128>")),
@@ -732,9 +750,9 @@ def run(args):
             "frac": achieved_gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "bytes_per_unit": bytes_unit,
-            "units_per_launch": wl.pairs,
+            "units_per_launch": wl.pairs * (wl.layers // launches),
             "avg_launch_us": avg_launch_s * 1e6,
-            "median_launch_us": median_pass_ms * 1e3 / wl.layers,
+            "median_launch_us": median_pass_ms * 1e3 / launches,
         },
         "median_pass_ms": median_pass_ms,
     }

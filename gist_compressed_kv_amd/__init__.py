@@ -185,6 +185,70 @@ def gist_attn_forward(pool: GistPool, layer: int, item_ids: torch.Tensor, q: tor
     return out
 
 
+class GroupedForward:
+    """A prepared gist_attn_forward_grouped call: the group table is checked
+    and marshalled once, and each call launches it (for loops that run the
+    same groups repeatedly).  groups: a sequence of dicts with keys layer,
+    item_ids, q [P, ell, Hq, d], k_new and v_new [P, ell, H, d], optional out,
+    and q_ids when qpool is given (every group has the same ell and Hq)."""
+
+    def __init__(self, pool: GistPool, groups, pos0: int | None = None,
+                 rope_base: float = 10000.0, scale: float | None = None,
+                 qpool: GistPool | None = None):
+        groups = list(groups)
+        self.pool, self.qpool, self.outs = pool, qpool, []
+        self.ell = self.Hq = 0
+        self.table = (_lib.GistGroup * max(len(groups), 1))()
+        self.n = len(groups)
+        if not groups:
+            self.pos0, self.rope_base, self.scale = 0, rope_base, 1.0
+            return
+        q0 = groups[0]["q"]
+        if q0.dim() != 4:
+            raise ValueError("q must have shape [P, ell, Hq, d]")
+        _, self.ell, self.Hq, d = q0.shape
+        self.pos0 = pool.k + (qpool.k if qpool is not None else 0) + 1 if pos0 is None else pos0
+        self.rope_base = rope_base
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        dt = pool.act_dtype
+        for i, gr in enumerate(groups):
+            q = gr["q"]
+            if q.dim() != 4 or tuple(q.shape[1:]) != (self.ell, self.Hq, pool.d):
+                raise ValueError("every group's q must have shape [P, ell, Hq, d] with one ell and Hq")
+            P = q.shape[0]
+            out = gr.get("out")
+            if out is None:
+                out = torch.empty_like(q)
+            kv_shape = (P, self.ell, pool.H, pool.d)
+            ptrs = _ptrs((gr["item_ids"], "item_ids", torch.int32, (P,)), (q, "q", dt, q.shape),
+                         (gr["k_new"], "k_new", dt, kv_shape), (gr["v_new"], "v_new", dt, kv_shape),
+                         (out, "out", dt, q.shape))
+            qi = _dev(gr["q_ids"], "q_ids", torch.int32, (P,)) if qpool is not None else None
+            self.table[i] = _lib.GistGroup(int(gr["layer"]), P, ptrs[0], qi, ptrs[1], ptrs[2],
+                                           ptrs[3], ptrs[4])
+            self.outs.append(out)
+        # the tensors stay referenced as long as the table points at them
+        self._keep = groups
+
+    def __call__(self, stream=None) -> list:
+        _lib.check(_lib.lib().gist_attn_forward_grouped(
+            self.pool.handle, self.qpool.handle if self.qpool is not None else None, self.table,
+            self.n, self.ell, self.Hq, self.pos0, self.rope_base, self.scale, _stream_ptr(stream)),
+            "gist_attn_forward_grouped")
+        return self.outs
+
+
+def gist_attn_forward_grouped(pool: GistPool, groups, pos0: int | None = None,
+                              rope_base: float = 10000.0, scale: float | None = None,
+                              qpool: GistPool | None = None, stream=None) -> list:
+    """Several gist_attn_forward calls of one shape in one launch (groups as
+    for GroupedForward); returns the outputs in group order."""
+    groups = list(groups)
+    if not groups:
+        return []
+    return GroupedForward(pool, groups, pos0, rope_base, scale, qpool)(stream)
+
+
 def gist_attn_forward_last(pool: GistPool, layer: int, item_ids: torch.Tensor, q_last: torch.Tensor,
                            k_new: torch.Tensor, v_new: torch.Tensor, pos0: int | None = None,
                            rope_base: float = 10000.0, scale: float | None = None,

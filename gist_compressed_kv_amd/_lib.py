@@ -35,6 +35,12 @@ _i32 = ctypes.c_int
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
+class GistGroup(ctypes.Structure):
+    """struct gist_group of include/gist_attn.h."""
+    _fields_ = [("layer", _i32), ("P", _i32), ("item_ids", _vp), ("q_ids", _vp), ("q", _vp),
+                ("k_new", _vp), ("v_new", _vp), ("out", _vp)]
+
+
 SIGNATURES = {
     "gist_pool_bytes": (_sz, [_i32, _i64, _i32, _i32, _i32, _i32]),
     "gist_pool_create": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _i32, _i32, _i32, _i32, _vp, _sz]),
@@ -50,6 +56,7 @@ SIGNATURES = {
                                            _f32, _f32, _vp, _vp]),
     "gist_attn_forward_last": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32,
                                       _f32, _f32, _vp, _vp, _vp, _vp]),
+    "gist_attn_forward_grouped": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _f32, _f32, _vp]),
     "gist_prefill_workspace_bytes": (_sz, [_i64, _i32, _i32]),
     "gist_prefill_attn": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                  _f32, _vp, _vp, _sz, _vp, _i32, _vp, _vp]),

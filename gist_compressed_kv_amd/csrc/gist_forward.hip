@@ -81,6 +81,40 @@ struct FwdArgs {
   const float* paged_vscales;
 };
 
+// What one workgroup of the l >= 2 kernel reads and writes: its call's
+// activations, outputs, ids and pool layer, and its (pair, KV head)
+struct Slice {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  const int32_t* item_ids;
+  const int32_t* q_ids;
+  int64_t pool_off, qpool_off;  // first element (fp8: byte) of the layer
+  const float* pool_scales;     // fp8: the layer's scales
+  const float* qpool_scales;
+  int p, g;                     // pair within the call, KV head
+  int bid;                      // workgroup index of the launch
+};
+
+// Groups of one grouped launch (gist_attn_forward_grouped), passed by value
+constexpr int kMaxGroups = 32;
+struct GroupEntry {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* out;
+  const int32_t* item_ids;
+  const int32_t* q_ids;
+  int64_t layer;
+};
+struct GroupTable {
+  int wg_end[kMaxGroups];  // running workgroup count after group i (INT_MAX past the last)
+  GroupEntry e[kMaxGroups];
+  int64_t pool_layer_stride, qpool_layer_stride;    // elements (fp8: bytes) per layer
+  int64_t scale_layer_stride, qscale_layer_stride;  // fp8 scales per layer
+};
+
 // ---------------------------------------------------------------------------
 // Shared helpers
 // ---------------------------------------------------------------------------
@@ -240,8 +274,7 @@ __device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo
 // Waves per SIMD: four workgroups per CU fit the LDS at d = 64 with up to
 // 80 keys (so up to 128 VGPRs); otherwise two (up to 256 VGPRs).
 template <int D, int NKT, int QPF, int GT, bool LAST, bool FP8>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NKT <= 5 ? 4 : 2)))
-gist_fwd_mfma(const FwdArgs a, int nk_pad) {
+__device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int nk_pad) {
   extern __shared__ __align__(16) bf16_t smem[];
   constexpr int VS = MfmaLds<D, NKT>::VS;
   constexpr int NS = D / 32;   // 32-channel k-steps of the Q·Kᵀ product
@@ -257,14 +290,14 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   bf16_t* Vt = smem + 2 * nk_pad * D;   // [D][VS], reversed key order
   char* xbuf = (char*)smem + MfmaLds<D, NKT>::kv_bytes(nk_pad);
 
-  const int p = blockIdx.x / a.H;
-  const int g = blockIdx.x - p * a.H;
+  const int p = sl.p;
+  const int g = sl.g;
   const int tid = threadIdx.x;
   const int kg = a.k + a.kq;
   const int ell = a.ell;
   const int nk = kg + ell;
   const int Hq = a.Hq, G = GT > 0 ? GT : a.G;
-  bf16_t* out = (bf16_t*)a.out;
+  bf16_t* out = (bf16_t*)sl.out;
 
   // ---- issue the first QPF heads' Q loads of this wave first: they do not
   // depend on the item id, so HBM traffic starts while the id is in flight --
@@ -272,7 +305,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // is a scalar and the tile loops branch on SGPRs)
   // The token block of a wave rotates with the workgroup index: later blocks
   // see more keys, and the rotation spreads that extra work over the SIMDs.
-  const int wv = __builtin_amdgcn_readfirstlane(((tid >> 6) + blockIdx.x) & 3);
+  const int wv = __builtin_amdgcn_readfirstlane(((tid >> 6) + sl.bid) & 3);
   const int lane = tid & 63;
   const int n = lane & 15, q4 = lane >> 4;
   const int t0 = LAST ? 16 * ((ell - 1) >> 4) : 16 * wv;
@@ -294,7 +327,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // loads are not: they touch parts of lines that other loads then reuse)
   const int cl = lane % CPR, rl = lane / CPR;
   const int64_t pair_off = (int64_t)p * (LAST ? 1 : ell) * Hq * D;
-  const char* qpair = (const char*)((const bf16_t*)a.q + pair_off);
+  const char* qpair = (const char*)((const bf16_t*)sl.q + pair_off);
   char* opair = (char*)(out + pair_off);
   uint32_t qlane[NS], olane[NS];
   bool ovalid[NS];
@@ -329,11 +362,11 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
-  const int32_t item = a.item_ids[p];
+  const int32_t item = sl.item_ids[p];
   int32_t qid = 0;
   bool bad = item < 0 || item >= a.N;
   if (a.kq) {
-    qid = a.q_ids[p];
+    qid = sl.q_ids[p];
     bad = bad || qid < 0 || qid >= a.qN;
   }
   if (bad) {
@@ -359,11 +392,11 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       qV = (const C*)a.paged_v + qb;
     }
   } else {
-    gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
+    gK = (const C*)a.pool + sl.pool_off + (int64_t)item * 2 * a.H * a.k * D +
          (int64_t)g * a.k * D;
     gV = gK + (int64_t)a.H * a.k * D;
     if (a.kq) {
-      qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
+      qK = (const C*)a.qpool + sl.qpool_off + (int64_t)qid * 2 * a.H * a.kq * D +
            (int64_t)g * a.kq * D;
       qV = qK + (int64_t)a.H * a.kq * D;
     }
@@ -379,11 +412,11 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
         svq = a.paged_vscales[(int64_t)qid * a.H + g];
       }
     } else {
-      const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+      const float* si = sl.pool_scales + (int64_t)item * 2 * a.H;
       ski = si[g];
       svi = si[a.H + g];
       if (a.kq) {
-        const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+        const float* sq = sl.qpool_scales + (int64_t)qid * 2 * a.H;
         skq = sq[g];
         svq = sq[a.H + g];
       }
@@ -413,7 +446,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // V of key j (< nk) as eight bf16: gist rows through gist_f32 (fp8:
   // rounded to bf16 once), new rows as loaded
   auto v_load = [&](int j, int ch) -> u32x4_t {
-    const bf16_t* nrow = (const bf16_t*)a.v_new + (((int64_t)p * ell + (j < kg ? 0 : j - kg)) * a.H + g) * D;
+    const bf16_t* nrow = (const bf16_t*)sl.v_new + (((int64_t)p * ell + (j < kg ? 0 : j - kg)) * a.H + g) * D;
     if constexpr (FP8) {
       // one unconditional load per lane: its gist row or its new row
       const bool gist = j < kg;
@@ -443,7 +476,7 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
   // lane's own query token: step s holds channels 32s + 8*q4 .. +7
   u32x4_t kn[NS];
   {
-    const bf16_t* krow = (const bf16_t*)a.k_new + (((int64_t)p * ell + tkl) * a.H + g) * D + 8 * q4;
+    const bf16_t* krow = (const bf16_t*)sl.k_new + (((int64_t)p * ell + tkl) * a.H + g) * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < NS; ++s) kn[s] = *(const u32x4_t*)(krow + 32 * s);
   }
@@ -789,6 +822,58 @@ gist_fwd_mfma(const FwdArgs a, int nk_pad) {
       });
     }
   }
+}
+
+
+template <int D, int NKT, int QPF, int GT, bool LAST, bool FP8>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NKT <= 5 ? 4 : 2)))
+gist_fwd_mfma(const FwdArgs a, int nk_pad) {
+  Slice sl;
+  sl.bid = blockIdx.x;
+  sl.p = blockIdx.x / a.H;
+  sl.g = blockIdx.x - sl.p * a.H;
+  sl.q = a.q;
+  sl.k_new = a.k_new;
+  sl.v_new = a.v_new;
+  sl.out = a.out;
+  sl.item_ids = a.item_ids;
+  sl.q_ids = a.q_ids;
+  sl.pool_off = a.pool_layer_off;
+  sl.qpool_off = a.qpool_layer_off;
+  sl.pool_scales = a.pool_scales;
+  sl.qpool_scales = a.qpool_scales;
+  mfma_body<D, NKT, QPF, GT, LAST, FP8>(a, sl, nk_pad);
+}
+
+// Several independent calls of one shape (each with its own layer, pairs,
+// activations and outputs) in one launch: the workgroups of group i follow
+// those of group i - 1 in launch order, so one group's last workgroups run
+// beside the next group's first.  Each workgroup finds its group from the
+// table's running workgroup counts.
+template <int D, int NKT, int QPF, int GT, bool FP8>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && NKT <= 5 ? 4 : 2)))
+gist_fwd_mfma_grouped(const FwdArgs a, const GroupTable t, int nk_pad) {
+  const int bid = blockIdx.x;
+  int gi = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxGroups - 1; ++i) gi += bid >= t.wg_end[i] ? 1 : 0;
+  const GroupEntry& e = t.e[gi];
+  const int local = bid - (gi == 0 ? 0 : t.wg_end[gi - 1]);
+  Slice sl;
+  sl.bid = bid;
+  sl.p = local / a.H;
+  sl.g = local - sl.p * a.H;
+  sl.q = e.q;
+  sl.k_new = e.k_new;
+  sl.v_new = e.v_new;
+  sl.out = e.out;
+  sl.item_ids = e.item_ids;
+  sl.q_ids = e.q_ids;
+  sl.pool_off = (int64_t)e.layer * t.pool_layer_stride;
+  sl.qpool_off = (int64_t)e.layer * t.qpool_layer_stride;
+  sl.pool_scales = FP8 ? a.pool_scales + (int64_t)e.layer * t.scale_layer_stride : nullptr;
+  sl.qpool_scales = FP8 && a.kq ? a.qpool_scales + (int64_t)e.layer * t.qscale_layer_stride : nullptr;
+  mfma_body<D, NKT, QPF, GT, false, FP8>(a, sl, nk_pad);
 }
 
 // ---------------------------------------------------------------------------
@@ -1427,9 +1512,12 @@ int device_cu_count() {
 // The l >= 2 kernel for a call's shape: head size, key tiles, gist element
 // type, group size (compile-time instances for the common ones) and Q
 // prefetch depth.
+// The l >= 2 kernel instance for a call's shape; with a group table, the
+// grouped kernel over all of its groups (wgs workgroups)
 template <bool L, bool F8>
-void launch_mfma_t(const FwdArgs& a, int d, int nk_pad, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)a.P * a.H));
+void launch_mfma_t(const FwdArgs& a, const GroupTable* t, int64_t wgs, int d, int nk_pad,
+                   hipStream_t s) {
+  const dim3 grid((unsigned)wgs);
   const int nkt = nk_pad / 16;
   const int G = a.G;
   // When the whole grid is resident at once (four workgroups per CU), every
@@ -1438,39 +1526,49 @@ void launch_mfma_t(const FwdArgs& a, int d, int nk_pad, hipStream_t s) {
   // generations of workgroups, two heads ahead.  A compile-time group size
   // loads no Q row past the group (the generic instance's clamped ring
   // refills re-read the last head).
-  const bool one_gen = (int64_t)a.P * a.H <= 4 * (int64_t)device_cu_count();
+  const bool one_gen = wgs <= 4 * (int64_t)device_cu_count();
+  auto go = [&](auto dc, auto nc, auto qc, auto gc) {
+    constexpr int DD = decltype(dc)::value, NK = decltype(nc)::value;
+    constexpr int QP = decltype(qc)::value, GG = decltype(gc)::value;
+    const size_t lds = MfmaLds<DD, NK>::bytes(nk_pad);
+    if (t) {
+      if constexpr (!L)
+        hipLaunchKernelGGL((gist_fwd_mfma_grouped<DD, NK, QP, GG, F8>), grid, dim3(256), lds, s, a, *t,
+                           nk_pad);
+    } else {
+      hipLaunchKernelGGL((gist_fwd_mfma<DD, NK, QP, GG, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    }
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I0 = std::integral_constant<int, 0>;
+  using I5 = std::integral_constant<int, 5>;
+  using I7 = std::integral_constant<int, 7>;
+  using I8 = std::integral_constant<int, 8>;
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
   if (d == 64 && nkt <= 5) {
-    const size_t lds = MfmaLds<64, 5>::bytes(nk_pad);
-    if (G == 7 && one_gen)
-      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 7, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
-    else if (G == 7)
-      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 7, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
-    else if (G == 8 && one_gen)
-      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
-    else if (G == 8)
-      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 2, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
-    else
-      hipLaunchKernelGGL((gist_fwd_mfma<64, 5, 1, 0, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    if (G == 7 && one_gen) go(D64{}, I5{}, I1{}, I7{});
+    else if (G == 7) go(D64{}, I5{}, I2{}, I7{});
+    else if (G == 8 && one_gen) go(D64{}, I5{}, I1{}, I8{});
+    else if (G == 8) go(D64{}, I5{}, I2{}, I8{});
+    else go(D64{}, I5{}, I1{}, I0{});
   } else if (d == 64) {
-    hipLaunchKernelGGL((gist_fwd_mfma<64, 8, 1, 0, L, F8>), grid, dim3(256),
-                       (MfmaLds<64, 8>::bytes(nk_pad)), s, a, nk_pad);
+    go(D64{}, I8{}, I1{}, I0{});
   } else if (nkt <= 5) {
-    const size_t lds = MfmaLds<128, 5>::bytes(nk_pad);
-    if (G == 8)
-      hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 8, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
-    else
-      hipLaunchKernelGGL((gist_fwd_mfma<128, 5, 2, 0, L, F8>), grid, dim3(256), lds, s, a, nk_pad);
+    if (G == 8) go(D128{}, I5{}, I2{}, I8{});
+    else go(D128{}, I5{}, I2{}, I0{});
   } else {
-    hipLaunchKernelGGL((gist_fwd_mfma<128, 8, 2, 0, L, F8>), grid, dim3(256),
-                       (MfmaLds<128, 8>::bytes(nk_pad)), s, a, nk_pad);
+    go(D128{}, I8{}, I2{}, I0{});
   }
 }
 
 void launch_mfma(const FwdArgs& a, int d, int nk_pad, bool fp8, bool last, hipStream_t s) {
-  if (last && fp8) launch_mfma_t<true, true>(a, d, nk_pad, s);
-  else if (last) launch_mfma_t<true, false>(a, d, nk_pad, s);
-  else if (fp8) launch_mfma_t<false, true>(a, d, nk_pad, s);
-  else launch_mfma_t<false, false>(a, d, nk_pad, s);
+  const int64_t wgs = (int64_t)a.P * a.H;
+  if (last && fp8) launch_mfma_t<true, true>(a, nullptr, wgs, d, nk_pad, s);
+  else if (last) launch_mfma_t<true, false>(a, nullptr, wgs, d, nk_pad, s);
+  else if (fp8) launch_mfma_t<false, true>(a, nullptr, wgs, d, nk_pad, s);
+  else launch_mfma_t<false, false>(a, nullptr, wgs, d, nk_pad, s);
 }
 
 // The l = 1 (EOS) kernel for a call's shape.
@@ -1496,6 +1594,43 @@ void launch_eos(const FwdArgs& a, int d, int kg, bool fp8, hipStream_t s) {
     if (kg <= 16) go(I128{}, I1{});
     else go(I128{}, I2{});
   }
+}
+
+// The arguments shared by every workgroup of a pooled call at one layer
+// (per-call pointers, P and last_only are left for the caller to set)
+void fill_args(FwdArgs& a, const gist_pool* pool, const gist_pool* qpool, int layer, int ell,
+               int Hq, int pos0, float rope_base, float scale) {
+  const bool fp8 = pool->dtype == GIST_FP8_E4M3;
+  const int H = pool->H, d = pool->d;
+  a.pool = pool->storage;
+  a.pool_layer_off = (int64_t)layer * pool->N * record_elems(pool);
+  a.N = pool->N;
+  a.k = pool->k;
+  a.qpool = qpool ? qpool->storage : nullptr;
+  a.qpool_layer_off = qpool ? (int64_t)layer * qpool->N * record_elems(qpool) : 0;
+  a.qN = qpool ? qpool->N : 0;
+  a.kq = qpool ? qpool->k : 0;
+  a.pool_scales = fp8 ? fp8_layer_scales(pool, layer) : nullptr;
+  a.qpool_scales = fp8 && qpool ? fp8_layer_scales(qpool, layer) : nullptr;
+  a.item_ids = a.q_ids = nullptr;
+  a.q = a.k_new = a.v_new = nullptr;
+  a.out = nullptr;
+  a.P = 0;
+  a.ell = ell;
+  a.Hq = Hq;
+  a.H = H;
+  a.G = Hq / H;
+  a.pos0 = pos0;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.last_only = 0;
+  a.paged = 0;
+  a.paged_k = a.paged_v = nullptr;
+  a.block_size = 0;
+  a.q_row0 = 0;
+  a.paged_kscales = a.paged_vscales = nullptr;
+  make_rope_freqs(a.freqs, d, rope_base);
+  double q = std::pow((double)rope_base, -2.0 / (double)d);
+  for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
 }
 
 // gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
@@ -1545,16 +1680,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     return fail(GIST_ERR_UNSUPPORTED, "gist_attn_forward: P*H*ell too large for one launch");
 
   FwdArgs a;
-  a.pool = pool->storage;
-  a.pool_layer_off = (int64_t)layer * pool->N * record_elems(pool);
-  a.N = pool->N;
-  a.k = pool->k;
-  a.qpool = qpool ? qpool->storage : nullptr;
-  a.qpool_layer_off = qpool ? (int64_t)layer * qpool->N * record_elems(qpool) : 0;
-  a.qN = qpool ? qpool->N : 0;
-  a.kq = qpool ? qpool->k : 0;
-  a.pool_scales = fp8 ? fp8_layer_scales(pool, layer) : nullptr;
-  a.qpool_scales = fp8 && qpool ? fp8_layer_scales(qpool, layer) : nullptr;
+  fill_args(a, pool, qpool, layer, ell, Hq, pos0, rope_base, scale);
   a.item_ids = item_ids;
   a.q_ids = qpool ? q_ids : nullptr;
   a.q = q;
@@ -1562,22 +1688,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
   a.v_new = v_new;
   a.out = out;
   a.P = P;
-  a.ell = ell;
-  a.Hq = Hq;
-  a.H = H;
-  a.G = Hq / H;
-  a.pos0 = pos0;
-  a.scale_log2 = scale * 1.4426950408889634f;
   a.last_only = last ? 1 : 0;
-  a.paged = 0;
-  a.paged_k = a.paged_v = nullptr;
-  a.block_size = 0;
-  a.q_row0 = 0;
-  make_rope_freqs(a.freqs, d, rope_base);
-  {
-    double q = std::pow((double)rope_base, -2.0 / (double)d);
-    for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
-  }
   hipStream_t s = (hipStream_t)stream;
 
   const int kg = a.k + a.kq;
@@ -1609,6 +1720,76 @@ extern "C" gist_status gist_attn_forward(const gist_pool* pool, int layer, const
                                          void* stream) {
   return attn_forward(pool, layer, item_ids, P, ell, Hq, q, k_new, v_new, pos0, rope_base, scale,
                       qpool, q_ids, out, stream, false);
+}
+
+extern "C" gist_status gist_attn_forward_grouped(const gist_pool* pool, const gist_pool* qpool,
+                                                 const gist_group* groups, int n_groups, int ell,
+                                                 int Hq, int pos0, float rope_base, float scale,
+                                                 void* stream) {
+  clear_error();
+  const char* fn = "gist_attn_forward_grouped";
+  auto err = [&](gist_status c, const char* m) { return fail(c, std::string(fn) + ": " + m); };
+  if (!pool) return err(GIST_ERR_INVALID_ARG, "pool is NULL");
+  if (n_groups < 0) return err(GIST_ERR_INVALID_ARG, "n_groups < 0");
+  if (n_groups > kMaxGroups) return err(GIST_ERR_UNSUPPORTED, "n_groups must be <= 32");
+  if (n_groups > 0 && !groups) return err(GIST_ERR_INVALID_ARG, "groups is NULL");
+  const int H = pool->H, d = pool->d;
+  if (Hq < H || Hq % H != 0) return err(GIST_ERR_INVALID_ARG, "Hq must be a positive multiple of H");
+  if (Hq / H > 32) return err(GIST_ERR_UNSUPPORTED, "Hq/H must be <= 32");
+  if (!(scale > 0.f) || !std::isfinite(scale))
+    return err(GIST_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (!(rope_base > 0.f) || !std::isfinite(rope_base))
+    return err(GIST_ERR_INVALID_ARG, "rope_base must be positive");
+  if (qpool && (qpool->H != H || qpool->d != d || qpool->dtype != pool->dtype || qpool->L != pool->L))
+    return err(GIST_ERR_INVALID_ARG, "qpool must match pool in L, H, d and dtype");
+  const int kg = pool->k + (qpool ? qpool->k : 0);
+  const int nk_pad = ((kg + ell + 15) / 16) * 16;
+  if (pool->dtype == GIST_F32 || ell < 2 || ell > 64 || nk_pad > 128)
+    return err(GIST_ERR_UNSUPPORTED,
+               "groups run the l >= 2 kernel: bf16 or fp8 pools, 2 <= ell <= 64, "
+               "k + k' + ell <= 128");
+  GroupTable t;
+  int m = 0;
+  int64_t wgs = 0;
+  for (int i = 0; i < n_groups; ++i) {
+    const gist_group& gr = groups[i];
+    if (gr.layer < 0 || gr.layer >= pool->L) return err(GIST_ERR_OUT_OF_RANGE, "layer out of range");
+    if (gr.P < 0) return err(GIST_ERR_INVALID_ARG, "P < 0");
+    if (gr.P == 0) continue;
+    if (!gr.item_ids || !gr.q || !gr.k_new || !gr.v_new || !gr.out || (qpool && !gr.q_ids))
+      return err(GIST_ERR_INVALID_ARG, "NULL tensor argument");
+    if (!aligned16(gr.q) || !aligned16(gr.k_new) || !aligned16(gr.v_new) || !aligned16(gr.out))
+      return err(GIST_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+    if ((int64_t)gr.P * H * ell > INT32_MAX) return err(GIST_ERR_UNSUPPORTED, "P*H*ell too large");
+    wgs += (int64_t)gr.P * H;
+    if (wgs > INT32_MAX) return err(GIST_ERR_UNSUPPORTED, "too many workgroups for one launch");
+    GroupEntry& e = t.e[m];
+    e.q = gr.q;
+    e.k_new = gr.k_new;
+    e.v_new = gr.v_new;
+    e.out = gr.out;
+    e.item_ids = gr.item_ids;
+    e.q_ids = qpool ? gr.q_ids : nullptr;
+    e.layer = gr.layer;
+    t.wg_end[m] = (int)wgs;
+    ++m;
+  }
+  if (m == 0) return GIST_OK;
+  for (int i = m; i < kMaxGroups; ++i) {
+    t.wg_end[i] = INT32_MAX;
+    t.e[i] = t.e[m - 1];
+  }
+  const bool fp8 = pool->dtype == GIST_FP8_E4M3;
+  FwdArgs a;
+  fill_args(a, pool, qpool, 0, ell, Hq, pos0, rope_base, scale);
+  t.pool_layer_stride = pool->N * record_elems(pool);
+  t.qpool_layer_stride = qpool ? qpool->N * record_elems(qpool) : 0;
+  t.scale_layer_stride = fp8 ? pool->N * 2 * H : 0;
+  t.qscale_layer_stride = fp8 && qpool ? qpool->N * 2 * H : 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (fp8) launch_mfma_t<false, true>(a, &t, wgs, d, nk_pad, s);
+  else launch_mfma_t<false, false>(a, &t, wgs, d, nk_pad, s);
+  return check_launch(fn);
 }
 
 namespace {

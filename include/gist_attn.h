@@ -245,6 +245,43 @@ gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32
                                    void* stream);
 
 /*
+ * gist_attn_forward_grouped — several independent gist_attn_forward calls of
+ * one shape in one launch.  Each group is one call of the online pass of
+ * [GIST] 在线的一次 attention (its own layer, pairs, ids, activations and
+ * outputs); groups share the pools, ell, Hq, pos0, rope_base and scale.  A
+ * caller that holds several such calls at once (micro-batches at different
+ * layers of a pipelined schedule, or several query batches at one layer)
+ * pays one launch instead of one per call, and the last workgroups of one
+ * group run beside the first of the next instead of idling the GPU.
+ *   groups    host array of n_groups descriptors, read during the call only
+ *             (its device pointers are as in gist_attn_forward: q, out
+ *             [P][ell][Hq][d]; k_new, v_new [P][ell][H][d]; item_ids [P];
+ *             q_ids [P] when qpool != NULL)
+ *   n_groups  0 .. 32 (more: GIST_ERR_UNSUPPORTED); groups with P == 0 are
+ *             skipped, and a call with no pairs is a no-op
+ * Limits: the l >= 2 kernel's (bf16 or fp8 pools, 2 <= ell <= 64, k + k' +
+ * ell <= 128 rounded up to 16, Hq/H <= 32), else GIST_ERR_UNSUPPORTED; a
+ * layer out of range is GIST_ERR_OUT_OF_RANGE.  Validation of every group
+ * precedes the launch.  Each group's output equals gist_attn_forward's for
+ * that group bit for bit (the same kernel code computes every row).  Groups
+ * whose outputs overlap each other or any group's inputs race.
+ */
+typedef struct gist_group {
+  int layer;                /* pool layer of this group's pass */
+  int P;                    /* pairs */
+  const int32_t* item_ids;  /* device [P] */
+  const int32_t* q_ids;     /* device [P], or NULL without a query-gist pool */
+  const void* q;            /* device bf16 [P][ell][Hq][d] */
+  const void* k_new;        /* device bf16 [P][ell][H][d] */
+  const void* v_new;        /* device bf16 [P][ell][H][d] */
+  void* out;                /* device bf16 [P][ell][Hq][d] */
+} gist_group;
+
+gist_status gist_attn_forward_grouped(const gist_pool* pool, const gist_pool* qpool,
+                                      const gist_group* groups, int n_groups, int ell, int Hq,
+                                      int pos0, float rope_base, float scale, void* stream);
+
+/*
  * gist_prefill_workspace_bytes — bytes of the workspace gist_prefill_attn
  * needs for n_tokens packed tokens, H KV heads and head size d: every K row
  * rotated, as a pair of bf16 arrays (the nearest bf16 values and the bf16

@@ -128,6 +128,57 @@ def test_forward_validation(L):
         L.gist_pool_destroy(pool)
 
 
+def _grp(L, pool, groups, ell=16, Hq=14, qpool=None, base=1e4, scale=0.125, n=None):
+    arr = (_lib.GistGroup * max(len(groups), 1))(*[_lib.GistGroup(*g) for g in groups])
+    return L.gist_attn_forward_grouped(pool, qpool, arr if groups or n else None,
+                                       len(groups) if n is None else n, ell, Hq, 9, base, scale,
+                                       None)
+
+
+def _g(layer=0, P=4, ptr=FAKE, ids=FAKE, qids=None):
+    return (layer, P, ids, qids, ptr, ptr, ptr, ptr)
+
+
+def test_grouped_validation(L):
+    pool = _pool(L)
+    f32 = _pool(L, dt=F32)
+    try:
+        assert _grp(L, None, [_g()]) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [], n=-1) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g()] * 33) == _lib.GIST_ERR_UNSUPPORTED
+        assert "32" in L.gist_last_error().decode()
+        assert L.gist_attn_forward_grouped(pool, None, None, 2, 16, 14, 9, 1e4, 0.125,
+                                           None) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g(), _g(layer=2)]) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert _grp(L, pool, [_g(layer=-1)]) == _lib.GIST_ERR_OUT_OF_RANGE
+        assert _grp(L, pool, [_g(P=-1)]) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g(), _g(ptr=None)]) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g(ids=None)]) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g(ptr=ctypes.c_void_p((1 << 20) + 4))]) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g()], Hq=13) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g()], Hq=66) == _lib.GIST_ERR_UNSUPPORTED
+        assert _grp(L, pool, [_g()], scale=0.0) == _lib.GIST_ERR_INVALID_ARG
+        assert _grp(L, pool, [_g()], base=float("inf")) == _lib.GIST_ERR_INVALID_ARG
+        # only the l >= 2 kernel runs grouped
+        assert _grp(L, pool, [_g()], ell=1) == _lib.GIST_ERR_UNSUPPORTED
+        assert _grp(L, pool, [_g()], ell=65) == _lib.GIST_ERR_UNSUPPORTED
+        assert _grp(L, pool, [_g()], ell=121) == _lib.GIST_ERR_UNSUPPORTED  # 8 + 121 keys
+        assert _grp(L, f32, [_g()]) == _lib.GIST_ERR_UNSUPPORTED
+        # a query-gist pool needs q_ids in every group that has pairs
+        q4 = _pool(L, k=4)
+        try:
+            assert _grp(L, pool, [_g(qids=FAKE), _g()], qpool=q4) == _lib.GIST_ERR_INVALID_ARG
+            assert _grp(L, pool, [_g(P=0, ptr=None, ids=None)], qpool=q4) == _lib.GIST_OK
+        finally:
+            L.gist_pool_destroy(q4)
+        # no pairs at all: a no-op that touches nothing
+        assert _grp(L, pool, []) == _lib.GIST_OK
+        assert _grp(L, pool, [_g(P=0, ptr=None, ids=None)] * 32) == _lib.GIST_OK
+    finally:
+        L.gist_pool_destroy(pool)
+        L.gist_pool_destroy(f32)
+
+
 def test_pool_write_validation(L):
     pool = _pool(L)
     try:

@@ -1039,3 +1039,74 @@ def test_paged_gist_ell_bad_block_gives_nan_rows(fp8):
     o = f64(o)
     torch.cuda.synchronize()
     assert np.isnan(o[[1, 2]]).all() and np.isfinite(o[[0, 3]]).all()
+
+
+# ---------------------------------------------------------------------------
+# Grouped launch: several calls of one shape in one launch
+# ---------------------------------------------------------------------------
+
+
+def _grouped_vs_calls(case, groups, qpool=None):
+    """groups: (layer, P) over the case's activations of that layer (the first
+    P pairs).  Runs them as one grouped launch and as one call each; returns
+    the grouped outputs after checking them equal to the calls' bit for bit."""
+    import gist_compressed_kv_amd as G
+    specs = []
+    for layer, P in groups:
+        spec = {"layer": layer, "item_ids": case.ids[:P], "q": case.q[layer][:P],
+                "k_new": case.kn[layer][:P], "v_new": case.vn[layer][:P]}
+        if case.qpool is not None:
+            spec["q_ids"] = case.q_ids[:P]
+        specs.append(spec)
+    outs = G.gist_attn_forward_grouped(case.pool, specs, pos0=case.pos0, rope_base=ROPE_BASE,
+                                       scale=case.scale, qpool=case.qpool)
+    torch.cuda.synchronize()
+    for (layer, P), sp, o in zip(groups, specs, outs):
+        ref = G.gist_attn_forward(case.pool, layer, sp["item_ids"], sp["q"], sp["k_new"],
+                                  sp["v_new"], case.pos0, ROPE_BASE, case.scale, qpool=case.qpool,
+                                  q_ids=sp.get("q_ids"))
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref), (layer, P)
+    return outs
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_grouped_24_layer_pool_equals_calls(fp8):
+    # the 24-layer, 100k-item pool of the 500-pair workload (layer 23's
+    # records lie past 2^31 elements); groups of several sizes, a layer twice
+    wl = synth.L24_B500
+    case = GistCase(wl.layers, wl.n_items, wl.k, wl.ell, wl.hq, wl.h, wl.d, wl.pairs, wl.dtype,
+                    wl.seed + 40, ids=_ids(wl), fp8=fp8, act_layers=[0, 5, 23])
+    groups = [(23, 500), (0, 37), (5, 1), (23, 200), (0, 500)]
+    outs = _grouped_vs_calls(case, groups)
+    sample = np.array([0, 1, 36, 250, 499])
+    err = case.max_err(23, outs[0], sample)
+    say(f"grouped, layer 23 of 24 ({'fp8' if fp8 else 'bf16'}): max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_grouped_query_gist_and_many_groups():
+    # k' = 8 query gists; 32 groups (the most one launch takes), 3 pairs each
+    qids = torch.arange(60) % 4
+    case = GistCase(6, 50, 8, 24, 16, 2, 128, 60, torch.bfloat16, 1200, kq=8, n_qrows=4,
+                    q_ids=qids)
+    groups = [(i % 6, 3 + (i % 5) * 10) for i in range(32)]
+    outs = _grouped_vs_calls(case, groups)
+    err = max(case.max_err(layer, o, np.arange(P)) for (layer, P), o in zip(groups[:6], outs[:6]))
+    say(f"grouped, 32 groups with query gists: max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_grouped_bad_id_only_touches_its_group():
+    import gist_compressed_kv_amd as G
+    case = GistCase(2, 11, 8, 64, 14, 2, 64, 6, torch.bfloat16, 1210)
+    bad = case.ids.clone()
+    bad[2] = 11
+    specs = [{"layer": 0, "item_ids": case.ids, "q": case.q[0], "k_new": case.kn[0], "v_new": case.vn[0]},
+             {"layer": 1, "item_ids": bad, "q": case.q[1], "k_new": case.kn[1], "v_new": case.vn[1]}]
+    o0, o1 = G.gist_attn_forward_grouped(case.pool, specs, pos0=case.pos0, rope_base=ROPE_BASE,
+                                         scale=case.scale)
+    torch.cuda.synchronize()
+    o0, o1 = f64(o0), f64(o1)
+    assert np.isfinite(o0).all()
+    assert np.isnan(o1[2]).all() and np.isfinite(np.delete(o1, 2, axis=0)).all()
