@@ -34,6 +34,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # workload, and the kernel source they were taken on
 COUNTER_FILES = {
     "24L_b500": ("gist_fwd_mfma_d64_24L_b500_counters.json", "gist_forward.hip"),
+    "24L_b500_grouped": ("gist_fwd_mfma_grouped_d64_24L_b500_counters.json", "gist_forward.hip"),
     "24L_b2000": ("gist_fwd_mfma_d64_24L_b2000_counters.json", "gist_forward.hip"),
     "wide_ell64": ("gist_fwd_mfma_d128_wide_ell64_counters.json", "gist_forward.hip"),
     "wide_eos": ("gist_fwd_eos_d128_wide_eos_counters.json", "gist_forward.hip"),
