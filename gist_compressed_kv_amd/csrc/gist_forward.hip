@@ -928,9 +928,15 @@ gist_fwd_eos(const FwdArgs a) {
   const int ngt = (kg + 15) >> 4;
   bf16_t* out = (bf16_t*)a.out;
   const int64_t orow0 = ((int64_t)p * Hq + (int64_t)g * G) * D;
+  // the ids first: the gist loads wait for them, and issued ahead of the
+  // token's row traffic they do not queue behind it (both loads are in
+  // flight before either is waited on)
+  const int32_t item = a.item_ids[p];
+  const int32_t qid = *(a.kq ? a.q_ids + p : a.item_ids + p);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- the token's own rows first: they do not depend on the ids, so their
-  // HBM traffic starts while the ids are in flight ------------------------
+  // ---- the token's own rows: they do not depend on the ids, so their HBM
+  // traffic starts while the ids are in flight ------------------------------
   // Q, coalesced: unit u = lane + 64*i covers head u / (D/16) and its chunk
   // pair (channels 8c..8c+7 and their RoPE partners D/2 + 8c..), so each
   // head's row is read whole and once; units past the group read its last
@@ -957,10 +963,7 @@ gist_fwd_eos(const FwdArgs a) {
   const u32x4_t rself = *(const u32x4_t*)(vnew + 8 * sc);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN); the
-  // two loads are issued before either is waited on -----------------------
-  const int32_t item = a.item_ids[p];
-  const int32_t qid = *(a.kq ? a.q_ids + p : a.item_ids + p);
+  // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
   bool bad = item < 0 || item >= a.N;
   if (a.kq) bad = bad || qid < 0 || qid >= a.qN;
   if (bad) {
