@@ -963,37 +963,45 @@ gist_fwd_eos(const FwdArgs a) {
   const u32x4_t rself = *(const u32x4_t*)(vnew + 8 * sc);
   __builtin_amdgcn_sched_barrier(0);
 
+  // the arguments that the gist addresses need, read in one batch here: left
+  // to the branches below, they were fetched one dependent scalar round trip
+  // at a time after the ids arrived.  The empty asm makes them (and the ids)
+  // arrive at this point.
+  const int paged = a.paged, ak = a.k, akq = a.kq, bsz = a.block_size, qrow0 = a.q_row0;
+  const int64_t aN = a.N, aqN = a.qN, plo = a.pool_layer_off, qplo = a.qpool_layer_off;
+  const C *pool_c = (const C*)a.pool, *qpool_c = (const C*)a.qpool;
+  const C *pk_c = (const C*)a.paged_k, *pv_c = (const C*)a.paged_v;
+  asm volatile("" ::"s"(paged), "s"(ak), "s"(akq), "s"(bsz), "s"(qrow0), "s"(aN), "s"(aqN), "s"(plo),
+               "s"(qplo), "s"(pool_c), "s"(qpool_c), "s"(pk_c), "s"(pv_c), "s"(item), "s"(qid));
+
   // ---- ids (bounds-checked; a bad id turns the pair's rows into NaN) ------
-  bool bad = item < 0 || item >= a.N;
-  if (a.kq) bad = bad || qid < 0 || qid >= a.qN;
+  bool bad = item < 0 || item >= aN;
+  if (akq) bad = bad || qid < 0 || qid >= aqN;
   if (bad) {
     for (int u = lane; u < G * D; u += 64) out[orow0 + u] = nan_value<bf16_t>();
     return;
   }
   // first K and V rows of the item gist and of the query gist
   const C *gK, *gV, *qK, *qV;
-  if (a.paged) {
-    const int64_t ib = ((int64_t)item * a.H + g) * a.block_size * D;
-    const int64_t qb = (((int64_t)qid * a.H + g) * a.block_size + a.q_row0) * D;
-    gK = (const C*)a.paged_k + ib;
-    gV = (const C*)a.paged_v + ib;
-    qK = (const C*)a.paged_k + qb;
-    qV = (const C*)a.paged_v + qb;
+  if (paged) {
+    const int64_t ib = ((int64_t)item * a.H + g) * bsz * D;
+    const int64_t qb = (((int64_t)qid * a.H + g) * bsz + qrow0) * D;
+    gK = pk_c + ib;
+    gV = pv_c + ib;
+    qK = pk_c + qb;
+    qV = pv_c + qb;
   } else {
     // pool record: K of every head, then V of every head
-    gK = (const C*)a.pool + a.pool_layer_off + (int64_t)item * 2 * a.H * a.k * D +
-         (int64_t)g * a.k * D;
-    gV = gK + (int64_t)a.H * a.k * D;
+    gK = pool_c + plo + (int64_t)item * 2 * a.H * ak * D + (int64_t)g * ak * D;
+    gV = gK + (int64_t)a.H * ak * D;
     qK = gK;
-    if (a.kq)
-      qK = (const C*)a.qpool + a.qpool_layer_off + (int64_t)qid * 2 * a.H * a.kq * D +
-           (int64_t)g * a.kq * D;
-    qV = qK + (int64_t)a.H * a.kq * D;
+    if (akq) qK = qpool_c + qplo + (int64_t)qid * 2 * a.H * akq * D + (int64_t)g * akq * D;
+    qV = qK + (int64_t)a.H * akq * D;
   }
   // gist key j (< kg): its K row, or V row
   auto gist_row = [&](int j, bool v) -> const C* {
-    if (j < a.k) return (v ? gV : gK) + (int64_t)j * D;
-    return (v ? qV : qK) + (int64_t)(j - a.k) * D;
+    if (j < ak) return (v ? gV : gK) + (int64_t)j * D;
+    return (v ? qV : qK) + (int64_t)(j - ak) * D;
   };
 
   // ---- gist loads, all unconditional (clamped rows) ------------------------
@@ -1017,14 +1025,16 @@ gist_fwd_eos(const FwdArgs a) {
     graw[it] = *(const CV*)(gist_row(r < kg ? r : 0, true) + 8 * c);
   }
   __builtin_amdgcn_sched_barrier(0);
-  // fp8: scales of the item and query gist (K, V); wave-uniform scalars
+  // fp8: scales of the item and query gist (K, V); wave-uniform scalars.
+  // (Vector loads, which would keep them off the counter the LDS waits below
+  // share, cost a wave of occupancy and ran slower.)
   float ski = 1.f, svi = 1.f, skq = 1.f, svq = 1.f;
   if constexpr (FP8) {
-    if (a.paged) {
+    if (paged) {
       // paged cache: the scales of the gists' blocks
       ski = a.paged_kscales[(int64_t)item * a.H + g];
       svi = a.paged_vscales[(int64_t)item * a.H + g];
-      if (a.kq) {
+      if (akq) {
         skq = a.paged_kscales[(int64_t)qid * a.H + g];
         svq = a.paged_vscales[(int64_t)qid * a.H + g];
       }
@@ -1032,7 +1042,7 @@ gist_fwd_eos(const FwdArgs a) {
       const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
       ski = si[g];
       svi = si[a.H + g];
-      if (a.kq) {
+      if (akq) {
         const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
         skq = sq[g];
         svq = sq[a.H + g];
