@@ -62,6 +62,9 @@ struct FwdArgs {
   // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
   // set bits b of i, for kernels that form a lane's frequency from scalars
   double rev_step[6];
+  // (cos, sin) of channel pair i at position pos0, evaluated on the host in
+  // double: the EOS kernel's single token of every pair sits at pos0
+  float cs_pos0[kMaxHalfDim][2];
   // fp8 pools: this layer's scales [N][2][H] (and [qN][2][H]); pool offsets
   // are then in bytes
   const float* pool_scales;
@@ -928,6 +931,11 @@ gist_fwd_eos(const FwdArgs a) {
   const int ngt = (kg + 15) >> 4;
   bf16_t* out = (bf16_t*)a.out;
   const int64_t orow0 = ((int64_t)p * Hq + (int64_t)g * G) * D;
+  // (cos, sin) at pos0 of channel pair `lane` (a lane-indexed read of the
+  // arguments, hence a vector load: issued first, so that waiting for it
+  // waits for nothing else)
+  const float cs_c = a.cs_pos0[lane & (D / 2 - 1)][0], cs_s = a.cs_pos0[lane & (D / 2 - 1)][1];
+  __builtin_amdgcn_sched_barrier(0);
   // the ids first: the gist loads wait for them, and issued ahead of the
   // token's row traffic they do not queue behind it (both loads are in
   // flight before either is waited on)
@@ -1062,17 +1070,9 @@ gist_fwd_eos(const FwdArgs a) {
     }
   };
 
-  // ---- cos/sin at pos0: lane i < D/2 evaluates channel pair i; its
-  // frequency rev_0 * q^i comes from scalar arguments --------------------
+  // ---- cos/sin at pos0 into the wave's table (lane i < D/2: pair i) -----
   float2* cst = cs_lds[wv];
-  float csc = 1.f, css = 0.f;
-  if (lane < D / 2) {
-    double rev = a.freqs.rev[0];
-#pragma unroll
-    for (int b = 0; b < 6; ++b) rev *= ((lane >> b) & 1) ? a.rev_step[b] : 1.0;
-    rope_cos_sin((double)a.pos0, rev, csc, css);
-    cst[lane] = make_float2(csc, css);
-  }
+  if (lane < D / 2) cst[lane] = make_float2(cs_c, cs_s);
   wave_lds_sync();
 
   // ---- rotate Q at pos0 in the coalesced layout, split it into bf16 hi +
@@ -1609,6 +1609,22 @@ void launch_eos(const FwdArgs& a, int d, int kg, bool fp8, hipStream_t s) {
   }
 }
 
+// RoPE tables of a call: revolutions per position of every channel pair,
+// the scalar steps q^(2^b), and (cos, sin) at pos0.  Revolutions are reduced
+// to a fraction in double before the angle is formed, as on the device.
+void set_rope(FwdArgs& a, int d, float rope_base, int pos0) {
+  make_rope_freqs(a.freqs, d, rope_base);
+  double q = std::pow((double)rope_base, -2.0 / (double)d);
+  for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < kMaxHalfDim; ++i) {
+    const double r = (double)pos0 * a.freqs.rev[i];
+    const double f = r - std::rint(r);
+    a.cs_pos0[i][0] = (float)std::cos(two_pi * f);
+    a.cs_pos0[i][1] = (float)std::sin(two_pi * f);
+  }
+}
+
 // The arguments shared by every workgroup of a pooled call at one layer
 // (per-call pointers, P and last_only are left for the caller to set)
 void fill_args(FwdArgs& a, const gist_pool* pool, const gist_pool* qpool, int layer, int ell,
@@ -1641,9 +1657,7 @@ void fill_args(FwdArgs& a, const gist_pool* pool, const gist_pool* qpool, int la
   a.block_size = 0;
   a.q_row0 = 0;
   a.paged_kscales = a.paged_vscales = nullptr;
-  make_rope_freqs(a.freqs, d, rope_base);
-  double q = std::pow((double)rope_base, -2.0 / (double)d);
-  for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
+  set_rope(a, d, rope_base, pos0);
 }
 
 // gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
@@ -1869,11 +1883,7 @@ gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const f
   a.G = Hq / H;
   a.pos0 = pos0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  make_rope_freqs(a.freqs, d, rope_base);
-  {
-    double qq = std::pow((double)rope_base, -2.0 / (double)d);
-    for (int b = 0; b < 6; ++b, qq *= qq) a.rev_step[b] = qq;
-  }
+  set_rope(a, d, rope_base, pos0);
   a.paged = 1;
   a.paged_k = k_cache;
   a.paged_v = v_cache;
