@@ -74,7 +74,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="24L_b500",
-                    choices=["24L_b500", "24L_b500_last", "24L_b500_grouped", "24L_b2000", "1L_b500",
+                    choices=["24L_b500", "24L_b500_last", "24L_b500_grouped", "wide_eos_grouped",
+                             "wide_eos_fp8_grouped", "24L_b2000", "1L_b500",
                              "1L_b500_paged",
                              "wide_ell64",
                              "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
@@ -585,7 +586,8 @@ def run(args):
     # token's rows (what the score head reads)
     last_layer_eos = args.workload == "24L_b500_last"
     wl = {"24L_b500": synth.L24_B500, "24L_b500_last": synth.L24_B500,
-          "24L_b500_grouped": synth.L24_B500, "24L_b2000": synth.L24_B2000,
+          "24L_b500_grouped": synth.L24_B500, "wide_eos_grouped": synth.WIDE_EOS,
+          "wide_eos_fp8_grouped": synth.WIDE_EOS_FP8, "24L_b2000": synth.L24_B2000,
           "1L_b500": synth.SINGLE_LAYER, "1L_b500_paged": synth.SINGLE_LAYER,
           "wide_ell64": synth.WIDE_ELL64, "wide_ell64_fp8": synth.WIDE_ELL64_FP8,
           "wide_eos": synth.WIDE_EOS, "wide_eos_fp8": synth.WIDE_EOS_FP8}[args.workload]
@@ -617,8 +619,10 @@ def run(args):
     # one distinct activation set per layer, and at least four for the
     # single-layer workload (one 133 MB set would stay in the 256 MB
     # Infinity Cache); consecutive passes walk through the sets.  The wide
-    # workloads reuse one set: 4.8 GB per layer already dwarfs every cache.
-    n_sets = max(wl.layers, 4) if wl.d == 64 else 1
+    # l = 64 workloads reuse one set: 4.8 GB per layer already dwarfs every
+    # cache.  The wide EOS workloads walk through eight sets (a layer's
+    # 72 MB of Q, K/V_new and O would otherwise stay cached between layers).
+    n_sets = max(wl.layers, 4) if wl.d == 64 else (8 if wl.ell == 1 else 1)
     qs, kns, vns, outs = [], [], [], []
     for li in range(n_sets):
         qs.append(synth.randn((wl.pairs, wl.ell, wl.hq, wl.d), synth.tensor_seed(wl.seed, 3, li), wl.dtype, dev))
@@ -632,14 +636,20 @@ def run(args):
         kc = torch.zeros((wl.n_items, wl.h, 16, wl.d), dtype=wl.dtype, device=dev)
         vc = torch.zeros_like(kc)
         kc[:, :, :wl.k], vc[:, :, :wl.k] = pool_t[0, :, 0], pool_t[0, :, 1]
-    # 24L_b500_grouped: the pass's 24 layer calls as one grouped launch (each
-    # layer a group with its own activation set)
+    # *_grouped: the pass's layer calls as one grouped launch (each layer a
+    # group with the activation set the per-layer pass gives it, and an
+    # output of its own)
     grouped = None
-    if args.workload == "24L_b500_grouped":
-        grouped = G.GroupedForward(pool, [{"layer": li, "item_ids": ids, "q": qs[li], "k_new": kns[li],
-                                           "v_new": vns[li], "out": outs[li]}
-                                          for li in range(wl.layers)], pos0=wl.pos0,
-                                   rope_base=10000.0, scale=1.0 / math.sqrt(wl.d))
+    if args.workload.endswith("_grouped"):
+        specs = []
+        for li in range(wl.layers):
+            sp = {"layer": li, "item_ids": ids, "q": qs[li % n_sets], "k_new": kns[li % n_sets],
+                  "v_new": vns[li % n_sets], "out": torch.empty_like(qs[li % n_sets])}
+            if qpool is not None:
+                sp["q_ids"] = q_ids
+            specs.append(sp)
+        grouped = G.GroupedForward(pool, specs, pos0=wl.pos0, rope_base=10000.0,
+                                   scale=1.0 / math.sqrt(wl.d), qpool=qpool)
     q_lasts = [q[:, -1].contiguous() for q in qs] if last_layer_eos else None
     out_last = torch.empty_like(q_lasts[0]) if last_layer_eos else None
     torch.cuda.synchronize()
@@ -696,7 +706,7 @@ def run(args):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    # the grouped workload runs the pass as one launch of all 24 layers
+    # a grouped workload runs the whole pass as one launch
     launches = 1 if grouped is not None else wl.layers
     avg_launch_s = evs[0].elapsed_time(evs[-1]) / 1e3 / (args.steps * launches)
     pass_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
@@ -731,7 +741,7 @@ def run(args):
         "data": "synthetic: N(0,1) pools" + (" (E4M3 codes, scale amax/448 per block)" if wl.fp8 else "")
                 + ", Q/K/V; seeded item ids (50 distinct candidates per query)"
                 + ("; gists read from a paged cache of 16-row blocks" if paged else "")
-                + ("; the 24 layer calls of a pass as one grouped launch" if grouped is not None else ""),
+                + (f"; the {wl.layers} layer calls of a pass as one grouped launch" if grouped is not None else ""),
         "config": {"workload": wl.name + (", gists in a paged cache" if paged else ""), "layers": wl.layers, "pairs": wl.pairs, "hq": wl.hq,
                    "h": wl.h, "head_dim": wl.d, "k": wl.k, "k_query_gist": wl.kq, "ell": wl.ell,
                    "pool_items": wl.n_items, "parallelism": "single GPU"},
@@ -741,7 +751,8 @@ def run(args):
             "bound": "hbm",
             "kernel": "gist_fwd_mfma<64> (23 full layers + 1 last-token layer; pass bytes / "
                       "launches)" if last_layer_eos else
-                      "gist_fwd_mfma_grouped<64> (24 layer groups in one launch)" if grouped is not None else
+                      (f"gist_fwd_{'mfma' if wl.ell > 1 else 'eos'}_grouped<{wl.d}{', fp8 gist' if wl.fp8 else ''}>"
+                       f" ({wl.layers} layer groups in one launch)") if grouped is not None else
                       "gist_fwd_mfma<64>" if wl.ell > 1 and wl.d == 64 else
                       (("gist_fwd_mfma<128, fp8 gist>" if wl.fp8 else "gist_fwd_mfma<128>") if wl.ell > 1 else
                        ("gist_fwd_eos<128, fp8 gist>" if wl.fp8 else "gist_fwd_eos<128>")),

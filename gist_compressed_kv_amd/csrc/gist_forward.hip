@@ -62,9 +62,6 @@ struct FwdArgs {
   // q^(2^b), b = 0..5, with q = base^(-2/d): rev_i = rev_0 * prod over the
   // set bits b of i, for kernels that form a lane's frequency from scalars
   double rev_step[6];
-  // (cos, sin) of channel pair i at position pos0, evaluated on the host in
-  // double: the EOS kernel's single token of every pair sits at pos0
-  float cs_pos0[kMaxHalfDim][2];
   // fp8 pools: this layer's scales [N][2][H] (and [qN][2][H]); pool offsets
   // are then in bytes
   const float* pool_scales;
@@ -82,6 +79,12 @@ struct FwdArgs {
   // fp8 paged gist: one scale per (block, KV head) for K and one for V
   const float* paged_kscales;
   const float* paged_vscales;
+};
+
+// (cos, sin) of channel pair i at position pos0, evaluated on the host in
+// double: the EOS kernel's single token of every pair sits at pos0
+struct CsPos0 {
+  float v[kMaxHalfDim][2];
 };
 
 // What one workgroup of the l >= 2 kernel reads and writes: its call's
@@ -112,11 +115,17 @@ struct GroupEntry {
   int64_t layer;
 };
 struct GroupTable {
-  int wg_end[kMaxGroups];  // running workgroup count after group i (INT_MAX past the last)
+  // running count of (pair, KV head) units after group i (INT_MAX past the
+  // last): the l >= 2 kernel's workgroups, the EOS kernel's waves
+  int wg_end[kMaxGroups];
+  int units;  // all groups' units
   GroupEntry e[kMaxGroups];
   int64_t pool_layer_stride, qpool_layer_stride;    // elements (fp8: bytes) per layer
   int64_t scale_layer_stride, qscale_layer_stride;  // fp8 scales per layer
 };
+// the grouped EOS launch passes all three by value
+static_assert(sizeof(FwdArgs) + sizeof(CsPos0) + sizeof(GroupTable) <= 4096,
+              "kernel arguments within 4 KiB");
 
 // ---------------------------------------------------------------------------
 // Shared helpers
@@ -903,8 +912,7 @@ gist_fwd_mfma_grouped(const FwdArgs a, const GroupTable t, int nk_pad) {
 // the unscaled weight).
 // QU: Q staging units per lane, G*D/16 units over 64 lanes (1 or 2).
 template <int D, int NGT, bool FP8, int QU>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
-gist_fwd_eos(const FwdArgs a) {
+__device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, const Slice& sl) {
   constexpr int NS = D / 32;
   constexpr int NDT = D / 16;
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -923,24 +931,22 @@ gist_fwd_eos(const FwdArgs a) {
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q4 = lane >> 4;
-  const int unit = blockIdx.x * 4 + wv;
-  if (unit >= a.P * a.H) return;
-  const int p = unit / a.H, g = unit - (unit / a.H) * a.H;
+  const int p = sl.p, g = sl.g;
   const int G = a.G, Hq = a.Hq;
   const int kg = a.k + a.kq;  // >= 1
   const int ngt = (kg + 15) >> 4;
-  bf16_t* out = (bf16_t*)a.out;
+  bf16_t* out = (bf16_t*)sl.out;
   const int64_t orow0 = ((int64_t)p * Hq + (int64_t)g * G) * D;
   // (cos, sin) at pos0 of channel pair `lane` (a lane-indexed read of the
   // arguments, hence a vector load: issued first, so that waiting for it
   // waits for nothing else)
-  const float cs_c = a.cs_pos0[lane & (D / 2 - 1)][0], cs_s = a.cs_pos0[lane & (D / 2 - 1)][1];
+  const float cs_c = cs.v[lane & (D / 2 - 1)][0], cs_s = cs.v[lane & (D / 2 - 1)][1];
   __builtin_amdgcn_sched_barrier(0);
   // the ids first: the gist loads wait for them, and issued ahead of the
   // token's row traffic they do not queue behind it (both loads are in
   // flight before either is waited on)
-  const int32_t item = a.item_ids[p];
-  const int32_t qid = *(a.kq ? a.q_ids + p : a.item_ids + p);
+  const int32_t item = sl.item_ids[p];
+  const int32_t qid = *(a.kq ? sl.q_ids + p : sl.item_ids + p);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- the token's own rows: they do not depend on the ids, so their HBM
@@ -951,9 +957,9 @@ gist_fwd_eos(const FwdArgs a) {
   // head's first pair.  The same chunk pair of K_new goes with it (the
   // group's lanes share the one 128- or 256-byte row).
   constexpr int QCH = D / 16;  // chunk pairs per head
-  const bf16_t* qgrp = (const bf16_t*)a.q + ((int64_t)p * Hq + (int64_t)g * G) * D;
-  const bf16_t* knew = (const bf16_t*)a.k_new + ((int64_t)p * a.H + g) * D;
-  const bf16_t* vnew = (const bf16_t*)a.v_new + ((int64_t)p * a.H + g) * D;
+  const bf16_t* qgrp = (const bf16_t*)sl.q + ((int64_t)p * Hq + (int64_t)g * G) * D;
+  const bf16_t* knew = (const bf16_t*)sl.k_new + ((int64_t)p * a.H + g) * D;
+  const bf16_t* vnew = (const bf16_t*)sl.v_new + ((int64_t)p * a.H + g) * D;
   u32x4_t qlo[QU], qhi[QU], klo[QU], khi[QU];
 #pragma unroll
   for (int i = 0; i < QU; ++i) {
@@ -976,7 +982,7 @@ gist_fwd_eos(const FwdArgs a) {
   // at a time after the ids arrived.  The empty asm makes them (and the ids)
   // arrive at this point.
   const int paged = a.paged, ak = a.k, akq = a.kq, bsz = a.block_size, qrow0 = a.q_row0;
-  const int64_t aN = a.N, aqN = a.qN, plo = a.pool_layer_off, qplo = a.qpool_layer_off;
+  const int64_t aN = a.N, aqN = a.qN, plo = sl.pool_off, qplo = sl.qpool_off;
   const C *pool_c = (const C*)a.pool, *qpool_c = (const C*)a.qpool;
   const C *pk_c = (const C*)a.paged_k, *pv_c = (const C*)a.paged_v;
   asm volatile("" ::"s"(paged), "s"(ak), "s"(akq), "s"(bsz), "s"(qrow0), "s"(aN), "s"(aqN), "s"(plo),
@@ -1047,11 +1053,11 @@ gist_fwd_eos(const FwdArgs a) {
         svq = a.paged_vscales[(int64_t)qid * a.H + g];
       }
     } else {
-      const float* si = a.pool_scales + (int64_t)item * 2 * a.H;
+      const float* si = sl.pool_scales + (int64_t)item * 2 * a.H;
       ski = si[g];
       svi = si[a.H + g];
       if (akq) {
-        const float* sq = a.qpool_scales + (int64_t)qid * 2 * a.H;
+        const float* sq = sl.qpool_scales + (int64_t)qid * 2 * a.H;
         skq = sq[g];
         svq = sq[a.H + g];
       }
@@ -1275,6 +1281,57 @@ gist_fwd_eos(const FwdArgs a) {
       *(uint4*)(orow + 32 * s) = pack8_bf16(v);
     }
   }
+}
+
+template <int D, int NGT, bool FP8, int QU>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
+gist_fwd_eos(const FwdArgs a, const CsPos0 cs) {
+  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= a.P * a.H) return;
+  Slice sl;
+  sl.bid = blockIdx.x;
+  sl.p = unit / a.H;
+  sl.g = unit - sl.p * a.H;
+  sl.q = a.q;
+  sl.k_new = a.k_new;
+  sl.v_new = a.v_new;
+  sl.out = a.out;
+  sl.item_ids = a.item_ids;
+  sl.q_ids = a.q_ids;
+  sl.pool_off = a.pool_layer_off;
+  sl.qpool_off = a.qpool_layer_off;
+  sl.pool_scales = a.pool_scales;
+  sl.qpool_scales = a.qpool_scales;
+  eos_body<D, NGT, FP8, QU>(a, cs, sl);
+}
+
+// The EOS kernel over the groups of a grouped launch: wave u of the launch
+// takes (pair, KV head) unit u of the concatenated groups.
+template <int D, int NGT, bool FP8, int QU>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
+gist_fwd_eos_grouped(const FwdArgs a, const CsPos0 cs, const GroupTable t) {
+  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (unit >= t.units) return;
+  int gi = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxGroups - 1; ++i) gi += unit >= t.wg_end[i] ? 1 : 0;
+  const GroupEntry& e = t.e[gi];
+  const int local = unit - (gi == 0 ? 0 : t.wg_end[gi - 1]);
+  Slice sl;
+  sl.bid = blockIdx.x;
+  sl.p = local / a.H;
+  sl.g = local - sl.p * a.H;
+  sl.q = e.q;
+  sl.k_new = e.k_new;
+  sl.v_new = e.v_new;
+  sl.out = e.out;
+  sl.item_ids = e.item_ids;
+  sl.q_ids = e.q_ids;
+  sl.pool_off = (int64_t)e.layer * t.pool_layer_stride;
+  sl.qpool_off = (int64_t)e.layer * t.qpool_layer_stride;
+  sl.pool_scales = FP8 ? a.pool_scales + (int64_t)e.layer * t.scale_layer_stride : nullptr;
+  sl.qpool_scales = FP8 && a.kq ? a.qpool_scales + (int64_t)e.layer * t.qscale_layer_stride : nullptr;
+  eos_body<D, NGT, FP8, QU>(a, cs, sl);
 }
 
 // ---------------------------------------------------------------------------
@@ -1585,16 +1642,37 @@ void launch_mfma(const FwdArgs& a, int d, int nk_pad, bool fp8, bool last, hipSt
 }
 
 // The l = 1 (EOS) kernel for a call's shape.
-void launch_eos(const FwdArgs& a, int d, int kg, bool fp8, hipStream_t s) {
-  const dim3 grid((unsigned)(((int64_t)a.P * a.H + 3) / 4));
+void launch_eos(const FwdArgs& a, const GroupTable* t, int64_t units, int d, int kg, bool fp8,
+                hipStream_t s) {
+  const dim3 grid((unsigned)((units + 3) / 4));
+  // (cos, sin) at pos0: the revolutions are reduced to a fraction in double
+  // before the angle is formed, as the other kernels do on the device
+  CsPos0 cs;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < kMaxHalfDim; ++i) {
+    const double r = (double)a.pos0 * a.freqs.rev[i];
+    const double f = r - std::rint(r);
+    cs.v[i][0] = (float)std::cos(two_pi * f);
+    cs.v[i][1] = (float)std::sin(two_pi * f);
+  }
   // Q staging units per lane: G heads x d/16 chunk pairs over 64 lanes
   const bool qu2 = a.G * (d / 16) > 64;
   auto go = [&](auto d_c, auto ngt_c) {
     constexpr int DD = decltype(d_c)::value, NG = decltype(ngt_c)::value;
-    if (fp8 && qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 2>), grid, dim3(256), 0, s, a);
-    else if (fp8) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, true, 1>), grid, dim3(256), 0, s, a);
-    else if (qu2) hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 2>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gist_fwd_eos<DD, NG, false, 1>), grid, dim3(256), 0, s, a);
+    auto launch = [&](auto f8_c, auto qu_c) {
+      constexpr bool F8 = decltype(f8_c)::value;
+      constexpr int QU = decltype(qu_c)::value;
+      if (t)
+        hipLaunchKernelGGL((gist_fwd_eos_grouped<DD, NG, F8, QU>), grid, dim3(256), 0, s, a, cs, *t);
+      else
+        hipLaunchKernelGGL((gist_fwd_eos<DD, NG, F8, QU>), grid, dim3(256), 0, s, a, cs);
+    };
+    using Q1 = std::integral_constant<int, 1>;
+    using Q2 = std::integral_constant<int, 2>;
+    if (fp8 && qu2) launch(std::true_type{}, Q2{});
+    else if (fp8) launch(std::true_type{}, Q1{});
+    else if (qu2) launch(std::false_type{}, Q2{});
+    else launch(std::false_type{}, Q1{});
   };
   using I64 = std::integral_constant<int, 64>;
   using I128 = std::integral_constant<int, 128>;
@@ -1609,20 +1687,12 @@ void launch_eos(const FwdArgs& a, int d, int kg, bool fp8, hipStream_t s) {
   }
 }
 
-// RoPE tables of a call: revolutions per position of every channel pair,
-// the scalar steps q^(2^b), and (cos, sin) at pos0.  Revolutions are reduced
-// to a fraction in double before the angle is formed, as on the device.
-void set_rope(FwdArgs& a, int d, float rope_base, int pos0) {
+// RoPE tables of a call: revolutions per position of every channel pair and
+// the scalar steps q^(2^b)
+void set_rope(FwdArgs& a, int d, float rope_base) {
   make_rope_freqs(a.freqs, d, rope_base);
   double q = std::pow((double)rope_base, -2.0 / (double)d);
   for (int b = 0; b < 6; ++b, q *= q) a.rev_step[b] = q;
-  const double two_pi = 6.283185307179586476925286766559;
-  for (int i = 0; i < kMaxHalfDim; ++i) {
-    const double r = (double)pos0 * a.freqs.rev[i];
-    const double f = r - std::rint(r);
-    a.cs_pos0[i][0] = (float)std::cos(two_pi * f);
-    a.cs_pos0[i][1] = (float)std::sin(two_pi * f);
-  }
 }
 
 // The arguments shared by every workgroup of a pooled call at one layer
@@ -1657,7 +1727,7 @@ void fill_args(FwdArgs& a, const gist_pool* pool, const gist_pool* qpool, int la
   a.block_size = 0;
   a.q_row0 = 0;
   a.paged_kscales = a.paged_vscales = nullptr;
-  set_rope(a, d, rope_base, pos0);
+  set_rope(a, d, rope_base);
 }
 
 // gist_attn_forward and gist_attn_forward_last (last: q and out hold only the
@@ -1725,7 +1795,7 @@ gist_status attn_forward(const gist_pool* pool, int layer, const int32_t* item_i
     return check_launch("gist_attn_forward(mfma)");
   }
   if ((pool->dtype == GIST_BF16 || fp8) && ell == 1 && a.G <= 16 && kg <= 32) {
-    launch_eos(a, d, kg, fp8, s);
+    launch_eos(a, nullptr, (int64_t)a.P * a.H, d, kg, fp8, s);
     return check_launch("gist_attn_forward(eos)");
   }
   if (pool->dtype == GIST_BF16) {
@@ -1771,10 +1841,12 @@ extern "C" gist_status gist_attn_forward_grouped(const gist_pool* pool, const gi
     return err(GIST_ERR_INVALID_ARG, "qpool must match pool in L, H, d and dtype");
   const int kg = pool->k + (qpool ? qpool->k : 0);
   const int nk_pad = ((kg + ell + 15) / 16) * 16;
-  if (pool->dtype == GIST_F32 || ell < 2 || ell > 64 || nk_pad > 128)
+  const bool eos = ell == 1 && Hq / H <= 16 && kg <= 32;
+  const bool mfma = ell >= 2 && ell <= 64 && nk_pad <= 128;
+  if (pool->dtype == GIST_F32 || !(eos || mfma))
     return err(GIST_ERR_UNSUPPORTED,
-               "groups run the l >= 2 kernel: bf16 or fp8 pools, 2 <= ell <= 64, "
-               "k + k' + ell <= 128");
+               "groups run the EOS kernel (ell == 1, Hq/H <= 16, k + k' <= 32) or the l >= 2 "
+               "kernel (2 <= ell <= 64, k + k' + ell <= 128) over bf16 or fp8 pools");
   GroupTable t;
   int m = 0;
   int64_t wgs = 0;
@@ -1806,6 +1878,7 @@ extern "C" gist_status gist_attn_forward_grouped(const gist_pool* pool, const gi
     t.wg_end[i] = INT32_MAX;
     t.e[i] = t.e[m - 1];
   }
+  t.units = (int)wgs;
   const bool fp8 = pool->dtype == GIST_FP8_E4M3;
   FwdArgs a;
   fill_args(a, pool, qpool, 0, ell, Hq, pos0, rope_base, scale);
@@ -1814,7 +1887,8 @@ extern "C" gist_status gist_attn_forward_grouped(const gist_pool* pool, const gi
   t.scale_layer_stride = fp8 ? pool->N * 2 * H : 0;
   t.qscale_layer_stride = fp8 && qpool ? qpool->N * 2 * H : 0;
   hipStream_t s = (hipStream_t)stream;
-  if (fp8) launch_mfma_t<false, true>(a, &t, wgs, d, nk_pad, s);
+  if (eos) launch_eos(a, &t, wgs, d, kg, fp8, s);
+  else if (fp8) launch_mfma_t<false, true>(a, &t, wgs, d, nk_pad, s);
   else launch_mfma_t<false, false>(a, &t, wgs, d, nk_pad, s);
   return check_launch(fn);
 }
@@ -1883,7 +1957,7 @@ gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const f
   a.G = Hq / H;
   a.pos0 = pos0;
   a.scale_log2 = scale * 1.4426950408889634f;
-  set_rope(a, d, rope_base, pos0);
+  set_rope(a, d, rope_base);
   a.paged = 1;
   a.paged_k = k_cache;
   a.paged_v = v_cache;
@@ -1892,7 +1966,7 @@ gist_status attn_forward_paged(const void* k_cache, const void* v_cache, const f
   a.paged_kscales = fp8 ? k_scale : nullptr;
   a.paged_vscales = fp8 ? v_scale : nullptr;
   hipStream_t s = (hipStream_t)stream;
-  if (ell == 1) launch_eos(a, d, k + kq, fp8, s);
+  if (ell == 1) launch_eos(a, nullptr, (int64_t)P * H, d, k + kq, fp8, s);
   else launch_mfma(a, d, (k + kq + ell + 15) / 16 * 16, fp8, false, s);
   return check_launch(fn);
 }

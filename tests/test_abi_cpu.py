@@ -159,8 +159,9 @@ def test_grouped_validation(L):
         assert _grp(L, pool, [_g()], Hq=66) == _lib.GIST_ERR_UNSUPPORTED
         assert _grp(L, pool, [_g()], scale=0.0) == _lib.GIST_ERR_INVALID_ARG
         assert _grp(L, pool, [_g()], base=float("inf")) == _lib.GIST_ERR_INVALID_ARG
-        # only the l >= 2 kernel runs grouped
-        assert _grp(L, pool, [_g()], ell=1) == _lib.GIST_ERR_UNSUPPORTED
+        # groups run the EOS kernel (ell = 1) or the l >= 2 kernel
+        assert _grp(L, pool, [_g()], ell=1, Hq=34) == _lib.GIST_ERR_UNSUPPORTED  # Hq/H = 17
+        assert _grp(L, pool, [_g(P=0, ptr=None, ids=None)], ell=1) == _lib.GIST_OK
         assert _grp(L, pool, [_g()], ell=65) == _lib.GIST_ERR_UNSUPPORTED
         assert _grp(L, pool, [_g()], ell=121) == _lib.GIST_ERR_UNSUPPORTED  # 8 + 121 keys
         assert _grp(L, f32, [_g()]) == _lib.GIST_ERR_UNSUPPORTED

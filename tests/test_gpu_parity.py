@@ -1110,3 +1110,33 @@ def test_grouped_bad_id_only_touches_its_group():
     o0, o1 = f64(o0), f64(o1)
     assert np.isfinite(o0).all()
     assert np.isnan(o1[2]).all() and np.isfinite(np.delete(o1, 2, axis=0)).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_grouped_eos_equals_calls(fp8):
+    # the EOS step (ell = 1, item gist + query gist + itself) at the wide
+    # shape, grouped over layers of a 4-layer pool, groups of several sizes
+    qids = torch.arange(300) // 50
+    case = GistCase(4, 1000, 8, 1, 64, 8, 128, 300, torch.bfloat16, 1300, kq=8, n_qrows=6,
+                    q_ids=qids, fp8=fp8)
+    groups = [(3, 300), (0, 17), (2, 1), (3, 64), (1, 300)]
+    outs = _grouped_vs_calls(case, groups)
+    err = max(case.max_err(layer, o, np.array([0, P // 2, P - 1]))
+              for (layer, P), o in zip(groups, outs))
+    say(f"grouped EOS ({'fp8' if fp8 else 'bf16'}): max-abs err {err:.3g}")
+    assert err <= TOL[torch.bfloat16]
+
+
+def test_grouped_eos_bad_id_only_touches_its_group():
+    import gist_compressed_kv_amd as G
+    case = GistCase(2, 11, 8, 1, 16, 2, 64, 5, torch.bfloat16, 1310)
+    bad = case.ids.clone()
+    bad[3] = -1
+    specs = [{"layer": 1, "item_ids": bad, "q": case.q[1], "k_new": case.kn[1], "v_new": case.vn[1]},
+             {"layer": 0, "item_ids": case.ids, "q": case.q[0], "k_new": case.kn[0], "v_new": case.vn[0]}]
+    o1, o0 = G.gist_attn_forward_grouped(case.pool, specs, pos0=case.pos0, rope_base=ROPE_BASE,
+                                         scale=case.scale)
+    torch.cuda.synchronize()
+    o0, o1 = f64(o0), f64(o1)
+    assert np.isfinite(o0).all()
+    assert np.isnan(o1[3]).all() and np.isfinite(np.delete(o1, 3, axis=0)).all()
