@@ -247,8 +247,9 @@ gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32
 /*
  * gist_attn_forward_grouped — several independent gist_attn_forward calls of
  * one shape in one launch.  Each group is one call of the online pass of
- * [GIST] 在线的一次 attention (its own layer, pairs, ids, activations and
- * outputs); groups share the pools, ell, Hq, pos0, rope_base and scale.  A
+ * [GIST] 在线的一次 attention, or of its EOS step at ell = 1 ([GIST]
+ * 能不能再进一步) (its own layer, pairs, ids, activations and outputs);
+ * groups share the pools, ell, Hq, pos0, rope_base and scale.  A
  * caller that holds several such calls at once (micro-batches at different
  * layers of a pipelined schedule, or several query batches at one layer)
  * pays one launch instead of one per call, and the last workgroups of one
@@ -259,8 +260,9 @@ gist_status gist_attn_forward_last(const gist_pool* pool, int layer, const int32
  *             q_ids [P] when qpool != NULL)
  *   n_groups  0 .. 32 (more: GIST_ERR_UNSUPPORTED); groups with P == 0 are
  *             skipped, and a call with no pairs is a no-op
- * Limits: the l >= 2 kernel's (bf16 or fp8 pools, 2 <= ell <= 64, k + k' +
- * ell <= 128 rounded up to 16, Hq/H <= 32), else GIST_ERR_UNSUPPORTED; a
+ * Limits: bf16 or fp8 pools, and either ell == 1 with Hq/H <= 16 and k + k'
+ * <= 32 (the EOS kernel) or 2 <= ell <= 64 with k + k' + ell <= 128 rounded
+ * up to 16 and Hq/H <= 32 (the l >= 2 kernel), else GIST_ERR_UNSUPPORTED; a
  * layer out of range is GIST_ERR_OUT_OF_RANGE.  Validation of every group
  * precedes the launch.  Each group's output equals gist_attn_forward's for
  * that group bit for bit (the same kernel code computes every row).  Groups
