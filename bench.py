@@ -38,6 +38,7 @@ COUNTER_FILES = {
     "24L_b2000": ("gist_fwd_mfma_d64_24L_b2000_counters.json", "gist_forward.hip"),
     "wide_ell64": ("gist_fwd_mfma_d128_wide_ell64_counters.json", "gist_forward.hip"),
     "wide_eos": ("gist_fwd_eos_d128_wide_eos_counters.json", "gist_forward.hip"),
+    "wide_eos_grouped": ("gist_fwd_eos_grouped_d128_wide_eos_counters.json", "gist_forward.hip"),
     "wide_eos_fp8": ("gist_fwd_eos_fp8_d128_wide_eos_counters.json", "gist_forward.hip"),
     "paged": ("paged_decode_32x4096_counters.json", "paged_decode.hip"),
     "paged_fp8": ("paged_decode_fp8_32x4096_counters.json", "paged_decode.hip"),
