@@ -274,7 +274,7 @@ def gist_baseline(wl, pool, ids, qs, kns, vns, n_sets, qpool=None, q_ids=None):
 
     if wl.d == 64:
         layers = list(range(wl.layers))
-        npairs = wl.pairs if wl.layers == 1 else min(128, wl.pairs)
+        npairs = wl.pairs if wl.layers == 1 else min(256, wl.pairs)
     elif wl.ell > 1:
         layers = sorted({0, wl.layers // 3, 2 * wl.layers // 3, wl.layers - 1})
         npairs = 128
