@@ -68,7 +68,7 @@ struct FwdArgs {
   const float* qpool_scales;
   // the VALU kernel produces only the last token's rows (q, out: one row per pair)
   int last_only;
-  // paged gist (EOS kernel): item_ids and q_ids are block indices of a paged
+  // paged gists (EOS and l >= 2 kernels): item_ids and q_ids are block indices of a paged
   // cache [N][H][block_size][d] (N blocks; qN = N); the item gist is rows
   // 0..k-1 of its block, the query gist rows q_row0..q_row0+k'-1 of its block
   int paged;
