@@ -211,7 +211,10 @@ class GroupedForward:
         self.rope_base = rope_base
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         dt = pool.act_dtype
-        for i, gr in enumerate(groups):
+        # every group's tensors are checked before any is required to be on
+        # the GPU (one _ptrs call over the whole table)
+        specs, per = [], 6
+        for gr in groups:
             q = gr["q"]
             if q.dim() != 4 or tuple(q.shape[1:]) != (self.ell, self.Hq, pool.d):
                 raise ValueError("every group's q must have shape [P, ell, Hq, d] with one ell and Hq")
@@ -220,13 +223,16 @@ class GroupedForward:
             if out is None:
                 out = torch.empty_like(q)
             kv_shape = (P, self.ell, pool.H, pool.d)
-            ptrs = _ptrs((gr["item_ids"], "item_ids", torch.int32, (P,)), (q, "q", dt, q.shape),
-                         (gr["k_new"], "k_new", dt, kv_shape), (gr["v_new"], "v_new", dt, kv_shape),
-                         (out, "out", dt, q.shape))
-            qi = _dev(gr["q_ids"], "q_ids", torch.int32, (P,)) if qpool is not None else None
-            self.table[i] = _lib.GistGroup(int(gr["layer"]), P, ptrs[0], qi, ptrs[1], ptrs[2],
-                                           ptrs[3], ptrs[4])
+            specs += [(gr["item_ids"], "item_ids", torch.int32, (P,)), (q, "q", dt, q.shape),
+                      (gr["k_new"], "k_new", dt, kv_shape), (gr["v_new"], "v_new", dt, kv_shape),
+                      (out, "out", dt, q.shape),
+                      (gr["q_ids"], "q_ids", torch.int32, (P,)) if qpool is not None else None]
             self.outs.append(out)
+        ptrs = _ptrs(*specs)
+        for i, gr in enumerate(groups):
+            item, q, kn, vn, out, qi = ptrs[per * i:per * (i + 1)]
+            self.table[i] = _lib.GistGroup(int(gr["layer"]), groups[i]["q"].shape[0], item, qi, q,
+                                           kn, vn, out)
         # the tensors stay referenced as long as the table points at them
         self._keep = groups
 

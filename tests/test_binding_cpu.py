@@ -100,3 +100,39 @@ def test_paged_decode_q_and_block_table_shapes(fp8):
         call(z(R + 1, mb, dtype=I32), z(R, hq, d))
     with pytest.raises(ValueError, match=ON_GPU):
         call(z(R, mb, dtype=I32), z(R, hq, d))
+
+
+def _grp(P_=P, ell=ELL, hq=HQ, d=D, kv_h=H, q_ids=False):
+    g = {"layer": 0, "item_ids": z(P_, dtype=I32), "q": z(P_, ell, hq, d),
+         "k_new": z(P_, ell, kv_h, D), "v_new": z(P_, ell, kv_h, D)}
+    if q_ids:
+        g["q_ids"] = z(P_, dtype=I32)
+    return g
+
+
+def test_grouped_shapes_are_checked_group_by_group():
+    # every group shares ell and Hq with the first, and its head size is the pool's
+    with pytest.raises(ValueError, match="one ell and Hq"):
+        G.GroupedForward(POOL, [_grp(), _grp(ell=ELL + 1)])
+    with pytest.raises(ValueError, match="one ell and Hq"):
+        G.GroupedForward(POOL, [_grp(), _grp(hq=HQ + 2)])
+    with pytest.raises(ValueError, match="one ell and Hq"):
+        G.GroupedForward(POOL, [_grp(d=32)])
+    with pytest.raises(ValueError, match="k_new must have shape"):
+        G.GroupedForward(POOL, [_grp(), _grp(kv_h=H + 1)])
+    with pytest.raises(ValueError, match=r"q must have shape \[P, ell, Hq, d\]"):
+        G.GroupedForward(POOL, [{"layer": 0, "item_ids": z(P, dtype=I32), "q": z(P, HQ, D),
+                                 "k_new": z(P, H, D), "v_new": z(P, H, D)}])
+    # a consistent table stops at the device check, before the library
+    with pytest.raises(ValueError, match=ON_GPU):
+        G.GroupedForward(POOL, [_grp(), _grp(P_=5)])
+    # no groups: nothing to launch
+    assert G.gist_attn_forward_grouped(POOL, []) == []
+
+
+def test_grouped_query_gist_ids_are_required():
+    qpool = types.SimpleNamespace(k=8, H=2, d=64, act_dtype=BF, handle=None)
+    with pytest.raises(KeyError):
+        G.GroupedForward(POOL, [_grp()], qpool=qpool)
+    with pytest.raises(ValueError, match=ON_GPU):
+        G.GroupedForward(POOL, [_grp(q_ids=True)], qpool=qpool)
