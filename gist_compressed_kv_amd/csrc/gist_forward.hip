@@ -18,8 +18,9 @@
 //    the G query heads of the GQA group, so every K/V tile in LDS serves all
 //    G heads.  Logits are computed transposed, Sᵀ = K·Qᵀ, with
 //    v_mfma_f32_16x16x32_bf16, so each lane ends up holding four keys of one
-//    token: exactly the B operand layout of the P·V product
-//    (v_mfma_f32_16x16x16_bf16, Oᵀ = Vᵀ·Pᵀ), and the softmax never leaves
+//    token: exactly the B operand layout of the P·V product (Oᵀ = Vᵀ·Pᵀ,
+//    v_mfma_f32_16x16x32_bf16 over pairs of key tiles, 16x16x16 for an
+//    unpaired last one), and the softmax never leaves
 //    registers.  All keys of a token are in registers at once, so the row
 //    maximum is exact before the exponentials; causally invisible tiles are
 //    skipped.
