@@ -917,11 +917,11 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   constexpr int NS = D / 32;
   constexpr int NDT = D / 16;
   constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int VSELF = 16 * NGT;        // LDS row of V_new
-  constexpr int ROWS = 16 * NGT + 1;
+  constexpr int ROWS = 16 * NGT;
   constexpr int RITG = 16 * NGT * CPR / 64;  // gist V row chunks per lane
   static_assert(16 * NGT * CPR % 64 == 0 && 2 * CPR <= 64, "staging layout");
   __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
+  __shared__ __align__(16) float vself_lds[4][D];  // V_new of the token, fp32
   __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) at pos0
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
@@ -1094,25 +1094,34 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   uint4 qlo_st[QU][2];
   float sdot[QU];  // this lane's part of the token's own logit q·k
   auto qpos = [](int h, int c) { return h * D + (((c ^ h) & (CPR - 1)) << 3); };
+  // The token's own logit: its query and its key sit at the same position,
+  // and a rotation keeps dot products, so q·k of the rotated rows is q·k of
+  // the rows as given.  It is summed from the bf16 pairs as loaded (v_dot2:
+  // the products of two bf16 values are exact in fp32); K_new is never
+  // rotated or unpacked here.
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v;
+  auto dot2 = [](uint32_t x, uint32_t y, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y),
+                                           acc, false);
+  };
 #pragma unroll
   for (int i = 0; i < QU; ++i) {
     const int u = lane + 64 * i;
     const int h = u / QCH, c = u - (u / QCH) * QCH;
-    float xl[8], xh[8], yl[8], yh[8], kl[8], kh[8];
+    float dot = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dot = dot2(qlo[i][w], klo[i][w], dot);
+      dot = dot2(qhi[i][w], khi[i][w], dot);
+    }
+    float xl[8], xh[8], yl[8], yh[8];
     unpack8(make_uint4(qlo[i].x, qlo[i].y, qlo[i].z, qlo[i].w), xl);
     unpack8(make_uint4(qhi[i].x, qhi[i].y, qhi[i].z, qhi[i].w), xh);
-    unpack8(make_uint4(klo[i].x, klo[i].y, klo[i].z, klo[i].w), kl);
-    unpack8(make_uint4(khi[i].x, khi[i].y, khi[i].z, khi[i].w), kh);
-    float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float2 cs = cst[8 * c + e];
       yl[e] = __builtin_fmaf(xl[e], cs.x, -(xh[e] * cs.y));
       yh[e] = __builtin_fmaf(xh[e], cs.x, xl[e] * cs.y);
-      const float rl = __builtin_fmaf(kl[e], cs.x, -(kh[e] * cs.y));
-      const float rh = __builtin_fmaf(kh[e], cs.x, kl[e] * cs.y);
-      dot = __builtin_fmaf(yl[e], rl, dot);
-      dot = __builtin_fmaf(yh[e], rh, dot);
     }
     // sum over the QCH lanes of head h (aligned groups of 4 or 8 lanes)
     dot += dpp_f<0xB1>(dot);
@@ -1199,7 +1208,16 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
     const int u = lane + 64 * it;
     put(u / CPR, u - (u / CPR) * CPR, to_bf16x8(graw[it]));
   }
-  if (lane < CPR) put(VSELF, sc, rself);
+  // the token's V row in fp32, unpacked once (lanes past the row repeat it)
+  float* vs = vself_lds[wv];
+  {
+    float f[8];
+    unpack8(make_uint4(rself.x, rself.y, rself.z, rself.w), f);
+    if (lane < CPR) {
+      *(float4*)(vs + 8 * sc) = make_float4(f[0], f[1], f[2], f[3]);
+      *(float4*)(vs + 8 * sc + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+  }
   wave_lds_sync();
   const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
   mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
@@ -1239,14 +1257,10 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
     const float ws = wself * inv;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const uint2* src = (const uint2*)(Rl + vrow_off(VSELF, 32 * s + 8 * q4, D));
-      float v[8];
-      unpack8(make_uint4(src[0].x, src[0].y, src[1].x, src[1].y), v);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        o[2 * s][r] = ws * v[r];
-        o[2 * s + 1][r] = ws * v[4 + r];
-      }
+      const float4 v0 = *(const float4*)(vs + 32 * s + 8 * q4);
+      const float4 v1 = *(const float4*)(vs + 32 * s + 8 * q4 + 4);
+      o[2 * s] = f32x4_t{ws * v0.x, ws * v0.y, ws * v0.z, ws * v0.w};
+      o[2 * s + 1] = f32x4_t{ws * v1.x, ws * v1.y, ws * v1.z, ws * v1.w};
     }
   }
 #pragma unroll
