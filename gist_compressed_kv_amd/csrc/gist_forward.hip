@@ -898,13 +898,14 @@ gist_fwd_mfma_grouped(const FwdArgs a, const GroupTable t, int nk_pad) {
 // slice, so no workgroup barrier is involved.
 //   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
 //   gist (kg = k + k' rows, padded with copies of row 0 that the mask
-//   removes), then the token's own key, rotated at pos0 like the query.
+//   removes), then the token's own key, at pos0 like the query.
 //   The rotated Q is carried as a bf16 pair hi + lo (split8_bf16) and a gist
 //   tile takes K·Q_hi + K·Q_lo on the matrix cores (the stored gist K is
-//   exact in bf16).  The token's own logit is a single key per head: it is
-//   the fp32 dot product of the rotated Q and K_new on the VALU, and its V
-//   row enters the output by fp32 FMAs.  The softmax scale is applied to the
-//   fp32 logits in the exponent.
+//   exact in bf16).  The token's own logit is a single key per head: its
+//   query and key share a position, so RoPE cancels and the logit is q·k of
+//   the unrotated rows on the VALU (v_dot2, exact bf16 products, fp32 sums);
+//   its V row enters the output by fp32 multiplies.  The softmax scale is
+//   applied to the fp32 logits in the exponent.
 // NGT: maximum number of gist tiles (kg <= 16*NGT).
 // FP8: the gist pools hold E4M3 codes.  Every E4M3 value is also a bf16
 // value, so the codes are decoded exactly into the bf16 MFMA operands; the K
