@@ -62,6 +62,14 @@ __device__ __forceinline__ uint4 pack8_bf16(const float* f) {
 // Four OCP FP8 E4M3 codes (one dword, lowest byte first) to floats.  gfx950's
 // v_cvt_pk_f32_fp8 decodes exactly this format (bias 7, subnormals, 0x7F and
 // 0xFF NaN).
+// Two E4M3 codes (bytes 0-1 of w, or 2-3 with HI) as two bf16 values packed
+// low first: gfx950's scaled conversion at scale 1, exact since every E4M3
+// value is a bf16 value.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 __device__ __forceinline__ void decode4_e4m3(uint32_t w, float* f) {
   typedef float f2_t __attribute__((ext_vector_type(2)));
   const f2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);

@@ -583,6 +583,39 @@ def test_fp8_pool_with_power_of_two_scales_equals_bf16_pool(shape, scales):
     assert torch.equal(o8, ob)
 
 
+@pytest.mark.parametrize("shape", [(8, 8, 1, 64, 8, 128, 9), (8, 8, 1, 16, 2, 64, 5),
+                                   (8, 8, 64, 64, 8, 128, 3), (8, 0, 64, 14, 2, 64, 5)],
+                         ids=lambda s: "k%d_kq%d_ell%d_hq%d_h%d_d%d_p%d" % s)
+def test_fp8_pool_every_finite_code_equals_bf16_pool(shape):
+    # every finite E4M3 code (both signs, the subnormals 0x01-0x07, +-448) in
+    # every gist record, K and V, at unit scales: the fp8 pool must give the
+    # bf16 pool of its decoded values (torch's decode) bit for bit, so each
+    # code decodes exactly, on the EOS kernel (ell = 1) and the ell >= 2 one
+    import gist_compressed_kv_amd as G
+    from gpu_cases import ROPE_BASE
+    k, kq, ell, hq, h, d, P = shape
+    qids = (torch.arange(P) * 5) % 3 if kq else None
+    case = GistCase(1, 7, k, ell, hq, h, d, P, torch.bfloat16, 690 + ell + hq, kq=kq, n_qrows=3,
+                    q_ids=qids, fp8=True)
+    finite = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+    bf = []
+    for j, pl in enumerate([case.pool] + ([case.qpool] if case.qpool is not None else [])):
+        n = pl.codes.numel()
+        # 7 is prime to 254: each run of 254 consecutive elements, hence each
+        # K half and each V half of every record, holds every finite code
+        idx = (torch.arange(n) * 7 + 13 * j) % 254
+        pl.codes.copy_(finite[idx].view(pl.codes.shape).to(pl.codes.device))
+        pl.scales.fill_(1.0)
+        bf.append(G.GistPool(pl.codes.view(torch.float8_e4m3fn).float().to(torch.bfloat16).contiguous()))
+    assert h * min(k, kq or k) * d >= 254
+    o8 = case.run(0).clone()
+    ob = G.gist_attn_forward(bf[0], 0, case.ids, case.q[0], case.kn[0], case.vn[0], case.pos0,
+                             ROPE_BASE, case.scale, qpool=bf[1] if kq else None, q_ids=case.q_ids)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o8.float()).all()
+    assert torch.equal(o8, ob)
+
+
 def test_mfma_fp8_out_of_range_ids_give_nan_rows_only():
     case = GistCase(1, 6, 8, 64, 14, 2, 64, 5, torch.bfloat16, 670, ids=torch.tensor([0, 6, 2, -1, 5]),
                     fp8=True)
