@@ -100,29 +100,6 @@ inline void make_rope_freqs(RopeFreqs& f, int d, float base) {
     f.rev[i] = (i < d / 2) ? std::pow((double)base, -2.0 * (double)i / (double)d) / two_pi : 0.0;
 }
 
-// rev[base + 8*chunk + e] for a lane-dependent chunk < NC, with base and e
-// known at compile time: every table read is a scalar load and the lane picks
-// its value with selects.  (Indexing the kernel-argument table with a
-// lane-dependent index would instead issue vector memory loads, which share
-// the wait counter with the data loads in flight.)
-__device__ __forceinline__ double sgpr_value(double v) {
-  // empty asm: keeps v a scalar-loaded value the optimizer cannot fold the
-  // selects below back into one lane-indexed (vector) load
-  asm volatile("" : "+s"(v));
-  return v;
-}
-
-template <int NC>
-__device__ __forceinline__ double rev_pick(const RopeFreqs& f, int base, int chunk, int e) {
-  double r = sgpr_value(f.rev[base + e]);
-#pragma unroll
-  for (int c = 1; c < NC; ++c) {
-    const double v = sgpr_value(f.rev[base + 8 * c + e]);
-    r = chunk == c ? v : r;
-  }
-  return r;
-}
-
 __device__ __forceinline__ void rope_cos_sin(double pos, double rev, float& c, float& s) {
   const double r = pos * rev;
   const float f = (float)(r - rint(r));
