@@ -894,8 +894,9 @@ gist_fwd_mfma_grouped(const FwdArgs a, const GroupTable t, int nk_pad) {
 // query heads are the MFMA columns
 // ---------------------------------------------------------------------------
 
-// One wave per (pair, KV head); four per workgroup, each with its own LDS
-// slice, so no workgroup barrier is involved.
+// One wave per (pair, KV head) and per workgroup: no workgroup barrier, and
+// a finished wave frees its slot at once (four independent waves per
+// workgroup held each slot until the slowest of them ended).
 //   keys, in order: gist tiles 0..ngt-1 hold the item gist then the query
 //   gist (kg = k + k' rows, padded with copies of row 0 that the mask
 //   removes), then the token's own key, at pos0 like the query.
@@ -921,16 +922,16 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   constexpr int ROWS = 16 * NGT;
   constexpr int RITG = 16 * NGT * CPR / 64;  // gist V row chunks per lane
   static_assert(16 * NGT * CPR % 64 == 0 && 2 * CPR <= 64, "staging layout");
-  __shared__ __align__(16) bf16_t rows_lds[4][ROWS * (D + 4)];
-  __shared__ __align__(16) float vself_lds[4][D];  // V_new of the token, fp32
-  __shared__ __align__(16) float2 cs_lds[4][D / 2];  // (cos, sin) at pos0
+  // the workgroup is this one wave
+  __shared__ __align__(16) bf16_t rows_lds[ROWS * (D + 4)];
+  __shared__ __align__(16) float vself_lds[D];  // V_new of the token, fp32
+  __shared__ __align__(16) float2 cs_lds[D / 2];  // (cos, sin) at pos0
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
   typedef std::conditional_t<FP8, uint8_t, bf16_t> C;  // gist element
   typedef std::conditional_t<FP8, uint2, u32x4_t> CV;   // 8 gist elements
 
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int n = lane & 15, q4 = lane >> 4;
   const int p = sl.p, g = sl.g;
@@ -1077,7 +1078,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   };
 
   // ---- cos/sin at pos0 into the wave's table (lane i < D/2: pair i) -----
-  float2* cst = cs_lds[wv];
+  float2* cst = cs_lds;
   if (lane < D / 2) cst[lane] = make_float2(cs_c, cs_s);
   wave_lds_sync();
 
@@ -1088,7 +1089,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   // rows are written with keys only after the B fragments are read.  Row h
   // holds head h; chunk c sits at chunk c ^ h, so the eight lanes of a
   // 16-byte access phase hit distinct banks on both sides.
-  bf16_t* Rl = rows_lds[wv];
+  bf16_t* Rl = rows_lds;
   static_assert(16 * D <= ROWS * (D + 4), "Q staging fits the row buffer");
   uint4 qlo_st[QU][2];
   float sdot[QU];  // this lane's part of the token's own logit q·k
@@ -1208,7 +1209,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
     put(u / CPR, u - (u / CPR) * CPR, to_bf16x8(graw[it]));
   }
   // the token's V row in fp32, unpacked once (lanes past the row repeat it)
-  float* vs = vself_lds[wv];
+  float* vs = vself_lds;
   {
     float f[8];
     unpack8(make_uint4(rself.x, rself.y, rself.z, rself.w), f);
@@ -1298,9 +1299,9 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
 }
 
 template <int D, int NGT, bool FP8, int QU>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
 gist_fwd_eos(const FwdArgs a, const CsPos0 cs) {
-  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x;
   if (unit >= a.P * a.H) return;
   Slice sl;
   sl.bid = blockIdx.x;
@@ -1322,9 +1323,9 @@ gist_fwd_eos(const FwdArgs a, const CsPos0 cs) {
 // The EOS kernel over the groups of a grouped launch: wave u of the launch
 // takes (pair, KV head) unit u of the concatenated groups.
 template <int D, int NGT, bool FP8, int QU>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 128 && NGT == 2 ? 2 : 4)))
 gist_fwd_eos_grouped(const FwdArgs a, const CsPos0 cs, const GroupTable t) {
-  const int unit = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x;
   if (unit >= t.units) return;
   int gi = 0;
 #pragma unroll
@@ -1658,7 +1659,7 @@ void launch_mfma(const FwdArgs& a, int d, int nk_pad, bool fp8, bool last, hipSt
 // The l = 1 (EOS) kernel for a call's shape.
 void launch_eos(const FwdArgs& a, const GroupTable* t, int64_t units, int d, int kg, bool fp8,
                 hipStream_t s) {
-  const dim3 grid((unsigned)((units + 3) / 4));
+  const dim3 grid((unsigned)units);  // one wave per unit and per workgroup
   // (cos, sin) at pos0: the revolutions are reduced to a fraction in double
   // before the angle is formed, as the other kernels do on the device
   CsPos0 cs;
@@ -1677,9 +1678,9 @@ void launch_eos(const FwdArgs& a, const GroupTable* t, int64_t units, int d, int
       constexpr bool F8 = decltype(f8_c)::value;
       constexpr int QU = decltype(qu_c)::value;
       if (t)
-        hipLaunchKernelGGL((gist_fwd_eos_grouped<DD, NG, F8, QU>), grid, dim3(256), 0, s, a, cs, *t);
+        hipLaunchKernelGGL((gist_fwd_eos_grouped<DD, NG, F8, QU>), grid, dim3(64), 0, s, a, cs, *t);
       else
-        hipLaunchKernelGGL((gist_fwd_eos<DD, NG, F8, QU>), grid, dim3(256), 0, s, a, cs);
+        hipLaunchKernelGGL((gist_fwd_eos<DD, NG, F8, QU>), grid, dim3(64), 0, s, a, cs);
     };
     using Q1 = std::integral_constant<int, 1>;
     using Q2 = std::integral_constant<int, 2>;
