@@ -236,18 +236,35 @@ __device__ __forceinline__ int kchunk(int r, int c) {
 // significant bits.  The product q·k of two such pairs, taken as
 // qhi·khi + qlo·khi + qhi·klo on the matrix cores, has a relative error of
 // about 2^-16, against 2^-8 for the product of the rounded values.
-// Per pair of values: one conversion for hi, two bit operations to read its
-// halves back, two subtractions and one conversion for lo.
-__device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo) {
+// Per pair of values: one conversion for hi, one v_dot2_f32_bf16 per value
+// for the remainder and one conversion for lo.  The remainder x - hi is read
+// straight off the packed pair: dot2(hi pair, (-1, 0), x0) = x0 - hi0 and
+// dot2(hi pair, (0, -1), x1) = x1 - hi1.  Both products are exact and the
+// difference is an fp32 number, so the result is exact whatever the
+// instruction's internal rounding.
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v;
+struct SplitOnes {
+  bf16x2v lo, hi;  // bf16 pairs (-1, 0) and (0, -1), low half first
+};
+// The two pairs live in registers: as an instruction constant, the
+// compiler encodes (-1, 0) as the inline constant -1.0, which a packed-bf16
+// operand does not read as that pair.  (The asm is not volatile: a volatile
+// one counts as a possible memory write, which turns later uniform loads
+// into vector loads.)
+__device__ __forceinline__ SplitOnes split_ones() {
+  uint32_t m_lo = 0x0000bf80u, m_hi = 0xbf800000u;
+  asm("" : "+s"(m_lo), "+s"(m_hi));
+  return SplitOnes{__builtin_bit_cast(bf16x2v, m_lo), __builtin_bit_cast(bf16x2v, m_hi)};
+}
+__device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo, const SplitOnes& m) {
   uint32_t h[4], l[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t w = pack2_bf16(y[2 * i], y[2 * i + 1]);
-    // opaque to the optimizer, which would otherwise convert y[2i] a second
-    // time to read the low half
-    asm volatile("" : "+v"(w));
+    const uint32_t w = pack2_bf16(y[2 * i], y[2 * i + 1]);
+    const bf16x2v wv = __builtin_bit_cast(bf16x2v, w);
     h[i] = w;
-    l[i] = pack2_bf16(y[2 * i] - __uint_as_float(w << 16), y[2 * i + 1] - __uint_as_float(w & 0xffff0000u));
+    l[i] = pack2_bf16(__builtin_amdgcn_fdot2_f32_bf16(wv, m.lo, y[2 * i], false),
+                      __builtin_amdgcn_fdot2_f32_bf16(wv, m.hi, y[2 * i + 1], false));
   }
   hi = make_uint4(h[0], h[1], h[2], h[3]);
   lo = make_uint4(l[0], l[1], l[2], l[3]);
@@ -311,6 +328,7 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
   const int nk = kg + ell;
   const int Hq = a.Hq, G = GT > 0 ? GT : a.G;
   bf16_t* out = (bf16_t*)sl.out;
+  const SplitOnes so = split_ones();
 
   // ---- issue the first QPF heads' Q loads of this wave first: they do not
   // depend on the item id, so HBM traffic starts while the id is in flight --
@@ -548,8 +566,8 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
           yh[e] = __builtin_fmaf(xh[e], c[s][e], xl[e] * sn[s][e]);
         }
         uint4 hl, ll, hh, lh;
-        split8_bf16(yl, hl, ll);
-        split8_bf16(yh, hh, lh);
+        split8_bf16(yl, hl, ll, so);
+        split8_bf16(yh, hh, lh, so);
         const int ol = kchunk<D>(R, 4 * s + q4), oh = kchunk<D>(R, 4 * (s + NP) + q4);
         *(uint4*)(Khi + ol) = hl;
         *(uint4*)(Klo + ol) = ll;
@@ -566,7 +584,7 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
     if constexpr (FP8) {
       float f[8];
       gist_f32(raw, j, false, 8 * c, f);
-      split8_bf16(f, hi, lo);
+      split8_bf16(f, hi, lo, so);
     } else {
       hi = make_uint4(raw.x, raw.y, raw.z, raw.w);
       lo = make_uint4(0, 0, 0, 0);
@@ -649,8 +667,8 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
         yh[e] = __builtin_fmaf(xh[e], qc[s][e], xl[e] * qsn[s][e]);
       }
       uint4 h0, l0, h1, l1;
-      split8_bf16(yl, h0, l0);
-      split8_bf16(yh, h1, l1);
+      split8_bf16(yl, h0, l0, so);
+      split8_bf16(yh, h1, l1, so);
       qh[s] = __builtin_bit_cast(bf16x8_t, h0);
       ql[s] = __builtin_bit_cast(bf16x8_t, l0);
       qh[s + NP] = __builtin_bit_cast(bf16x8_t, h1);
@@ -1099,7 +1117,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   // the rows as given.  It is summed from the bf16 pairs as loaded (v_dot2:
   // the products of two bf16 values are exact in fp32); K_new is never
   // rotated or unpacked here.
-  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2v;
+  const SplitOnes so = split_ones();
   auto dot2 = [](uint32_t x, uint32_t y, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, x), __builtin_bit_cast(bf16x2v, y),
                                            acc, false);
@@ -1129,8 +1147,8 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
     if constexpr (QCH == 8) dot += dpp_f<0x141>(dot);
     sdot[i] = dot;
     uint4 hl, hh;
-    split8_bf16(yl, hl, qlo_st[i][0]);
-    split8_bf16(yh, hh, qlo_st[i][1]);
+    split8_bf16(yl, hl, qlo_st[i][0], so);
+    split8_bf16(yh, hh, qlo_st[i][1], so);
     if (u < G * QCH) {
       *(uint4*)(Rl + qpos(h, c)) = hl;
       *(uint4*)(Rl + qpos(h, c + QCH)) = hh;
