@@ -152,6 +152,19 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// max of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four rows of an
+// MFMA 16x16 accumulator column) with the gfx950 lane swaps: after a swap of
+// x with itself, one result holds the partner's value in one half of the
+// wave and the lane's own value in the other, the second result the
+// reverse, so the maximum of x and both is the pair's maximum.  The values
+// stay in VALU registers (no LDS round trip, unlike ds_bpermute).
+__device__ __forceinline__ float col4_max(float x) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax3(x, __uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax3(x, __uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // Orders the LDS accesses of one wave around an exchange between its lanes
 // (one lane writes what another reads).  A wave's LDS accesses already
 // complete in program order, so this emits no instruction; it keeps the
@@ -707,8 +720,6 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
   // (opaque, so the compiler keeps them in registers rather than rebuilding
   // them for every head)
   asm volatile("" : "+v"(bias0), "+v"(bias1));
-  // ds_bpermute byte addresses of the lanes that hold the same token
-  const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
   const float sl2 = a.scale_log2;
   typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
   u32x4_t ones_w = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // eight bf16 1.0
@@ -739,8 +750,7 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
       }
     }
     // row max across the four lanes that share a token
-    mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
-    mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
+    mx = col4_max(mx);
 
     // P = exp2((s - max) * scale*log2 e) in bf16, the product as one fma;
     // O = P·V and the row sum (P against a ones tile) both on the matrix
@@ -1237,9 +1247,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
     }
   }
   wave_lds_sync();
-  const int perm16 = (lane ^ 16) << 2, perm32 = (lane ^ 32) << 2;
-  mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm16, __float_as_int(mx))), mx);
-  mx = vmax3(mx, __int_as_float(__builtin_amdgcn_ds_bpermute(perm32, __float_as_int(mx))), mx);
+  mx = col4_max(mx);
 
   // ---- P = exp2((s - max) * scale*log2 e); O = P·V and row sums on the
   // matrix cores; V fragment (d-tile dt, key tile kt) by transpose read: the
