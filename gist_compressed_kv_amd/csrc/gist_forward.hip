@@ -342,6 +342,13 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
   const int Hq = a.Hq, G = GT > 0 ? GT : a.G;
   bf16_t* out = (bf16_t*)sl.out;
   const SplitOnes so = split_ones();
+  // Single-generation launches (the instances with a one-head Q ring and a
+  // compile-time group size are used only when every workgroup of the grid
+  // is resident at once): the SIMD's issue arbiter favours the oldest wave,
+  // so the waves dispatched last fell behind and finished alone.  Instead
+  // each wave's priority follows its remaining work (see the head loop),
+  // and every wave stages its keys at the top priority.
+  constexpr bool LPT = QPF == 1 && GT > 0 && !LAST;
 
   // ---- issue the first QPF heads' Q loads of this wave first: they do not
   // depend on the item id, so HBM traffic starts while the id is in flight --
@@ -466,6 +473,10 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
       }
     }
   }
+  // (set after the id and scale loads: the compiler takes s_setprio for a
+  // possible memory write and would otherwise turn those scalar loads into
+  // vector loads that wait for the Q prefetch)
+  if constexpr (LPT) __builtin_amdgcn_s_setprio(3);
   // Eight gist elements (channels ch.., K or V of gist key j < kg) as fp32.
   // fp8 gist rows are decoded and multiplied by their block's scale.  Every
   // lane issues one 16-byte load (fp8: the aligned 16 codes that hold its 8).
@@ -842,6 +853,16 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
     // exact), then head h attends and head h + 1's Q is prepared.
     for_each_const<GT>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
+      if constexpr (LPT) {
+        // remaining key tiles of this wave (this head's included), in
+        // quarters of the most any wave starts with: the wave with the most
+        // work left on a SIMD issues first (longest remaining job first)
+        const int q = (4 * (GT - h) * nkt - 1) / (GT * NKT);
+        if (q >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (q == 2) __builtin_amdgcn_s_setprio(2);
+        else if (q == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       if constexpr (h + QPF < GT) load_q(std::integral_constant<int, h % QPF>{}, h + QPF);
       attend(h);
       if constexpr (h + 1 < GT) prep_q(std::integral_constant<int, (h + 1) % QPF>{}, qh, ql);
