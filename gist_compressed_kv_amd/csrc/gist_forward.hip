@@ -285,7 +285,9 @@ __device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo
 
 // D: head_dim.  NKT: maximum number of 16-key tiles (keys <= 16*NKT).
 // QPF: Q ring depth: once head h has taken its Q out of the ring, the
-// loads of heads h+1 .. h+QPF are in flight.
+// loads of heads h+1 .. h+QPF are in flight.  The instances with QPF = 1 and
+// a compile-time group size serve single-generation launches: they load one
+// head before the staging and keep two in flight after it.
 // GT: the GQA group size when known at compile time (0 = taken from the
 // arguments).  With GT > 0 the head loop is fully unrolled, so the compiler
 // knows exactly which loads each wait has to cover and never drains the
@@ -393,8 +395,11 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
     olane[s] = (uint32_t)((((LAST ? 0 : tc) * Hq + g * G) * D + 8 * cl) * 2);
   }
   // Q ring held in native vectors (not the HIP uint4 struct) so it always
-  // stays in registers
-  u32x4_t raw[QPF][NS];
+  // stays in registers.  QPF heads are loaded before the staging; after it
+  // the ring holds DEP heads in flight (two in single-generation launches)
+  constexpr int DEP = LPT ? 2 : QPF;
+  constexpr int RQ = DEP > QPF ? DEP : QPF;
+  u32x4_t raw[RQ][NS];
   auto load_q = [&](auto slot, const int hq) {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -851,21 +856,28 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
     // Head h's Q was prepared before this point; its slot is refilled with
     // head h + QPF (heads past the group are not loaded, so the waits stay
     // exact), then head h attends and head h + 1's Q is prepared.
+    // Heads QPF .. DEP-1 (a deeper ring than before the staging) are
+    // issued first.
+    for_each_const<DEP - QPF>([&](auto ic) {
+      constexpr int j = QPF + decltype(ic)::value;
+      if constexpr (j < GT) load_q(std::integral_constant<int, j % RQ>{}, j);
+    });
     for_each_const<GT>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
       if constexpr (LPT) {
         // remaining key tiles of this wave (this head's included), in
         // quarters of the most any wave starts with: the wave with the most
-        // work left on a SIMD issues first (longest remaining job first)
-        const int q = (4 * (GT - h) * nkt - 1) / (GT * NKT);
-        if (q >= 3) __builtin_amdgcn_s_setprio(3);
-        else if (q == 2) __builtin_amdgcn_s_setprio(2);
+        // work left on a SIMD issues first (longest remaining job first).
+        // Capped at 2, below the staging priority, so a wave still staging
+        // its keys issues ahead of every wave in its heads.
+        const int q = min(2, (4 * (GT - h) * nkt - 1) / (GT * NKT));
+        if (q == 2) __builtin_amdgcn_s_setprio(2);
         else if (q == 1) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
       }
-      if constexpr (h + QPF < GT) load_q(std::integral_constant<int, h % QPF>{}, h + QPF);
+      if constexpr (h + DEP < GT) load_q(std::integral_constant<int, (h + DEP) % RQ>{}, h + DEP);
       attend(h);
-      if constexpr (h + 1 < GT) prep_q(std::integral_constant<int, (h + 1) % QPF>{}, qh, ql);
+      if constexpr (h + 1 < GT) prep_q(std::integral_constant<int, (h + 1) % RQ>{}, qh, ql);
     });
   } else {
     // the ring is refilled with the head QPF further on (clamped: always a
