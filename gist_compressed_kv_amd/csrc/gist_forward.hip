@@ -287,7 +287,7 @@ __device__ __forceinline__ void split8_bf16(const float* y, uint4& hi, uint4& lo
 // QPF: Q ring depth: once head h has taken its Q out of the ring, the
 // loads of heads h+1 .. h+QPF are in flight.  The instances with QPF = 1 and
 // a compile-time group size serve single-generation launches: they load one
-// head before the staging and keep two in flight after it.
+// head before the staging and keep three in flight after it.
 // GT: the GQA group size when known at compile time (0 = taken from the
 // arguments).  With GT > 0 the head loop is fully unrolled, so the compiler
 // knows exactly which loads each wait has to cover and never drains the
@@ -396,8 +396,8 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
   }
   // Q ring held in native vectors (not the HIP uint4 struct) so it always
   // stays in registers.  QPF heads are loaded before the staging; after it
-  // the ring holds DEP heads in flight (two in single-generation launches)
-  constexpr int DEP = LPT ? 2 : QPF;
+  // the ring holds DEP heads in flight (three in single-generation launches)
+  constexpr int DEP = LPT ? 3 : QPF;
   constexpr int RQ = DEP > QPF ? DEP : QPF;
   u32x4_t raw[RQ][NS];
   auto load_q = [&](auto slot, const int hq) {
