@@ -72,8 +72,10 @@ def gist_bytes_per_pair_layer(wl, last_only: bool = False) -> int:
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed passes (default 200; 4800 for the one-launch single-layer workloads)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed passes first (default 20; 480 for the single-layer workloads)")
     ap.add_argument("--workload", default="24L_b500",
                     choices=["24L_b500", "24L_b500_last", "24L_b500_grouped", "wide_eos_grouped",
                              "wide_eos_fp8_grouped", "24L_b2000", "1L_b500",
@@ -82,7 +84,17 @@ def parse():
                              "wide_ell64_fp8", "wide_eos", "wide_eos_fp8", "paged", "paged_fp8",
                              "prefill", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    return ap.parse_args()
+    args = ap.parse_args()
+    # A single-layer pass is one launch of about 30 us: 200 of them time 6 ms,
+    # too short a region (the launch time read 31-34 us in runs of 200
+    # passes and 28.6 us in runs of 4800).  Those workloads time as many
+    # launches as the 24-layer pass does by default.
+    one_launch = args.workload in ("1L_b500", "1L_b500_paged")
+    if args.steps is None:
+        args.steps = 4800 if one_launch else 200
+    if args.warmup is None:
+        args.warmup = 480 if one_launch else 20
+    return args
 
 
 def kernel_source_hash(source: str) -> str:
