@@ -569,7 +569,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the gist path has no "
-              "cross-GPU step in this build.", file=sys.stderr)
+              "cross-GPU step.", file=sys.stderr)
         sys.exit(2)
     if not args.no_cpu_baseline and args.workload not in ("copy", "paged", "paged_fp8", "prefill"):
         start_oracle_pool()  # before anything touches the GPU
