@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import gist_compressed_kv_amd as G
 from gpu_cases import TOL, DecodeCase, GistCase, f64, say
 from gist_compressed_kv_amd import synth
 
@@ -156,6 +157,26 @@ def test_several_workgroup_generations_sampled(hq, fp8):
     case = GistCase(1, 3000, 8, 64, hq, 2, 64, 700, torch.bfloat16, 321 + hq, fp8=fp8)
     sample = np.array([0, 1, 349, 511, 512, 698, 699])
     check_gist(case, sample=sample, label=f"700 pairs, Hq={hq}, {'fp8' if fp8 else 'bf16'} pool (sampled)")
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("hq", [14, 16], ids=["G7", "G8"])
+def test_single_and_multi_generation_instances_agree_bitwise(hq, fp8):
+    # The same pairs through the single-generation instance (300 pairs x 2
+    # KV heads = 600 workgroups, all resident: one head of Q before the
+    # staging, three after it, wave priorities by remaining work) and, as the
+    # first 300 of 700 pairs, through the several-generation one (two heads
+    # of Q, the hardware's issue order).  Only the schedule differs, so the
+    # rows must be identical bit for bit.
+    big = GistCase(1, 3000, 8, 64, hq, 2, 64, 700, torch.bfloat16, 611 + hq, fp8=fp8)
+    n = 300
+    ids = big.ids[:n].contiguous()
+    q, kn, vn = (t[0][:n].contiguous() for t in (big.q, big.kn, big.vn))
+    small = G.gist_attn_forward(big.pool, 0, ids, q, kn, vn, big.pos0, 10000.0, big.scale)
+    full = big.run(0)
+    torch.cuda.synchronize()
+    assert torch.equal(small.view(torch.int16), full[:n].view(torch.int16))
+    assert torch.isfinite(full.float()).all()
 
 
 def _wide_sample(wl, seed):
