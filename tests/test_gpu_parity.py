@@ -299,30 +299,36 @@ def test_bitwise_deterministic_reruns():
 
 
 def test_hip_graph_capture_replays_match_eager():
-    # A 24-layer pass of l = 64 calls (the single-generation instance) and an
-    # l = 1 call with a query gist (the EOS kernel), captured once into a HIP
-    # graph.  The library allocates nothing and issues no memsets, so the
+    # A 24-layer pass of l = 64 calls (the single-generation instance), an
+    # l = 1 call with a query gist (the EOS kernel) and a paged decode step
+    # (split and combine kernels), captured once into a HIP graph.  The library allocates nothing and issues no memsets, so the
     # calls capture as plain kernel launches.  Each replay, with eager work on
     # the outputs in between, must give the eager rows bit for bit.
     case = GistCase(24, 500, 8, 64, 14, 2, 64, 40, torch.bfloat16, 771)
     eos = GistCase(1, 60, 8, 1, 64, 8, 128, 48, torch.bfloat16, 772, kq=8, n_qrows=3,
                    q_ids=torch.arange(48) % 3)
-    eager = [case.run(li).clone() for li in range(24)] + [eos.run(0).clone()]
+    dc = DecodeCase(64, 4, 256, 128, 8, [1000, 2000, 17], torch.bfloat16, 773)
+    eager = [case.run(li).clone() for li in range(24)] + [eos.run(0).clone(), dc.run().clone()]
     torch.cuda.synchronize()
     outs = [torch.empty_like(o) for o in eager]
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):  # the first calls on the capture stream run eagerly
+    ws = torch.empty(G.paged_decode_workspace_bytes(3, 8, dc.table.shape[1], 256, 128),
+                     dtype=torch.uint8, device="cuda")
+
+    def calls():
         for li in range(24):
             case.run(li, out=outs[li])
         eos.run(0, out=outs[24])
+        dc.run(out=outs[25], workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # the first calls on the capture stream run eagerly
+        calls()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for li in range(24):
-            case.run(li, out=outs[li])
-        eos.run(0, out=outs[24])
+        calls()
     for rep in range(3):
         for o in outs:
             o.fill_(float("nan"))
