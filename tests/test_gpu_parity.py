@@ -339,6 +339,31 @@ def test_hip_graph_capture_replays_match_eager():
             assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {rep}"
 
 
+def test_calls_on_concurrent_streams_match_sequential():
+    # The library keeps no device state between calls (the paged decode
+    # scratch of the allocation-free entry point aside), so calls in flight on
+    # several streams at once give the rows they give one after the other.
+    case = GistCase(4, 500, 8, 64, 14, 2, 64, 300, torch.bfloat16, 781)
+    eos = GistCase(1, 60, 8, 1, 64, 8, 128, 200, torch.bfloat16, 782, kq=8, n_qrows=4,
+                   q_ids=torch.arange(200) % 4)
+    seq = [case.run(li).clone() for li in range(4)] + [eos.run(0).clone()]
+    torch.cuda.synchronize()
+    outs = [torch.full_like(o, float("nan")) for o in seq]
+    streams = [torch.cuda.Stream() for _ in range(5)]
+    torch.cuda.synchronize()
+    for i, st in enumerate(streams):
+        if i < 4:
+            G.gist_attn_forward(case.pool, i, case.ids, case.q[i], case.kn[i], case.vn[i],
+                                case.pos0, 10000.0, case.scale, out=outs[i], stream=st)
+        else:
+            G.gist_attn_forward(eos.pool, 0, eos.ids, eos.q[0], eos.kn[0], eos.vn[0], eos.pos0,
+                                10000.0, eos.scale, qpool=eos.qpool, q_ids=eos.q_ids,
+                                out=outs[4], stream=st)
+    torch.cuda.synchronize()
+    for o, e in zip(outs, seq):
+        assert torch.equal(o.view(torch.int16), e.view(torch.int16))
+
+
 def test_empty_batch_is_a_noop():
     import gist_compressed_kv_amd as G
     case = GistCase(1, 3, 8, 16, 4, 1, 64, 1, torch.bfloat16, 406)
