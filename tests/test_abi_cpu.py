@@ -392,3 +392,32 @@ def test_paged_gist_fp8_validation(L):
     assert _pg8(L, vs=ctypes.c_void_p((1 << 20) + 2)) == _lib.GIST_ERR_INVALID_ARG
     assert "4-byte" in L.gist_last_error().decode()
     assert _pg8(L, P=0, ptr=None, ks=None, vs=None) == _lib.GIST_OK
+
+
+def test_last_error_is_per_thread(L):
+    # gist_last_error reports the last failing call of the calling thread:
+    # two threads that fail in different ways each read their own message
+    import threading
+
+    pool = _pool(L)
+    seen = {}
+    ready = threading.Barrier(2)
+
+    def worker(name, kwargs):
+        st = _fwd(L, pool, **kwargs)
+        ready.wait()  # both calls have failed before either message is read
+        seen[name] = (st, L.gist_last_error().decode())
+
+    try:
+        ts = [threading.Thread(target=worker, args=("layer", {"layer": 5})),
+              threading.Thread(target=worker, args=("scale", {"scale": 0.0}))]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+    finally:
+        L.gist_pool_destroy(pool)
+    assert seen["layer"][0] == _lib.GIST_ERR_OUT_OF_RANGE
+    assert seen["scale"][0] == _lib.GIST_ERR_INVALID_ARG
+    assert seen["layer"][1] != seen["scale"][1]
+    assert "layer" in seen["layer"][1] and "scale" in seen["scale"][1]
