@@ -981,8 +981,11 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   constexpr int NDT = D / 16;
   constexpr int CPR = D / 8;             // 16-byte chunks per row
   constexpr int ROWS = 16 * NGT;
-  constexpr int RITG = 16 * NGT * CPR / 64;  // gist V row chunks per lane
-  static_assert(16 * NGT * CPR % 64 == 0 && 2 * CPR <= 64, "staging layout");
+  // gist V rows are read in 16-byte units: 8 bf16 values or 16 fp8 codes
+  constexpr int VCH = FP8 ? 2 : 1;   // 8-element chunks per unit
+  constexpr int VPR = CPR / VCH;     // units per row
+  constexpr int RITG = 16 * NGT * VPR / 64;  // gist V units per lane
+  static_assert(16 * NGT * VPR % 64 == 0 && 2 * CPR <= 64 && NS % 2 == 0, "staging layout");
   // the workgroup is this one wave
   __shared__ __align__(16) bf16_t rows_lds[ROWS * (D + 4)];
   __shared__ __align__(16) float vself_lds[D];  // V_new of the token, fp32
@@ -1083,24 +1086,38 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   };
 
   // ---- gist loads, all unconditional (clamped rows) ------------------------
-  // K: MFMA A layout straight from HBM (lane n = key, 8 channels of step s)
+  // K: MFMA A layout straight from HBM (lane n = key, 8 channels per step).
+  // The contraction takes the 8-channel chunks in the order kc(s, q4): in
+  // steps 2t and 2t + 1 lane q4 holds chunks 2q4 and 2q4 + 1 of channels
+  // 64t..64t+63, so with fp8 codes one 16-byte load feeds both steps.  Q's B
+  // fragments are read in the same order.
+  auto kc = [](int s, int qq) { return 8 * (s >> 1) + 2 * qq + (s & 1); };
   CV kraw[NGT][NS];
 #pragma unroll
   for (int kt = 0; kt < NGT; ++kt) {
     const int j = 16 * kt + n;
     const C* row = gist_row(j < kg ? j : 0, false);
+    if constexpr (FP8) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) kraw[kt][s] = *(const CV*)(row + 32 * s + 8 * q4);
+      for (int t = 0; t < NS / 2; ++t) {
+        const uint4 w = *(const uint4*)(row + 64 * t + 16 * q4);
+        kraw[kt][2 * t] = make_uint2(w.x, w.y);
+        kraw[kt][2 * t + 1] = make_uint2(w.z, w.w);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) kraw[kt][s] = *(const CV*)(row + 8 * kc(s, q4));
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // V rows, coalesced (lane covers chunk u % CPR of row u / CPR); issued
+  // V rows, coalesced (lane covers unit u % VPR of row u / VPR); issued
   // last, so the logits of the gist tiles only wait for K and Q
-  CV graw[RITG];
+  u32x4_t graw[RITG];
 #pragma unroll
   for (int it = 0; it < RITG; ++it) {
     const int u = lane + 64 * it;
-    const int r = u / CPR, c = u - (u / CPR) * CPR;
-    graw[it] = *(const CV*)(gist_row(r < kg ? r : 0, true) + 8 * c);
+    const int r = u / VPR, c = u - (u / VPR) * VPR;
+    graw[it] = *(const u32x4_t*)(gist_row(r < kg ? r : 0, true) + 8 * VCH * c);
   }
   __builtin_amdgcn_sched_barrier(0);
   // fp8: scales of the item and query gist (K, V); wave-uniform scalars.
@@ -1212,7 +1229,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   }
   wave_lds_sync();
 #pragma unroll
-  for (int s = 0; s < NS; ++s) qh[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
+  for (int s = 0; s < NS; ++s) qh[s] = *(const bf16x8_t*)(Rl + qpos(hcol, kc(s, q4)));
   wave_lds_sync();
 #pragma unroll
   for (int i = 0; i < QU; ++i) {
@@ -1225,7 +1242,7 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
   }
   wave_lds_sync();
 #pragma unroll
-  for (int s = 0; s < NS; ++s) ql[s] = *(const bf16x8_t*)(Rl + qpos(hcol, 4 * s + q4));
+  for (int s = 0; s < NS; ++s) ql[s] = *(const bf16x8_t*)(Rl + qpos(hcol, kc(s, q4)));
   wave_lds_sync();  // the rows below overwrite the Q buffer
 
   // ---- logits Sᵀ[key][head] of the gist tiles (unscaled: scale*log2 e is
@@ -1267,7 +1284,13 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
 #pragma unroll
   for (int it = 0; it < RITG; ++it) {
     const int u = lane + 64 * it;
-    put(u / CPR, u - (u / CPR) * CPR, to_bf16x8(graw[it]));
+    const int r = u / VPR, c = u - (u / VPR) * VPR;
+    if constexpr (FP8) {
+      put(r, 2 * c, to_bf16x8(make_uint2(graw[it].x, graw[it].y)));
+      put(r, 2 * c + 1, to_bf16x8(make_uint2(graw[it].z, graw[it].w)));
+    } else {
+      put(r, c, graw[it]);
+    }
   }
   // the token's V row in fp32, unpacked once (lanes past the row repeat it)
   float* vs = vself_lds;
