@@ -32,6 +32,9 @@ namespace gist {
 
 constexpr int kSplitKeys = 256;  // keys per workgroup of the split kernel
 constexpr int kWsPad = 4;        // workspace row = d channels + (m, l, 2 pad)
+// A row's reference maximum moves only when a logit passes it by more than
+// this many log2 units (weights up to 2^8 between moves).
+constexpr float kLazyMax = 8.f;
 
 struct DecodeArgs {
   const void* kc;
@@ -281,26 +284,77 @@ decode_split(const DecodeArgs a) {
     unpack(vb[t % PD], vf);
     if constexpr (t + PD < 16) issue(std::integral_constant<int, t + PD>{});
     const bool valid = t < nvalid;
+    if constexpr (!FP8) {
+      // running maximum updated at every key
 #pragma unroll
-    for (int hh = 0; hh < MAXG; ++hh) {
-      if (hh == 0 || hh < G) {  // head 0 always exists: no branch around it
-        float part = 0.f;
+      for (int hh = 0; hh < MAXG; ++hh) {
+        if (hh == 0 || hh < G) {  // head 0 always exists: no branch around it
+          float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kf[e], part);
-        // the logit is formed for every key and masked by selects (no branch,
-        // so the loads stay where they were issued)
-        const float dot = row16_sum_d(part) * kmul;
-        const float sc = valid ? dot : -INFINITY;
-        const float mnew = fmaxf(m[hh], sc);
-        // exponents never see -inf - -inf: an all-masked state keeps alpha = 1,
-        // a masked key gets weight exp2(-inf) = 0
-        const float alpha = __builtin_amdgcn_exp2f(mnew == -INFINITY ? 0.f : m[hh] - mnew);
-        const float pw = __builtin_amdgcn_exp2f(valid ? sc - mnew : -INFINITY);
-        m[hh] = mnew;
-        l[hh] = l[hh] * alpha + pw;
-        const float pv = pw * vmul;
+          for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kf[e], part);
+          // the logit is formed for every key and masked by selects (no branch,
+          // so the loads stay where they were issued)
+          const float dot = row16_sum_d(part) * kmul;
+          const float sc = valid ? dot : -INFINITY;
+          const float mnew = fmaxf(m[hh], sc);
+          // exponents never see -inf - -inf: an all-masked state keeps alpha = 1,
+          // a masked key gets weight exp2(-inf) = 0
+          const float alpha = __builtin_amdgcn_exp2f(mnew == -INFINITY ? 0.f : m[hh] - mnew);
+          const float pw = __builtin_amdgcn_exp2f(valid ? sc - mnew : -INFINITY);
+          m[hh] = mnew;
+          l[hh] = l[hh] * alpha + pw;
+          const float pv = pw * vmul;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pv, vf[e], o[hh][e] * alpha);
+          for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pv, vf[e], o[hh][e] * alpha);
+        }
+      }
+    } else {
+      // the logit of this key for every head of the group (log2 units), formed
+      // for every key and masked by selects
+      float sc[MAXG];
+      bool up = false;
+#pragma unroll
+      for (int hh = 0; hh < MAXG; ++hh) {
+        if (hh == 0 || hh < G) {  // head 0 always exists: no branch around it
+          float part = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e) part = fmaf(qv[hh][e], kf[e], part);
+          const float dot = row16_sum_d(part) * kmul;
+          sc[hh] = valid ? dot : -INFINITY;
+          up = up || sc[hh] > m[hh] + kLazyMax;
+        }
+      }
+      // fp8 cache (its decode adds VALU work per key): the state (m, l, o) is
+      // kept relative to a reference maximum m that moves only when a logit
+      // passes it by more than kLazyMax (always at a row's first valid key), so
+      // most keys cost no rescale of o and l; the weights stay below
+      // 2^kLazyMax.  The branch is taken by the whole wave when any of its rows
+      // needs it (alpha = 1 for the others).
+      if (__builtin_expect(__any(up) != 0, 0)) {
+#pragma unroll
+        for (int hh = 0; hh < MAXG; ++hh) {
+          if (hh == 0 || hh < G) {
+            const float mnew = fmaxf(m[hh], sc[hh]);
+            // an all-masked state keeps alpha = 1 (no -inf - -inf)
+            const float alpha = __builtin_amdgcn_exp2f(mnew == -INFINITY ? 0.f : m[hh] - mnew);
+            m[hh] = mnew;
+            l[hh] *= alpha;
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[hh][e] *= alpha;
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < MAXG; ++hh) {
+        if (hh == 0 || hh < G) {
+          // a masked key gets weight exp2(-inf) = 0; a valid key has a finite
+          // reference maximum by now (its own logit at the latest)
+          const float pw = __builtin_amdgcn_exp2f(valid ? sc[hh] - m[hh] : -INFINITY);
+          l[hh] += pw;
+          const float pv = pw * vmul;
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[hh][e] = fmaf(pv, vf[e], o[hh][e]);
+        }
       }
     }
   });
