@@ -1375,7 +1375,9 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
         v[r] = o[2 * s][r];
         v[4 + r] = o[2 * s + 1][r];
       }
-      *(uint4*)(orow + 32 * s) = pack8_bf16(v);
+      // non-temporal: the output is written once and not read here
+      const uint4 w = pack8_bf16(v);
+      __builtin_nontemporal_store(u32x4_t{w.x, w.y, w.z, w.w}, (u32x4_t*)(orow + 32 * s));
     }
   }
 }
