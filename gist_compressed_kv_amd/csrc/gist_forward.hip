@@ -1365,8 +1365,13 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
       }
     }
   }
+  // The group's G output rows are one contiguous G*D block.  Lane (n, q4)
+  // holds 16-byte chunks 4s + q4 of row n; they go through the row buffer
+  // (chunk c of row n at chunk c ^ n: conflict-free on both sides, and every
+  // P·V read of the buffer has completed, since o depends on it) so that the
+  // stores write whole lines, non-temporal (read nowhere here).
+  wave_lds_sync();
   if (n < G) {
-    bf16_t* orow = out + orow0 + (int64_t)n * D + 8 * q4;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       float v[8];
@@ -1375,10 +1380,15 @@ __device__ __forceinline__ void eos_body(const FwdArgs& a, const CsPos0& cs, con
         v[r] = o[2 * s][r];
         v[4 + r] = o[2 * s + 1][r];
       }
-      // non-temporal: the output is written once and not read here
-      const uint4 w = pack8_bf16(v);
-      __builtin_nontemporal_store(u32x4_t{w.x, w.y, w.z, w.w}, (u32x4_t*)(orow + 32 * s));
+      *(uint4*)(Rl + qpos(n, 4 * s + q4)) = pack8_bf16(v);
     }
+  }
+  wave_lds_sync();
+  static_assert(16 * D <= ROWS * (D + 4), "output staging fits the row buffer");
+  for (int u = lane; u < G * CPR; u += 64) {
+    const int h = u / CPR, c = u - (u / CPR) * CPR;
+    const u32x4_t w = *(const u32x4_t*)(Rl + qpos(h, c));
+    __builtin_nontemporal_store(w, (u32x4_t*)(out + orow0 + 8 * (int64_t)u));
   }
 }
 
