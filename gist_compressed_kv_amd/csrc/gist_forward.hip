@@ -376,8 +376,9 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
   // one instruction.  A per-wave LDS buffer converts to and from the MFMA
   // operand layout.  Addresses are a wave-uniform base plus 32-bit lane
   // offsets (scalar-base addressing form).
-  // Q is read once, in whole lines: its loads are non-temporal (the staging
-  // loads are not: they touch parts of lines that other loads then reuse)
+  // Q is read once, in whole lines: its loads are non-temporal, as are the
+  // bf16 V staging loads (whole rows); the K staging loads touch parts of
+  // lines that other loads then reuse and are ordinary
   const int cl = lane % CPR, rl = lane / CPR;
   const int64_t pair_off = (int64_t)p * (LAST ? 1 : ell) * Hq * D;
   const char* qpair = (const char*)((const bf16_t*)sl.q + pair_off);
@@ -513,7 +514,8 @@ __device__ __forceinline__ void mfma_body(const FwdArgs& a, const Slice& sl, int
       return *(const u32x4_t*)(gist ? (const void*)(gist_row(j, true) + (ch & ~15))
                                     : (const void*)(nrow + ch));
     } else {
-      return *(const u32x4_t*)(j < kg ? gist_row(j, true) + ch : nrow + ch);
+      // whole rows, read once: non-temporal
+      return __builtin_nontemporal_load((const u32x4_t*)(j < kg ? gist_row(j, true) + ch : nrow + ch));
     }
   };
   auto v_bf16 = [&](const u32x4_t& raw, int j, int ch) -> uint4 {
