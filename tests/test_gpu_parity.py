@@ -101,6 +101,8 @@ VALU_SHAPES = [
     (1, 3, 0, 3, 1, 128, 3, torch.bfloat16),
     # the EOS kernel at both of its limits: k + k' = 32 and G = 16
     (1, 16, 16, 16, 1, 64, 3, torch.bfloat16),
+    # G = 16 at d = 128: two Q units per lane and a 16-row output block
+    (1, 8, 8, 32, 2, 128, 3, torch.bfloat16),
     (100, 8, 0, 14, 2, 64, 2, torch.bfloat16),
     (70, 64, 0, 4, 2, 128, 2, torch.bfloat16),
     (1, 8, 0, 14, 2, 64, 3, torch.float32),
@@ -565,6 +567,7 @@ EOS_FP8_SHAPES = [
     (3, 0, 3, 1, 128, 5),
     (16, 16, 32, 2, 64, 11),
     (1, 0, 1, 1, 64, 3),
+    (8, 8, 32, 2, 128, 5),
 ]
 
 
